@@ -1,0 +1,302 @@
+/*
+ * oracle.c -- plain, slow fp64 CPU reference for the tiled matrix product
+ * Out = A . B^T.  TEST INFRASTRUCTURE ONLY: nothing in the product library
+ * links, includes or calls this file; only the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark do.  It shares no code, header, table or
+ * helper with the HIP path.
+ *
+ * What it computes (the plain definition, no blocking, no reordering):
+ *
+ *   ref[i][j]    = sum_{k=0}^{K-1} a(i,k) * b(j,k)      fp64, k ascending
+ *   abssum[i][j] = sum_{k=0}^{K-1} |a(i,k) * b(j,k)|    fp64, for tolerances
+ *
+ * where a(i,k), b(j,k) are the exact real values of the stored input
+ * elements.  B is stored N x K ("K-major"): the product uses B transposed.
+ *   - "Blackwell Tensor Cores" (TVM TIRx guide), "The Accumulator's
+ *     Lifetime": the example computes Out = A @ B.T with A (128, 64) and
+ *     B (64, 64), float16 in, float32 out; the first MMA ignores the previous
+ *     accumulator contents, so there is no C input.
+ *   - "mma.sync" (TVM TIRx tile-op reference), "Operand coordinates and
+ *     ownership": B's logical axes are (N, K) although the product uses B
+ *     transposed.
+ *   - "API Card: Blackwell Pipeline (tcgen05)" (cuBLASDx), "Descriptor.":
+ *     row-major A, column-major B (K x N), i.e. the TN arrangement.
+ *
+ * Block-scaled (MX) inputs follow "Hopper and Blackwell GEMM", Concept
+ * section "FP8 and FP4, with block scaling" and its format table: every row
+ * of A and column of B (= row of the N x K storage) is cut into blocks of 32
+ * consecutive K elements and each block's values are multiplied by their own
+ * E8M0 scale, a power of two:
+ *
+ *   a(i,k) = e4m3(A[i][k]) * e8m0(SA[i][k/32])
+ *   b(j,k) = e4m3(B[j][k]) * e8m0(SB[j][k/32])
+ *
+ * Element decoders are written from the format definitions (IEEE 754
+ * binary16; bfloat16 = the upper half of binary32; OCP MX E4M3 "FN" with bias
+ * 7, no infinities, S.1111.111 = NaN; E8M0 = 2^(e-127), 0xFF = NaN).  The page
+ * table names these formats but does not print their bit layouts; the OCP
+ * Microscaling specification cited in that page's "Go deeper" list does.
+ *
+ * Accuracy: sequential fp64 summation errs by at most about K * 2^-53 *
+ * abssum, far below any tolerance used against the GPU path.  Every MX
+ * product is exact in fp64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F16 = 0, OR_BF16 = 1, OR_F32 = 2, OR_E4M3 = 3, OR_E8M0 = 4 };
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits. */
+static double dec_f16(uint16_t h) {
+    int s = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m/1024 * 2^-14 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 mantissa bits. */
+static double dec_bf16(uint16_t h) {
+    int s = h >> 15, e = (h >> 7) & 0xff, m = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -133); /* m/128 * 2^-126 */
+    else if (e == 255)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + m), e - 134); /* (1 + m/128) * 2^(e-127) */
+    return s ? -v : v;
+}
+
+/* OCP E4M3 (FN): 1 sign, 4 exponent (bias 7), 3 mantissa; no infinities;
+ * exponent 1111 with mantissa 111 is NaN; max normal 448. */
+static double dec_e4m3(uint8_t b) {
+    int s = b >> 7, e = (b >> 3) & 0xf, m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9); /* m/8 * 2^-6 */
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* OCP E8M0: unsigned exponent only, 2^(e-127); 0xFF is NaN. */
+static double dec_e8m0(uint8_t b) {
+    if (b == 0xff)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+static double dec_f32(uint32_t w) {
+    float f;
+    memcpy(&f, &w, 4);
+    return (double)f;
+}
+
+static int elem_size(int dtype) {
+    switch (dtype) {
+    case OR_F16:
+    case OR_BF16:
+        return 2;
+    case OR_F32:
+        return 4;
+    case OR_E4M3:
+    case OR_E8M0:
+        return 1;
+    }
+    return 0;
+}
+
+static double dec_one(int dtype, const void* src, int64_t idx) {
+    switch (dtype) {
+    case OR_F16:
+        return dec_f16(((const uint16_t*)src)[idx]);
+    case OR_BF16:
+        return dec_bf16(((const uint16_t*)src)[idx]);
+    case OR_F32:
+        return dec_f32(((const uint32_t*)src)[idx]);
+    case OR_E4M3:
+        return dec_e4m3(((const uint8_t*)src)[idx]);
+    case OR_E8M0:
+        return dec_e8m0(((const uint8_t*)src)[idx]);
+    }
+    return NAN;
+}
+
+/* Decode n stored elements of the given format into exact fp64 values. */
+int oracle_decode(int dtype, const void* src, int64_t n, double* dst) {
+    if (!elem_size(dtype) || (n > 0 && (!src || !dst)))
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        dst[i] = dec_one(dtype, src, i);
+    return 0;
+}
+
+/* Exact real value of operand element (r, k) of an R x K matrix: the element
+ * itself, times its block's E8M0 scale when a scale tensor is given. */
+static double operand_value(int dtype, const void* X, const uint8_t* SX, int64_t K, int64_t r,
+                            int64_t k) {
+    double v = dec_one(dtype, X, r * K + k);
+    if (SX)
+        v *= dec_e8m0(SX[r * (K / 32) + k / 32]);
+    return v;
+}
+
+/* Decode rows [r0, r1) of an R x K operand into dst (row-major). */
+static void decode_rows(int dtype, const void* X, const uint8_t* SX, int64_t K, int64_t r0,
+                        int64_t r1, double* dst) {
+    for (int64_t r = r0; r < r1; ++r)
+        for (int64_t k = 0; k < K; ++k)
+            dst[(r - r0) * K + k] = operand_value(dtype, X, SX, K, r, k);
+}
+
+typedef struct {
+    const double *a, *b; /* decoded A (M x K) and B (N x K) */
+    int64_t M, N, K;
+    double *ref, *abssum;
+    int64_t row0, row1;
+} job_t;
+
+/* The definition itself: for each (i, j), a sequential fp64 sum over k. */
+static void* rows_worker(void* p) {
+    job_t* j = (job_t*)p;
+    for (int64_t i = j->row0; i < j->row1; ++i) {
+        const double* ai = j->a + i * j->K;
+        for (int64_t c = 0; c < j->N; ++c) {
+            const double* bc = j->b + c * j->K;
+            double s = 0.0, sa = 0.0;
+            for (int64_t k = 0; k < j->K; ++k) {
+                double prod = ai[k] * bc[k];
+                s += prod;
+                sa += fabs(prod);
+            }
+            if (j->ref)
+                j->ref[i * j->N + c] = s;
+            if (j->abssum)
+                j->abssum[i * j->N + c] = sa;
+        }
+    }
+    return NULL;
+}
+
+static int run_rows(const double* a, const double* b, int64_t M, int64_t N, int64_t K, double* ref,
+                    double* abssum, int nthreads) {
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > M)
+        nthreads = (int)(M > 0 ? M : 1);
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    job_t* jobs = (job_t*)calloc((size_t)nthreads, sizeof(job_t));
+    if (!th || !jobs) {
+        free(th);
+        free(jobs);
+        return -2;
+    }
+    int started = 0, rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (job_t){a, b, M, N, K, ref, abssum, M * t / nthreads, M * (t + 1) / nthreads};
+        if (pthread_create(&th[t], NULL, rows_worker, &jobs[t]) != 0) {
+            rc = -3;
+            break;
+        }
+        ++started;
+    }
+    for (int t = 0; t < started; ++t)
+        pthread_join(th[t], NULL);
+    free(th);
+    free(jobs);
+    return rc;
+}
+
+/* One problem: decode both operands exactly, then apply the definition. */
+static int gemm_one(int dtype, const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
+                    int64_t M, int64_t N, int64_t K, double* ref, double* abssum, int nthreads) {
+    double* a = (double*)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
+    double* b = (double*)malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(double));
+    if (!a || !b) {
+        free(a);
+        free(b);
+        return -2;
+    }
+    decode_rows(dtype, A, SA, K, 0, M, a);
+    decode_rows(dtype, B, SB, K, 0, N, b);
+    int rc = run_rows(a, b, M, N, K, ref, abssum, nthreads);
+    free(a);
+    free(b);
+    return rc;
+}
+
+static int shape_ok(int64_t batch, int64_t M, int64_t N, int64_t K) {
+    return batch >= 1 && M >= 1 && N >= 1 && K >= 0;
+}
+
+/*
+ * Batched plain GEMM: batch independent problems stored contiguously
+ * (strides M*K, N*K and M*N elements).  dtype is OR_F16, OR_BF16 or OR_F32.
+ * ref / abssum (either may be NULL) receive batch*M*N fp64 values.
+ */
+int oracle_gemm_tn(int dtype, const void* A, const void* B, int64_t batch, int64_t M, int64_t N,
+                   int64_t K, double* ref, double* abssum, int nthreads) {
+    if (!(dtype == OR_F16 || dtype == OR_BF16 || dtype == OR_F32) || !A || !B ||
+        !shape_ok(batch, M, N, K))
+        return -1;
+    int es = elem_size(dtype);
+    for (int64_t p = 0; p < batch; ++p) {
+        int rc = gemm_one(dtype, (const char*)A + p * M * K * es, (const char*)B + p * N * K * es,
+                          NULL, NULL, M, N, K, ref ? ref + p * M * N : NULL,
+                          abssum ? abssum + p * M * N : NULL, nthreads);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}
+
+/* MX block-scaled GEMM: E4M3 elements, one E8M0 scale per 32 consecutive K
+ * elements of every row of A (SA: M x K/32) and of B (SB: N x K/32). */
+int oracle_gemm_mx(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const uint8_t* SB,
+                   int64_t M, int64_t N, int64_t K, double* ref, double* abssum, int nthreads) {
+    if (!A || !B || !SA || !SB || !shape_ok(1, M, N, K) || K % 32 != 0)
+        return -1;
+    return gemm_one(OR_E4M3, A, B, SA, SB, M, N, K, ref, abssum, nthreads);
+}
+
+/*
+ * Selected entries only, for problems too large to compute whole: entry t is
+ * (row ii[t], column jj[t]) of problem bb[t] (bb may be NULL for batch 1).
+ * SA/SB non-NULL selects the MX definition (dtype must then be OR_E4M3).
+ */
+int oracle_entries(int dtype, const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
+                   int64_t M, int64_t N, int64_t K, const int64_t* bb, const int64_t* ii,
+                   const int64_t* jj, int64_t n, double* ref, double* abssum) {
+    if (!elem_size(dtype) || !A || !B || !ii || !jj || !shape_ok(1, M, N, K) ||
+        ((SA || SB) && (!SA || !SB || dtype != OR_E4M3 || K % 32 != 0)))
+        return -1;
+    int es = elem_size(dtype);
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t p = bb ? bb[t] : 0, i = ii[t], j = jj[t];
+        if (p < 0 || i < 0 || i >= M || j < 0 || j >= N || (SA && p != 0))
+            return -1;
+        const char* Ap = (const char*)A + p * M * K * es;
+        const char* Bp = (const char*)B + p * N * K * es;
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double prod = operand_value(dtype, Ap, SA, K, i, k) * operand_value(dtype, Bp, SB, K, j, k);
+            s += prod;
+            sa += fabs(prod);
+        }
+        if (ref)
+            ref[t] = s;
+        if (abssum)
+            abssum[t] = sa;
+    }
+    return 0;
+}

@@ -1,0 +1,210 @@
+"""Plain fp64 CPU oracle for Out = A . B^T (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  The product library never does: the
+oracle shares no code with the HIP path, and the HIP path never falls back to
+it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, sequential sums over K,
+threads over output rows).  This wrapper builds it with gcc, passes raw input
+storage through ctypes, and holds the elementwise comparison rule:
+
+    |gpu - ref| <= 1e-4 * sum_k |a_ik * b_jk|  (+ one bf16 ulp of ref when the
+                                                 output is bf16)
+
+The rule states the accuracy expected of an fp32-accumulating product whose
+element products are exact ("Blackwell Tensor Cores", The Accumulator's
+Lifetime: float16 products accumulated in float32).  Its bf16 ulp term covers
+the single rounding of the fp32 result to a bf16 output.
+
+Inputs are numpy arrays holding the raw storage of the operands:
+uint16 for float16 / bfloat16 bit patterns, uint8 for E4M3 and E8M0 bytes,
+float32 for float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+F16, BF16, F32, E4M3, E8M0 = 0, 1, 2, 3, 4
+DTYPE_NAMES = {"f16": F16, "bf16": BF16, "f32": F32, "e4m3": E4M3, "e8m0": E8M0}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so beside it (gcc, -O2, no fast-math so
+    the fp64 sums keep their sequential order)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra",
+             "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+            lib.oracle_decode.argtypes = [ctypes.c_int, vp, i64, dp]
+            lib.oracle_gemm_tn.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, i64, dp, dp,
+                                           ctypes.c_int]
+            lib.oracle_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, dp, dp, ctypes.c_int]
+            lib.oracle_entries.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, vp, vp,
+                                           vp, i64, dp, dp]
+            for f in (lib.oracle_decode, lib.oracle_gemm_tn, lib.oracle_gemm_mx,
+                      lib.oracle_entries):
+                f.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+_STORAGE = {F16: np.uint16, BF16: np.uint16, F32: np.float32, E4M3: np.uint8, E8M0: np.uint8}
+
+
+def _raw(x: np.ndarray, dtype: int) -> np.ndarray:
+    want = _STORAGE[dtype]
+    x = np.ascontiguousarray(x)
+    if x.dtype.itemsize != np.dtype(want).itemsize:
+        raise TypeError(f"storage of dtype {dtype} must be {np.dtype(want)}, got {x.dtype}")
+    return x
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data
+
+
+def decode(dtype: int, raw: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of stored elements (format definitions, see oracle.c)."""
+    raw = _raw(raw, dtype)
+    out = np.empty(raw.shape, dtype=np.float64)
+    rc = _load().oracle_decode(dtype, _ptr(raw), raw.size, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_decode failed ({rc})")
+    return out
+
+
+def gemm_tn(dtype: int, a: np.ndarray, b: np.ndarray, nthreads: int | None = None):
+    """ref, abssum for Out = A . B^T.  a: [batch,] M x K, b: [batch,] N x K raw
+    storage.  Returns fp64 arrays of shape [batch,] M x N."""
+    a, b = _raw(a, dtype), _raw(b, dtype)
+    batched = a.ndim == 3
+    if not batched:
+        a, b = a[None], b[None]
+    if a.ndim != 3 or b.ndim != 3 or a.shape[0] != b.shape[0] or a.shape[2] != b.shape[2]:
+        raise ValueError(f"bad shapes {a.shape} {b.shape}")
+    bt, M, K = a.shape
+    N = b.shape[1]
+    ref = np.empty((bt, M, N), np.float64)
+    s = np.empty((bt, M, N), np.float64)
+    rc = _load().oracle_gemm_tn(dtype, _ptr(a), _ptr(b), bt, M, N, K, _ptr(ref), _ptr(s),
+                                nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_gemm_tn failed ({rc})")
+    return (ref, s) if batched else (ref[0], s[0])
+
+
+def gemm_mx(a: np.ndarray, b: np.ndarray, sa: np.ndarray, sb: np.ndarray,
+            nthreads: int | None = None):
+    """ref, abssum for the MX block-scaled product: a M x K, b N x K E4M3 bytes;
+    sa M x K/32, sb N x K/32 E8M0 bytes."""
+    a, b, sa, sb = _raw(a, E4M3), _raw(b, E4M3), _raw(sa, E8M0), _raw(sb, E8M0)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or K % 32 or sa.shape != (M, K // 32) or sb.shape != (N, K // 32):
+        raise ValueError("bad MX shapes")
+    ref = np.empty((M, N), np.float64)
+    s = np.empty((M, N), np.float64)
+    rc = _load().oracle_gemm_mx(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K, _ptr(ref),
+                                _ptr(s), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_gemm_mx failed ({rc})")
+    return ref, s
+
+
+def entries(dtype: int, a: np.ndarray, b: np.ndarray, ii, jj, bb=None, sa=None, sb=None):
+    """ref, abssum at selected outputs (ii[t], jj[t]) [of problem bb[t]], each
+    computed one by one from the definition; for problems too big to do whole."""
+    a, b = _raw(a, dtype), _raw(b, dtype)
+    if a.ndim == 2:
+        a3, b3 = a[None], b[None]
+    else:
+        a3, b3 = a, b
+    _, M, K = a3.shape
+    N = b3.shape[1]
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    bbv = None if bb is None else np.ascontiguousarray(bb, dtype=np.int64)
+    if sa is not None:
+        sa, sb = _raw(sa, E8M0), _raw(sb, E8M0)
+    n = ii.size
+    ref = np.empty(n, np.float64)
+    s = np.empty(n, np.float64)
+    rc = _load().oracle_entries(dtype, _ptr(a3), _ptr(b3), _ptr(sa), _ptr(sb), M, N, K,
+                                _ptr(bbv), _ptr(ii), _ptr(jj), n, _ptr(ref), _ptr(s))
+    if rc:
+        raise ValueError(f"oracle_entries failed ({rc})")
+    return ref, s
+
+
+# ----------------------------------------------------------------------------
+# Comparison rule
+# ----------------------------------------------------------------------------
+REL_TOL = 1e-4
+
+
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 numbers at |x|: 2^(max(floor(log2|x|), -126) - 7),
+    and the subnormal spacing 2^-133 at zero (bfloat16 keeps 7 stored mantissa
+    bits and binary32's exponent range)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.full(x.shape, -126.0)
+    nz = x > 0
+    e[nz] = np.maximum(np.floor(np.log2(x[nz])), -126.0)
+    return np.exp2(e - 7.0)
+
+
+def bound(ref: np.ndarray, abssum: np.ndarray, out_bf16: bool) -> np.ndarray:
+    b = REL_TOL * np.asarray(abssum, np.float64)
+    if out_bf16:
+        b = b + ulp_bf16(ref)
+    return b
+
+
+def check(gpu: np.ndarray, ref: np.ndarray, abssum: np.ndarray, out_bf16: bool):
+    """Elementwise acceptance.  Returns (ok, max(err/bound), n_violations).
+    Any NaN or Inf in the GPU output is a violation."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if gpu.shape != ref.shape:
+        raise ValueError(f"shape mismatch {gpu.shape} vs {ref.shape}")
+    bnd = bound(ref, abssum, out_bf16)
+    err = np.abs(gpu - ref)
+    finite = np.isfinite(gpu)
+    bad = ~finite | (err > bnd)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bnd > 0, err / bnd, np.where(err > 0, np.inf, 0.0))
+    ratio = np.where(finite, ratio, np.inf)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    nbad = int(bad.sum())
+    return nbad == 0, worst, nbad

@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module draws random numbers and stores them in the operand formats; it
+holds none of the product's arithmetic, so both the fp64 oracle and the HIP
+path can read the very same bytes.  Every draw uses a CPU ``torch.Generator``
+seeded explicitly, in the order A, B, then the scale tensors.
+
+Workloads (sizes, formats and value distributions of the five measured
+problems):
+
+* ``tile_f16``   -- one tile, A 128x64 and B 64x64 float16, uniform [-1, 1],
+  seed 0, float32 output (the single-CTA example of "Blackwell Tensor Cores",
+  The Accumulator's Lifetime).
+* ``bf16_4096``  -- A, B 4096x4096 bfloat16, N(0,1)*0.1, seed 1, bf16 output.
+* ``batched``    -- 1024 problems of A 128x64, B 256x64 bfloat16, uniform
+  [-1, 1], seed 2, float32 output (the 128x256x64 bf16 tile of "API Card:
+  Blackwell Pipeline (tcgen05)", Descriptor.).
+* ``bf16_8192``  -- A, B 8192x8192 bfloat16, N(0,1)*0.05, seed 3, bf16 output.
+* ``mxfp8_8192`` -- A, B 8192x8192 E4M3 drawn N(0,1) then cast, one E8M0 scale
+  per 32 K elements per row with exponents uniform on the integers -4..4,
+  seed 4, bf16 output ("Hopper and Blackwell GEMM", block-scaling table).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+E8M0_BIAS = 127
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    M: int
+    N: int
+    K: int
+    dtype: str          # "f16", "bf16" or "e4m3" (MX block-scaled)
+    out_dtype: str      # "f32" or "bf16"
+    seed: int
+    dist: str           # "uniform" or "normal"
+    sigma: float = 1.0
+    scale_exp: tuple = field(default=(-4, 4))
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.M * self.N * self.K
+
+
+WORKLOADS = {
+    "tile_f16": Workload("tile_f16", 1, 128, 64, 64, "f16", "f32", 0, "uniform"),
+    "bf16_4096": Workload("bf16_4096", 1, 4096, 4096, 4096, "bf16", "bf16", 1, "normal", 0.1),
+    "batched": Workload("batched", 1024, 128, 256, 64, "bf16", "f32", 2, "uniform"),
+    "bf16_8192": Workload("bf16_8192", 1, 8192, 8192, 8192, "bf16", "bf16", 3, "normal", 0.05),
+    "mxfp8_8192": Workload("mxfp8_8192", 1, 8192, 8192, 8192, "e4m3", "bf16", 4, "normal", 1.0),
+}
+
+TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def generator(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return g
+
+
+def uniform(shape, gen, dtype) -> torch.Tensor:
+    """Uniform on [-1, 1] drawn in float32, then rounded to ``dtype``."""
+    return (torch.rand(shape, generator=gen, dtype=torch.float32) * 2 - 1).to(dtype)
+
+
+def normal(shape, gen, sigma, dtype) -> torch.Tensor:
+    """N(0, sigma^2) drawn in float32, then rounded to ``dtype``."""
+    return (torch.randn(shape, generator=gen, dtype=torch.float32) * sigma).to(dtype)
+
+
+def e4m3_normal(shape, gen, sigma=1.0) -> torch.Tensor:
+    """N(0, sigma^2) in float32, clamped to the E4M3 range, cast to E4M3; the
+    bytes are returned as uint8."""
+    x = torch.randn(shape, generator=gen, dtype=torch.float32) * sigma
+    return x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def e8m0_scales(shape, gen, lo=-4, hi=4) -> torch.Tensor:
+    """E8M0 bytes 127+s with s uniform on the integers lo..hi."""
+    return (torch.randint(lo, hi + 1, shape, generator=gen, dtype=torch.int32)
+            + E8M0_BIAS).to(torch.uint8)
+
+
+def quarter_integers(shape, gen, dtype) -> torch.Tensor:
+    """Values in {-1, -3/4, ..., 3/4, 1}: integers -4..4 divided by 4 (the input
+    structure of the 16x8x32 example in "mma.sync", Examples)."""
+    return (torch.randint(-4, 5, shape, generator=gen, dtype=torch.int32).float() / 4).to(dtype)
+
+
+def make(w: Workload | str) -> dict:
+    """CPU tensors for a workload: A, B (and SA, SB for MX)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    g = generator(w.seed)
+    lead = (w.batch,) if w.batch > 1 else ()
+    shp_a, shp_b = lead + (w.M, w.K), lead + (w.N, w.K)
+    if w.dtype == "e4m3":
+        a = e4m3_normal(shp_a, g, w.sigma)
+        b = e4m3_normal(shp_b, g, w.sigma)
+        lo, hi = w.scale_exp
+        sa = e8m0_scales((w.M, w.K // 32), g, lo, hi)
+        sb = e8m0_scales((w.N, w.K // 32), g, lo, hi)
+        return {"A": a, "B": b, "SA": sa, "SB": sb}
+    dt = TORCH_DTYPES[w.dtype]
+    if w.dist == "uniform":
+        a, b = uniform(shp_a, g, dt), uniform(shp_b, g, dt)
+    else:
+        a, b = normal(shp_a, g, w.sigma, dt), normal(shp_b, g, w.sigma, dt)
+    return {"A": a, "B": b}
+
+
+def raw(t: torch.Tensor):
+    """The storage of a CPU tensor as a numpy array of unsigned integers
+    (uint16 for 16-bit formats, uint8 for bytes), for the oracle."""
+    t = t.contiguous()
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16).numpy().view("uint16")
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn, torch.float8_e8m0fnu):
+        return t.view(torch.uint8).numpy()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError(f"no raw view for {t.dtype}")

@@ -1,0 +1,306 @@
+"""Pins of the fp64 oracle against facts fixed outside it (CPU only).
+
+Each check is chosen so that a plausible slip in the oracle -- a wrong
+decoder bit, a dropped K term, a transposed or swapped operand, a scale
+applied to the wrong block -- fails at least one of them:
+
+* decoders: every bit pattern of float16, bfloat16, E4M3 and E8M0 against
+  torch's own casts to float64 (an independent library routine);
+* brute force: exact rational sums (fractions.Fraction) on tiny random shapes;
+* identity / permutation operands: the output is a transposed or permuted
+  copy of an input, bit for bit;
+* all-ones operands: the closed form K (and its MX analogue with scales);
+* quarter-integer operands (the input structure of the 16x8x32 example on the
+  "mma.sync" page, Examples): exact integer arithmetic;
+* invariants: transpose symmetry, power-of-two linearity, batch slices, MX
+  with unit scales equals the plain E4M3 product, uniform scale shifts.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from tensor_core_matrix_amd import inputs as inp
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _same(x, y):
+    """Bitwise-equal float64 arrays, NaN matching NaN."""
+    x, y = np.asarray(x, np.float64), np.asarray(y, np.float64)
+    return x.shape == y.shape and bool(np.all((x == y) | (np.isnan(x) & np.isnan(y))))
+
+
+# ---------------------------------------------------------------- decoders
+def test_decode_f16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.float16).double().numpy()
+    assert _same(orc.decode(orc.F16, bits), want)
+
+
+def test_decode_bf16_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert _same(orc.decode(orc.BF16, bits), want)
+
+
+def test_decode_e4m3_all_patterns():
+    bits = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(bits).view(torch.float8_e4m3fn).double().numpy()
+    got = orc.decode(orc.E4M3, bits)
+    assert _same(got, want)
+    assert np.nanmax(got) == 448.0 and np.isnan(got).sum() == 2  # 0x7F, 0xFF
+
+
+def test_decode_e8m0_all_patterns():
+    bits = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(bits).view(torch.float8_e8m0fnu).float().double().numpy()
+    got = orc.decode(orc.E8M0, bits)
+    assert _same(got, want)
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and np.isnan(got[255])
+
+
+# ------------------------------------------------------------- brute force
+def _exact(av, bv):
+    """Exact rational A . B^T from float64-representable values."""
+    M, K = av.shape
+    N = bv.shape[0]
+    out = [[sum((Fraction(float(av[i, k])) * Fraction(float(bv[j, k])) for k in range(K)),
+                Fraction(0)) for j in range(N)] for i in range(M)]
+    return out
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (8, 2, 16), (5, 8, 3)])
+def test_brute_force_plain(dt, shape):
+    M, N, K = shape
+    g = inp.generator(11 + M * 100 + N * 10 + K)
+    tdt = inp.TORCH_DTYPES[dt]
+    a = inp.normal((M, K), g, 3.0, tdt)
+    b = inp.normal((N, K), g, 3.0, tdt)
+    ref, s = orc.gemm_tn(orc.DTYPE_NAMES[dt], inp.raw(a), inp.raw(b))
+    ex = _exact(a.double().numpy(), b.double().numpy())
+    for i in range(M):
+        for j in range(N):
+            assert abs(Fraction(ref[i, j]) - ex[i][j]) <= Fraction(K * 2.0 ** -52) * Fraction(s[i, j])
+    # abssum is the exact |.| sum up to the same rounding
+    absx = _exact(np.abs(a.double().numpy()), np.abs(b.double().numpy()))
+    for i in range(M):
+        for j in range(N):
+            assert abs(Fraction(s[i, j]) - absx[i][j]) <= Fraction(K * 2.0 ** -52) * absx[i][j]
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (3, 4, 64), (4, 2, 96)])
+def test_brute_force_mx(shape):
+    M, N, K = shape
+    g = inp.generator(5 + K)
+    a = inp.e4m3_normal((M, K), g)
+    b = inp.e4m3_normal((N, K), g)
+    sa = inp.e8m0_scales((M, K // 32), g, -6, 6)
+    sb = inp.e8m0_scales((N, K // 32), g, -6, 6)
+    ref, s = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb))
+    av = a.view(torch.float8_e4m3fn).double().numpy()
+    bv = b.view(torch.float8_e4m3fn).double().numpy()
+    ea = sa.numpy().astype(np.int64) - 127
+    eb = sb.numpy().astype(np.int64) - 127
+    for i in range(M):
+        for j in range(N):
+            ex = sum((Fraction(float(av[i, k])) * Fraction(2) ** int(ea[i, k // 32])
+                      * Fraction(float(bv[j, k])) * Fraction(2) ** int(eb[j, k // 32])
+                      for k in range(K)), Fraction(0))
+            assert abs(Fraction(ref[i, j]) - ex) <= Fraction(K * 2.0 ** -52) * Fraction(s[i, j])
+
+
+# ------------------------------------------------- identity / permutation
+def test_identity_left_gives_transpose_of_b():
+    K, N = 48, 40
+    g = inp.generator(21)
+    a = torch.eye(K, dtype=torch.bfloat16)
+    b = inp.normal((N, K), g, 1.0, torch.bfloat16)
+    ref, _ = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    assert _same(ref, b.double().numpy().T)  # Out[i, j] = B[j, i]
+
+
+def test_identity_right_gives_a():
+    M, K = 33, 24
+    g = inp.generator(22)
+    a = inp.normal((M, K), g, 1.0, torch.float16)
+    b = torch.eye(K, dtype=torch.float16)
+    ref, _ = orc.gemm_tn(orc.F16, inp.raw(a), inp.raw(b))
+    assert _same(ref, a.double().numpy())
+
+
+def test_permutation_permutes_columns():
+    M, K = 17, 32
+    g = inp.generator(23)
+    a = inp.normal((M, K), g, 1.0, torch.bfloat16)
+    perm = torch.randperm(K, generator=g)
+    b = torch.zeros(K, K, dtype=torch.bfloat16)
+    b[torch.arange(K), perm] = 1  # B[j, perm[j]] = 1
+    ref, _ = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    assert _same(ref, a.double().numpy()[:, perm.numpy()])  # Out[i, j] = A[i, perm[j]]
+
+
+# ------------------------------------------------------------ closed forms
+@pytest.mark.parametrize("K", [1, 64, 1000])
+def test_all_ones_is_k(K):
+    a = torch.ones(5, K, dtype=torch.bfloat16)
+    b = torch.ones(7, K, dtype=torch.bfloat16)
+    ref, s = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    assert np.all(ref == K) and np.all(s == K)
+
+
+def test_all_ones_mx_closed_form():
+    M, N, K = 6, 5, 128
+    g = inp.generator(24)
+    one = 0x38  # E4M3 1.0: exponent field 7 (bias 7), mantissa 0
+    a = torch.full((M, K), one, dtype=torch.uint8)
+    b = torch.full((N, K), one, dtype=torch.uint8)
+    sa = inp.e8m0_scales((M, K // 32), g, -4, 4)
+    sb = inp.e8m0_scales((N, K // 32), g, -4, 4)
+    ref, _ = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb))
+    ea = sa.numpy().astype(np.int64) - 127
+    eb = sb.numpy().astype(np.int64) - 127
+    want = np.array([[sum(32 * 2.0 ** (ea[i, q] + eb[j, q]) for q in range(K // 32))
+                      for j in range(N)] for i in range(M)])
+    assert _same(ref, want)
+
+
+# -------------------------------------------------------- quarter integers
+def test_quarter_integer_page_example_exact():
+    """The 16x8x32 example's input recipe (numpy default_rng(0), integers in
+    [-4, 5) divided by 4, float16): every partial sum is a multiple of 1/16, so
+    the exact result is an integer product divided by 16."""
+    rng = np.random.default_rng(0)
+    ai = rng.integers(-4, 5, (16, 32))
+    bi = rng.integers(-4, 5, (8, 32))
+    a = (ai / 4).astype("float16")
+    b = (bi / 4).astype("float16")
+    ref, _ = orc.gemm_tn(orc.F16, a.view("uint16"), b.view("uint16"))
+    assert _same(ref, (ai @ bi.T) / 16.0)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_quarter_integer_tile_exact(dt):
+    M, N, K = 128, 64, 64
+    g = inp.generator(25)
+    a = inp.quarter_integers((M, K), g, inp.TORCH_DTYPES[dt])
+    b = inp.quarter_integers((N, K), g, inp.TORCH_DTYPES[dt])
+    ai = (a.float() * 4).round().long().numpy()
+    bi = (b.float() * 4).round().long().numpy()
+    ref, _ = orc.gemm_tn(orc.DTYPE_NAMES[dt], inp.raw(a), inp.raw(b))
+    assert _same(ref, (ai @ bi.T) / 16.0)
+
+
+# --------------------------------------------------------------- invariants
+def test_transpose_symmetry_and_linearity():
+    g = inp.generator(26)
+    a = inp.normal((19, 40), g, 1.0, torch.bfloat16)
+    b = inp.normal((23, 40), g, 1.0, torch.bfloat16)
+    r_ab, _ = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    r_ba, _ = orc.gemm_tn(orc.BF16, inp.raw(b), inp.raw(a))
+    assert _same(r_ab, r_ba.T)
+    r_2a, _ = orc.gemm_tn(orc.BF16, inp.raw(a * 2), inp.raw(b))
+    assert _same(r_2a, 2 * r_ab)
+
+
+def test_batch_slices_equal_single_problems():
+    g = inp.generator(27)
+    a = inp.uniform((3, 9, 16), g, torch.bfloat16)
+    b = inp.uniform((3, 11, 16), g, torch.bfloat16)
+    rb, sb = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    for p in range(3):
+        r1, s1 = orc.gemm_tn(orc.BF16, inp.raw(a[p]), inp.raw(b[p]))
+        assert _same(rb[p], r1) and _same(sb[p], s1)
+
+
+def test_mx_unit_scales_equal_plain_e4m3_and_shift():
+    M, N, K = 7, 6, 64
+    g = inp.generator(28)
+    a = inp.e4m3_normal((M, K), g)
+    b = inp.e4m3_normal((N, K), g)
+    unit_a = torch.full((M, K // 32), 127, dtype=torch.uint8)
+    unit_b = torch.full((N, K // 32), 127, dtype=torch.uint8)
+    r_mx, _ = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(unit_a), inp.raw(unit_b))
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    r_plain, _ = orc.entries(orc.E4M3, inp.raw(a), inp.raw(b), ii.ravel(), jj.ravel())
+    assert _same(r_mx.ravel(), r_plain)
+    # shifting every A scale by +3 and every B scale by -1 multiplies by 2^2
+    r_sh, _ = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(unit_a + 3), inp.raw(unit_b - 1))
+    assert _same(r_sh, 4 * r_mx)
+    # a scale change in one block touches only that block's terms
+    sa = unit_a.clone()
+    sa[2, 1] = 127 + 5
+    r_blk, _ = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(unit_b))
+    av = a.view(torch.float8_e4m3fn).double().numpy()
+    bv = b.view(torch.float8_e4m3fn).double().numpy()
+    delta = (2.0 ** 5 - 1) * (av[2, 32:64] @ bv[:, 32:64].T)
+    assert np.allclose(r_blk[2] - r_mx[2], delta, rtol=0, atol=1e-12)
+    assert _same(np.delete(r_blk, 2, 0), np.delete(r_mx, 2, 0))
+
+
+def test_entries_match_full_product():
+    g = inp.generator(29)
+    a = inp.normal((2, 13, 24), g, 1.0, torch.float16)
+    b = inp.normal((2, 9, 24), g, 1.0, torch.float16)
+    full, fs = orc.gemm_tn(orc.F16, inp.raw(a), inp.raw(b))
+    bb = np.array([0, 1, 1, 0])
+    ii = np.array([0, 12, 5, 7])
+    jj = np.array([8, 0, 3, 4])
+    r, s = orc.entries(orc.F16, inp.raw(a), inp.raw(b), ii, jj, bb=bb)
+    assert _same(r, full[bb, ii, jj]) and _same(s, fs[bb, ii, jj])
+
+
+def test_nan_inputs_propagate():
+    a = torch.ones(2, 8, dtype=torch.bfloat16)
+    a[1, 3] = float("nan")
+    b = torch.ones(3, 8, dtype=torch.bfloat16)
+    ref, _ = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    assert np.all(ref[0] == 8) and np.all(np.isnan(ref[1]))
+
+
+# -------------------------------------------- planted mistakes are caught
+def test_planted_mistakes_fail_the_pins():
+    """Planted on the CPU: reading B as K x N (A . B instead of A . B^T) or a
+    dropped K term must break the permutation and closed-form pins above."""
+    M, K = 17, 32
+    g = inp.generator(30)
+    a = inp.normal((M, K), g, 1.0, torch.bfloat16)
+    perm = torch.randperm(K, generator=g)
+    b = torch.zeros(K, K, dtype=torch.bfloat16)
+    b[torch.arange(K), perm] = 1
+    want = a.double().numpy()[:, perm.numpy()]
+    untransposed, _ = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b.T.contiguous()))  # A . B
+    assert not _same(untransposed, want)
+    dropped, _ = orc.gemm_tn(orc.BF16, inp.raw(torch.ones(3, 63, dtype=torch.bfloat16)),
+                             inp.raw(torch.ones(4, 63, dtype=torch.bfloat16)))
+    assert not np.all(dropped == 64)
+
+
+# ------------------------------------------------------- comparison rule
+def test_ulp_bf16_matches_bit_spacing():
+    g = inp.generator(31)
+    v = inp.normal((4096,), g, 10.0, torch.bfloat16).abs()
+    v = v[(v > 0) & torch.isfinite(v)]
+    bits = v.view(torch.int16).numpy().astype(np.int32)
+    up = torch.from_numpy((bits + 1).astype(np.int16)).view(torch.bfloat16).double().numpy()
+    spacing = up - v.double().numpy()
+    assert _same(orc.ulp_bf16(v.double().numpy()), spacing)
+    tiny = np.array([0.0, 2.0 ** -130, 2.0 ** -126])
+    assert _same(orc.ulp_bf16(tiny), np.full(3, 2.0 ** -133))
+
+
+def test_check_rule():
+    ref = np.array([1.0, -2.0, 0.0, 100.0])
+    s = np.array([10.0, 10.0, 0.0, 1000.0])
+    ok, worst, nbad = orc.check(ref + np.array([9e-4, -9e-4, 0.0, 0.09]), ref, s, False)
+    assert ok and nbad == 0 and worst < 1
+    ok, _, nbad = orc.check(ref + np.array([2e-3, 0, 0, 0]), ref, s, False)
+    assert not ok and nbad == 1
+    ok, _, nbad = orc.check(np.array([1.0, -2.0, np.nan, 100.0]), ref, s, False)
+    assert not ok and nbad == 1
+    # bf16 output: one ulp of 100 (0.5) is allowed on top of 1e-4 * 1000
+    ok, _, _ = orc.check(ref + np.array([0, 0, 0, 0.55]), ref, s, True)
+    assert ok
