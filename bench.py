@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled product Out = A . B^T on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-seconds S]
+
+A step is one call of the product on the headline workload: bfloat16
+8192 x 8192 x 8192, fp32 accumulation, bf16 output (persistent 256 x 256 x 64
+tiles), inputs N(0,1)*0.05 from seed 3, already resident in HBM.  The other
+measured workloads (MXFP8 8192^3, bf16 4096^3, 1024 batched 128x256x64 and
+the 128x64x64 single tile) are timed after it and reported in the same line.
+
+Prints ONE JSON line.  `roofline` describes the dominant kernel: achieved =
+algorithmic flops per launch / mean launch time (HIP events on the launch
+stream), against the dense bf16 MFMA peak.  `roofline.traffic` is the HBM
+bytes per launch measured with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
+scaled by a copy kernel's reading) when profiles/traffic.json was taken on
+the current kernel sources, else null.  `cpu_baseline` is the fp64 oracle
+timed on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s and % of MFMA dense peak (bf16 8192³; MXFP8 8192³)"
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}   # dense MFMA, MI355X
+HBM_GBS = 8000.0
+KERNEL_SOURCES = ["gemm_kernel.h", "tcm_device.h", "tcm_internal.h", "gemm_tn.hip",
+                  "gemm_mx.hip", "tcm_api.cpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tensor_core_matrix_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle's CPU sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", default=None, help="time a single workload (profiling runs)")
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, torch):
+    """Mean ms per call over `steps` back-to-back calls on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def prepare(name, torch, inp, tcm):
+    w = inp.WORKLOADS[name]
+    x = {k: v.to("cuda") for k, v in inp.make(w).items()}
+    odt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+    if w.dtype == "e4m3":
+        out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
+        fn = lambda: tcm.gemm_mx_fp8(x["A"], x["B"], x["SA"], x["SB"], out)
+    elif w.batch > 1:
+        out = torch.empty(w.batch, w.M, w.N, dtype=odt, device="cuda")
+        fn = lambda: tcm.batched_gemm_tn(x["A"], x["B"], out)
+    else:
+        out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
+        fn = lambda: tcm.gemm_tn(x["A"], x["B"], out)
+    nbytes = sum(v.numel() * v.element_size() for v in x.values()) + out.numel() * out.element_size()
+    return w, fn, nbytes, x
+
+
+def cpu_baseline(target_s: float):
+    """The fp64 oracle as it stands, on whole rows of the 8192^3 bf16 product."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    from tensor_core_matrix_amd import inputs as inp
+
+    w = inp.WORKLOADS["bf16_8192"]
+    x = inp.make(w)
+    a, b = inp.raw(x["A"]), inp.raw(x["B"])
+    threads = orc.default_threads()
+
+    def run(rows):
+        t0 = time.perf_counter()
+        orc.gemm_tn(orc.BF16, a[:rows], b, nthreads=threads)
+        return time.perf_counter() - t0
+
+    # Each call decodes all of B once, then computes `rows` whole output rows:
+    # two short calls give the fixed and the per-row cost, which sizes the
+    # measured call to last about target_s.
+    r1, r2 = threads, 3 * threads
+    t1, t2 = run(r1), run(r2)
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    fixed = max(t1 - r1 * per_row, 0.0)
+    rows2 = int(max(r2, min(w.M, (target_s - fixed) / per_row)))
+    rows2 = max(threads, rows2 - rows2 % threads)
+    dt = run(rows2)
+    flops = 2.0 * rows2 * w.N * w.K
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows2 - 1} of the 8192^3 bf16 product ({rows2}x8192 outputs, "
+                      f"full K, fp64), {dt:.1f} s wall on {threads} threads ({cpu})",
+            "seconds": dt}
+
+
+def load_traffic(workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    entry = t.get(workload)
+    if not entry or entry.get("kernel_hash") != kernel_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the product needs no exchange between GPUs and no multi-GPU path is built",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    import tensor_core_matrix_amd as tcm
+    from tensor_core_matrix_amd import inputs as inp
+
+    tcm.lib()
+    order = ["bf16_8192", "mxfp8_8192", "bf16_4096", "batched", "tile_f16"]
+    if args.only:
+        order = [args.only]
+    results = {}
+    for name in order:
+        w, fn, nbytes, keep = prepare(name, torch, inp, tcm)
+        steps = args.steps if name == order[0] else max(5, args.steps // 2)
+        if name == "tile_f16":
+            steps = max(steps, 200)
+        ms = timed(fn, steps, args.warmup, torch)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        results[name] = {
+            "ms": ms, "tflops": tflops, "steps": steps,
+            "frac_of_peak": tflops / PEAK_TFLOPS[w.dtype],
+            "gbs": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes,
+            "plan": tcm.plan(w.M, w.N, w.K, batch=w.batch, mx=w.dtype == "e4m3",
+                             dtype=tcm.F16 if w.dtype == "f16" else tcm.BF16,
+                             out_dtype=tcm.BF16 if w.out_dtype == "bf16" else tcm.F32,
+                             num_cus=0),
+        }
+        print(f"[bench] {name}: {ms:.4f} ms/call, {tflops:.1f} TFLOP/s", file=sys.stderr,
+              flush=True)
+        del keep, fn
+        torch.cuda.empty_cache()
+
+    head = order[0]
+    hw = inp.WORKLOADS[head]
+    r = results[head]
+    bound = "hbm" if head == "batched" else "mfma"
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_TFLOPS[hw.dtype],
+                "unit": "TFLOP/s", "frac": r["frac_of_peak"], "traffic": load_traffic(head)}
+    else:
+        roof = {"bound": "hbm", "achieved": r["gbs"], "peak": HBM_GBS, "unit": "GB/s",
+                "frac": r["gbs"] / HBM_GBS, "traffic": load_traffic(head)}
+    line = {
+        "metric": METRIC,
+        "value": r["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": r["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": r["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if hw.dtype != "e4m3" else "e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{head}: M=N=K={hw.M} TN, {hw.dtype} in, fp32 accumulate, "
+                               f"{hw.out_dtype} out, seed {hw.seed}",
+                   "tile": [r["plan"]["tile_m"], r["plan"]["tile_n"], r["plan"]["tile_k"]],
+                   "stages": r["plan"]["stages"], "grid": r["plan"]["grid"],
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "workloads": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                          for kk, vv in v.items() if kk != "plan"} for k, v in results.items()},
+    }
+    if not args.no_cpu and not args.only:
+        print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,138 @@
+/*
+ * tcm.h -- C ABI of libtcm, a tiled dense matrix product Out = A . B^T for
+ * AMD Instinct MI355X (gfx950), written in HIP for the CDNA4 matrix cores.
+ *
+ * The operation is the one the pages state:
+ *   - "Blackwell Tensor Cores" (TVM TIRx guide), "The Accumulator's Lifetime":
+ *     Out = A @ B.T, float16 inputs, float32 accumulation and output; the
+ *     first MMA of a tile ignores the accumulator, so Out is overwritten
+ *     (there is no C input and no alpha/beta).
+ *   - "API Card: Blackwell Pipeline (tcgen05)" (cuBLASDx), "Descriptor." and
+ *     "Host side.": row-major A (M x K), column-major B (K x N, i.e. stored
+ *     N x K, "K-major"), row-major C (the TN arrangement); 16-byte alignment
+ *     of A, B and C; bfloat16 inputs with float accumulation; batched
+ *     problems as in its batched example.
+ *   - "Hopper and Blackwell GEMM", Concept "FP8 and FP4, with block scaling"
+ *     and its format table: MXFP8 = E4M3 elements with one E8M0 (power of
+ *     two) scale per 32 consecutive elements of every row of A and column of
+ *     B^T, the scales applied inside the product.
+ *
+ * Conventions shared by every entry point
+ *   Layout     A: M x K row-major (leading dimension K).  B: N x K row-major
+ *              (leading dimension K).  Out: M x N row-major (leading dimension
+ *              N).  Batched operands are contiguous: problem p starts at
+ *              p*M*K, p*N*K and p*M*N elements.
+ *   Pointers   device pointers (hipMalloc'ed or torch CUDA tensors) on the
+ *              current HIP device.  The caller owns all buffers; the library
+ *              never allocates, frees or retains them and keeps no per-call
+ *              device state.
+ *   Alignment  A, B and Out must be 16-byte aligned, and every row of A and
+ *              B must be a whole number of 16-byte chunks (K * element size
+ *              % 16 == 0); otherwise TCM_ERR_MISALIGNED.  Scale tensors need
+ *              no alignment.
+ *   Shapes     batch, M, N >= 0 and K >= 0.  A call with batch, M or N equal
+ *              to 0 writes nothing and returns TCM_OK.  K == 0 writes zeros.
+ *              Sizes whose products overflow, or negative sizes, give
+ *              TCM_ERR_INVALID_SHAPE.  K > 2^20 gives TCM_ERR_UNSUPPORTED_SHAPE.
+ *              Ragged M and N (not multiples of the tile) are masked.
+ *   Execution  every call is asynchronous on `stream` (a hipStream_t; NULL is
+ *              the default stream) and does not synchronize.  All arguments
+ *              are validated on the host before any HIP call, so invalid
+ *              calls return an error without touching the device.  A launch
+ *              failure gives TCM_ERR_HIP.  No call falls back silently to
+ *              another algorithm: an unsupported request is an error.
+ *   Accuracy   element products are exact in fp32; sums are fp32.  The
+ *              result r satisfies |r - exact| <= 1e-4 * sum_k |a_ik b_jk| for
+ *              fp32 output, plus one bf16 ulp of the exact value for bf16
+ *              output (fp32 -> bf16 is round-to-nearest-even).
+ *   Threads    thread-safe: the only global state is a per-device cache of
+ *              device properties filled once.
+ */
+#ifndef TCM_H
+#define TCM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tcm_status {
+    TCM_OK = 0,
+    TCM_ERR_NULL_POINTER = 1,      /* a required pointer is NULL */
+    TCM_ERR_INVALID_SHAPE = 2,     /* negative size or size products overflow */
+    TCM_ERR_UNSUPPORTED_SHAPE = 3, /* valid but not handled (K > 2^20, MX K % 32) */
+    TCM_ERR_MISALIGNED = 4,        /* pointer or row length not 16-byte aligned */
+    TCM_ERR_UNSUPPORTED_DTYPE = 5, /* dtype / out_dtype pair not supported */
+    TCM_ERR_NO_DEVICE = 6,         /* no HIP device, or it is not gfx950 */
+    TCM_ERR_HIP = 7                /* a HIP runtime call or kernel launch failed */
+} tcm_status;
+
+typedef enum tcm_dtype {
+    TCM_F16 = 0,  /* IEEE binary16 */
+    TCM_BF16 = 1, /* bfloat16 */
+    TCM_F32 = 2,  /* IEEE binary32 */
+    TCM_E4M3 = 3, /* OCP FP8 E4M3 ("FN": no infinities, max 448) */
+    TCM_E8M0 = 4  /* OCP E8M0 scale: 2^(e-127), 0xFF = NaN */
+} tcm_dtype;
+
+/*
+ * Out = A . B^T for one problem.
+ *   A        M x K elements of `dtype` (TCM_F16 or TCM_BF16)
+ *   B        N x K elements of `dtype`
+ *   Out      M x N elements of `out_dtype` (TCM_F32 or TCM_BF16), overwritten
+ * Supported pairs: (F16, F32), (F16, BF16), (BF16, F32), (BF16, BF16).
+ */
+tcm_status tcm_gemm_tn(const void* A, const void* B, void* Out, int64_t M, int64_t N, int64_t K,
+                       tcm_dtype dtype, tcm_dtype out_dtype, void* stream);
+
+/*
+ * `batch` independent problems Out[p] = A[p] . B[p]^T, stored contiguously
+ * (strides M*K, N*K, M*N elements).  Same dtypes and rules as tcm_gemm_tn;
+ * the batched example of "API Card: Blackwell Pipeline (tcgen05)" (intro and
+ * Descriptor.: a 128 x 256 x 64 bfloat16 tile, float accumulation, 16-byte
+ * alignment) is this call with M = 128, N = 256, K = 64.
+ */
+tcm_status tcm_batched_gemm_tn(const void* A, const void* B, void* Out, int64_t batch, int64_t M,
+                               int64_t N, int64_t K, tcm_dtype dtype, tcm_dtype out_dtype,
+                               void* stream);
+
+/*
+ * MXFP8 block-scaled Out = (A * SA) . (B * SB)^T.
+ *   A        M x K E4M3 bytes;  B  N x K E4M3 bytes
+ *   scale_A  M x (K/32) E8M0 bytes, row-major: scale_A[i][q] multiplies
+ *            A[i][32q .. 32q+31]
+ *   scale_B  N x (K/32) E8M0 bytes: scale_B[j][q] multiplies B[j][32q .. 32q+31]
+ *   Out      M x N of `out_dtype` (TCM_F32 or TCM_BF16)
+ * K must be a multiple of 32 (TCM_ERR_UNSUPPORTED_SHAPE otherwise).  A NaN
+ * scale (0xFF) or element makes the affected outputs NaN.
+ */
+tcm_status tcm_gemm_mx_fp8(const void* A, const void* B, const void* scale_A, const void* scale_B,
+                           void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
+                           void* stream);
+
+/* What a call with these arguments would launch (host only: no HIP call when
+ * num_cus > 0; num_cus == 0 asks the current device for its CU count). */
+typedef struct tcm_plan {
+    int32_t tile_m, tile_n, tile_k; /* output tile and K slice per stage */
+    int32_t stages;                 /* depth of the LDS operand ring */
+    int32_t threads;                /* threads per workgroup */
+    int32_t stage_bytes;            /* LDS bytes of one stage (A tile + B tile) */
+    int32_t lds_bytes;              /* LDS bytes per workgroup */
+    int32_t grid;                   /* workgroups launched (persistent when < tiles) */
+    int64_t tiles;                  /* output tiles over all problems */
+    int32_t kernel;                 /* internal kernel variant id */
+} tcm_plan;
+
+/* mx != 0 plans tcm_gemm_mx_fp8 (dtype is then ignored). */
+tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
+                         tcm_dtype out_dtype, int mx, int num_cus, tcm_plan* plan);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* tcm_status_string(tcm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TCM_H */

@@ -1,0 +1,175 @@
+"""tensor_core_matrix_amd -- tiled Out = A . B^T on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libtcm.so`` (C ABI declared in ``include/tcm.h``):
+it only marshals torch tensors into pointers, sizes, dtype codes and the
+current HIP stream.  Every step of the product runs in the library's HIP
+kernels; there is no fallback.  If the library is missing, every call raises.
+
+    gemm_tn(a, b, out=None, out_dtype=None)            a: M x K, b: N x K
+    batched_gemm_tn(a, b, out=None, out_dtype=None)    a: B x M x K, b: B x N x K
+    gemm_mx_fp8(a, b, scale_a, scale_b, out=None, out_dtype=torch.bfloat16)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["gemm_tn", "batched_gemm_tn", "gemm_mx_fp8", "plan", "lib", "TcmError", "LIB_PATH",
+           "F16", "BF16", "F32", "E4M3", "E8M0"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtcm.so")
+
+# tcm_dtype codes
+F16, BF16, F32, E4M3, E8M0 = 0, 1, 2, 3, 4
+
+
+class TcmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("tile_k", ctypes.c_int32), ("stages", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("stage_bytes", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("tiles", ctypes.c_int64), ("kernel", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lock = threading.Lock()
+_lib = None
+EXPORTS = ("tcm_gemm_tn", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8", "tcm_plan_gemm",
+           "tcm_status_string")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtcm (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: build it with "
+                                  "`python -m tensor_core_matrix_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+            L.tcm_gemm_tn.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+            L.tcm_batched_gemm_tn.argtypes = [vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
+            L.tcm_gemm_mx_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
+            L.tcm_plan_gemm.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(Plan)]
+            L.tcm_status_string.argtypes = [ci]
+            L.tcm_status_string.restype = ctypes.c_char_p
+            for f in ("tcm_gemm_tn", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8", "tcm_plan_gemm"):
+                getattr(L, f).restype = ci
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().tcm_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise TcmError(status, status_string(status))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _code(dt) -> int:
+    torch = _torch()
+    table = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32,
+             torch.uint8: E4M3, torch.float8_e4m3fn: E4M3}
+    if dt not in table:
+        raise TypeError(f"unsupported dtype {dt}")
+    return table[dt]
+
+
+def _ptr(t) -> int:
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def gemm_tn(a, b, out=None, out_dtype=None):
+    """Out = a . b^T; a (M, K), b (N, K) float16/bfloat16 CUDA tensors."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError(f"K mismatch: {tuple(a.shape)} vs {tuple(b.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be {(M, N)}")
+    if a.dtype != b.dtype:
+        raise TypeError("a and b must have the same dtype")
+    with torch.cuda.device(a.device):
+        _check(lib().tcm_gemm_tn(_ptr(a), _ptr(b), _ptr(out), M, N, K, _code(a.dtype),
+                                 _code(out.dtype), _stream(a)))
+    return out
+
+
+def batched_gemm_tn(a, b, out=None, out_dtype=None):
+    """out[p] = a[p] . b[p]^T; a (batch, M, K), b (batch, N, K)."""
+    torch = _torch()
+    bt, M, K = a.shape
+    if b.shape[0] != bt or b.shape[2] != K:
+        raise ValueError(f"shape mismatch: {tuple(a.shape)} vs {tuple(b.shape)}")
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((bt, M, N), dtype=out_dtype or torch.float32, device=a.device)
+    if tuple(out.shape) != (bt, M, N):
+        raise ValueError(f"out must be {(bt, M, N)}")
+    if a.dtype != b.dtype:
+        raise TypeError("a and b must have the same dtype")
+    with torch.cuda.device(a.device):
+        _check(lib().tcm_batched_gemm_tn(_ptr(a), _ptr(b), _ptr(out), bt, M, N, K,
+                                         _code(a.dtype), _code(out.dtype), _stream(a)))
+    return out
+
+
+def gemm_mx_fp8(a, b, scale_a, scale_b, out=None, out_dtype=None):
+    """MXFP8 Out = (a * scale_a) . (b * scale_b)^T.  a (M, K), b (N, K) E4M3 bytes
+    (uint8 or float8_e4m3fn); scale_a (M, K/32), scale_b (N, K/32) E8M0 bytes."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("K mismatch")
+    if K % 32 or tuple(scale_a.shape) != (M, K // 32) or tuple(scale_b.shape) != (N, K // 32):
+        raise ValueError("scale tensors must be (rows, K/32) with K a multiple of 32")
+    for t in (a, b):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError("MX elements must be uint8 or float8_e4m3fn")
+    for t in (scale_a, scale_b):
+        if t.dtype not in (torch.uint8, torch.float8_e8m0fnu):
+            raise TypeError("MX scales must be uint8 or float8_e8m0fnu")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be {(M, N)}")
+    with torch.cuda.device(a.device):
+        _check(lib().tcm_gemm_mx_fp8(_ptr(a), _ptr(b), _ptr(scale_a), _ptr(scale_b), _ptr(out),
+                                     M, N, K, _code(out.dtype), _stream(a)))
+    return out
+
+
+def plan(M, N, K, dtype=BF16, out_dtype=BF16, batch=1, mx=False, num_cus=256) -> dict:
+    """The launch a call would make (tile, ring depth, LDS bytes, grid)."""
+    p = Plan()
+    _check(lib().tcm_plan_gemm(batch, M, N, K, dtype, out_dtype, int(mx), num_cus,
+                               ctypes.byref(p)))
+    return p.as_dict()

@@ -1,0 +1,401 @@
+// The tiled product kernel for gfx950: Out = A . B^T, A M x K and B N x K
+// both K-contiguous ("TN"), fp32 accumulation in the matrix cores.
+//
+// Structure (the pipelined tile loop of "Hopper and Blackwell GEMM", Concept
+// and Maths sections, and of "API Card: Blackwell Pipeline (tcgen05)",
+// Device side., rebuilt for CDNA4):
+//
+//  * Persistent tile scheduler.  A workgroup takes output tiles
+//    lid, lid + G, lid + 2G, ... of a host-computed tile count, with an
+//    XCD-aware renumbering of workgroups and a grouped tile order; every wave
+//    of the workgroup leaves the loop at the same point.
+//  * One flattened loop over (tile, K slice) pairs, g = t * ksteps + k, as in
+//    the page's slice numbering.  Operand copies run S - 1 slices ahead of the
+//    matrix cores, across tile boundaries, so the next tile's first slices are
+//    already in flight while the current tile's epilogue converts and stores.
+//  * LDS ring of S stages, one A tile and one B tile per stage.  Copies go
+//    from HBM straight into LDS (buffer_load ... lds, 16 bytes per lane),
+//    without passing through registers; out-of-range rows and the K tail read
+//    as zeros through the buffer resource's bounds.
+//  * Stage hand-off: the "full" condition is this wave's own vmcnt wait plus
+//    the workgroup barrier; the "empty" condition is the same barrier, since
+//    every wave has read its fragments of the previous slice before it.
+//  * XOR-swizzled LDS rows so that the 16-byte fragment reads of 64 lanes
+//    spread over all banks (the swizzled shared layouts of "Blackwell Tensor
+//    Cores", The Accumulator's Lifetime, redesigned for LDS banks).
+//  * Four waves in a 2 x 2 arrangement, each owning a (BM/2) x (BN/2) block of
+//    32 x 32 MFMA accumulators; the first slice of a tile starts from zero and
+//    later slices accumulate ("mma.sync", Code generation: the first K issue
+//    reads C, later issues read D).
+//  * Epilogue: fp32 accumulators converted (bf16 round-to-nearest-even, or
+//    fp32 as is) and stored with edge masks.
+#pragma once
+
+#include <type_traits>
+
+#include "tcm_device.h"
+
+namespace tcm {
+
+// ---------------------------------------------------------------------------
+// Matrix-core operations.  The 32x32 MFMA forms take, per lane l, operand row
+// l % 32 and one contiguous run of K values selected by l / 32; the result
+// lands as 16 floats per lane: rows 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+// ---------------------------------------------------------------------------
+struct OpBF16 {
+    static constexpr int kElemBytes = 2;
+    static constexpr int kK = 16;  // K per MFMA
+    static constexpr bool kScaled = false;
+    typedef bf16x8_t frag_t;
+    __device__ static __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+struct OpF16 {
+    static constexpr int kElemBytes = 2;
+    static constexpr int kK = 16;
+    static constexpr bool kScaled = false;
+    typedef f16x8_t frag_t;
+    __device__ static __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// MXFP8: E4M3 x E4M3 with one E8M0 scale per 32 K values per row, applied by
+// the scaled MFMA.  Each lane holds 32 consecutive K values of its row -- one
+// scale block -- and supplies that block's scale byte; `SEL` picks the byte
+// of the 32-bit scale register.
+struct OpMXFP8 {
+    static constexpr int kElemBytes = 1;
+    static constexpr int kK = 64;
+    static constexpr bool kScaled = true;
+    typedef i32x8_t frag_t;
+    template <int SEL>
+    __device__ static __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c, int sa, int sb) {
+        // format codes 0 / 0: both operands FP8 E4M3
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
+    }
+};
+
+struct TileCursor {
+    int tl, kk, batch, tm, tn;
+};
+
+template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int SWZ,
+          bool SCALE_WORDS = false>
+__global__ __launch_bounds__(kThreads, OCC) void tiled_gemm_kernel(GemmArgs p) {
+    constexpr int ESZ = Op::kElemBytes;
+    constexpr int RB = BK * ESZ;   // bytes of one operand row's K slice
+    constexpr int CPR = RB / 16;   // 16-byte chunks per row
+    constexpr int A_BYTES = BM * RB;
+    constexpr int B_BYTES = BN * RB;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_LOADS = A_BYTES / (kThreads * 16);  // copies per thread per slice
+    constexpr int B_LOADS = B_BYTES / (kThreads * 16);
+    constexpr int ROWS_PER_WAVE_COPY = kWaveSize * 16 / RB;
+    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int KSTEPS = BK / Op::kK;
+    constexpr int CPL = Op::kK * ESZ / 32;  // 16-byte chunks per lane per MFMA
+    constexpr int LOADS = A_LOADS + B_LOADS;
+    static_assert(KSTEPS % 2 == 0, "fragment double buffer alternates per K step");
+    static_assert(((4 * ROWS_PER_WAVE_COPY) >> SWZ) % CPR == 0, "copy chunk independent of i");
+    static_assert((S - 1) * LOADS < 64, "vmcnt range");
+    static_assert(CPR == 4 || CPR == 8, "row slice must be 64 or 128 bytes");
+    static_assert(A_BYTES % (kThreads * 16) == 0 && B_BYTES % (kThreads * 16) == 0, "copy split");
+    static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+    static_assert(S >= 2, "ring depth");
+    static_assert((32 >> SWZ) % CPR == 0, "swizzle must depend on the row within 32 only");
+    static_assert(!Op::kScaled || (BK == 128 && S == 2), "MX path: 128-deep slices, 2 stages");
+
+    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    const int G = gridDim.x;
+    const int lid = logical_block(blockIdx.x, G);
+    if (lid >= p.total_tiles) return;
+    const int my_tiles = (p.total_tiles - 1 - lid) / G + 1;
+    const int total = my_tiles * p.ksteps;
+    const int K = p.K;
+
+    // ---- per-lane copy geometry -------------------------------------------
+    // Copy i of wave w fills LDS chunk q = (4 i + w) * 64 + lane of the A (B)
+    // region: row q / CPR, physical chunk q % CPR, which holds logical chunk
+    // (q % CPR) ^ swz(row) of that row's K slice.  The chunk is the same for
+    // every i, and copy i sits 4 * ROWS_PER_WAVE_COPY rows below copy i - 1.
+    const int cp_row = wave * ROWS_PER_WAVE_COPY + lane / CPR;
+    const int cp_chunk = (lane % CPR) ^ ((cp_row >> SWZ) & (CPR - 1));
+    const uint32_t cp_off = (uint32_t)cp_row * (uint32_t)K * ESZ + cp_chunk * 16;
+    const int cp_k = cp_chunk * (16 / ESZ);  // first K element of the chunk
+    const uint32_t cp_step = 4u * ROWS_PER_WAVE_COPY * (uint32_t)K * ESZ;
+
+    auto locate = [&](TileCursor& c) {
+        tile_coords(p, c.tl * G + lid, c.batch, c.tm, c.tn);
+    };
+    auto advance = [&](TileCursor& c) {
+        if (++c.kk == p.ksteps) {
+            c.kk = 0;
+            if (++c.tl < my_tiles) locate(c);
+        }
+    };
+
+    // Issue the copies of slice (cursor) into ring stage `st`.
+    auto issue = [&](const TileCursor& c, int st) {
+        const int rows_a = min(BM, p.M - c.tm * BM);
+        const int rows_b = min(BN, p.N - c.tn * BN);
+        const char* abase = (const char*)p.A + c.batch * p.stride_a + (int64_t)c.tm * BM * K * ESZ;
+        const char* bbase = (const char*)p.B + c.batch * p.stride_b + (int64_t)c.tn * BN * K * ESZ;
+        __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, (uint32_t)rows_a * (uint32_t)K * ESZ);
+        __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase, (uint32_t)rows_b * (uint32_t)K * ESZ);
+        const int k0 = c.kk * BK;
+        const bool in_k = k0 + cp_k < K;
+        const uint32_t off0 = in_k ? cp_off + (uint32_t)k0 * ESZ : kOutOfRange;
+        char* sa = lds + st * STAGE;
+        char* sb = sa + A_BYTES;
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i)
+            copy16_to_lds(ra, sa + (4 * i + wave) * 1024, off0 + (in_k ? i * cp_step : 0));
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i)
+            copy16_to_lds(rb, sb + (4 * i + wave) * 1024, off0 + (in_k ? i * cp_step : 0));
+    };
+
+    // ---- per-lane fragment geometry ---------------------------------------
+    const int xr = (l32 >> SWZ) & (CPR - 1);
+    const uint32_t a_frag = (uint32_t)(wm * WTM + l32) * RB;
+    const uint32_t b_frag = (uint32_t)A_BYTES + (uint32_t)(wn * WTN + l32) * RB;
+
+    typedef typename Op::frag_t frag_t;
+    auto read_frag = [&](const char* base, int s) -> frag_t {
+        frag_t f;
+        if constexpr (CPL == 1) {
+            int ch = (2 * s + hi) ^ xr;
+            f = *(const frag_t*)(base + ch * 16);
+        } else {
+            int ch0 = (4 * s + 2 * hi) ^ xr;
+            int ch1 = (4 * s + 2 * hi + 1) ^ xr;
+            i32x4_t lo = *(const i32x4_t*)(base + ch0 * 16);
+            i32x4_t up = *(const i32x4_t*)(base + ch1 * 16);
+            f = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        return f;
+    };
+    frag_t fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, const char* st, int s) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[buf][i] = read_frag(st + a_frag + i * 32 * RB, s);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[buf][j] = read_frag(st + b_frag + j * 32 * RB, s);
+    };
+
+    // ---- MX scales: one 32-bit register per fragment row per slice; byte 0
+    // holds block (k0/32 + hi), byte 2 block (k0/32 + 2 + hi), so the MFMA of
+    // K step s selects byte 2 s.
+    int sc_a[Op::kScaled ? FM : 1], sc_b[Op::kScaled ? FN : 1];
+    int nx_a[Op::kScaled ? FM : 1], nx_b[Op::kScaled ? FN : 1];
+    auto load_scales = [&](const TileCursor& c, int* out_a, int* out_b) {
+        if constexpr (Op::kScaled) {
+            const int kblocks = K / 32;
+            const int kb0 = c.kk * (BK / 32);
+#pragma unroll
+            for (int f = 0; f < FM + FN; ++f) {
+                const bool is_a = f < FM;
+                const int idx = is_a ? f : f - FM;
+                const int lim = is_a ? p.M : p.N;
+                int row = (is_a ? c.tm * BM + wm * WTM : c.tn * BN + wn * WTN) + idx * 32 + l32;
+                row = min(row, lim - 1);
+                const uint8_t* src = (const uint8_t*)(is_a ? p.SA : p.SB) + (int64_t)row * kblocks;
+                int v;
+                if constexpr (SCALE_WORDS) {
+                    uint32_t w = *(const uint32_t*)(src + kb0);
+                    v = (int)(w >> (8 * hi));
+                } else {
+                    int q0 = kb0 + hi, q2 = kb0 + 2 + hi;
+                    int b0 = q0 < kblocks ? src[q0] : 127;
+                    int b2 = q2 < kblocks ? src[q2] : 127;
+                    v = b0 | (b2 << 16);
+                }
+                if (is_a) out_a[idx] = v; else out_b[idx] = v;
+            }
+        }
+    };
+
+    // Accumulators hold D = B_frag . A_frag^T per 32 x 32 block (operands
+    // swapped), so lane l owns output row m = l % 32 and, for each r / 4, the
+    // four consecutive output columns 8 (r / 4) + 4 (l / 32) + 0..3.
+    f32x16_t acc[FM][FN];
+    // ZERO (a std::integral_constant) selects the first MFMA of a tile, which
+    // takes an all-zero accumulator input instead of clearing the registers.
+    auto mma_block = [&](int buf, int s, auto ZERO) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                f32x16_t c;
+                if constexpr (decltype(ZERO)::value)
+                    c = (f32x16_t){};
+                else
+                    c = acc[i][j];
+                if constexpr (Op::kScaled) {
+                    if (s == 0)
+                        acc[i][j] = Op::template mma<0>(fb[buf][j], fa[buf][i], c, sc_b[j], sc_a[i]);
+                    else
+                        acc[i][j] = Op::template mma<2>(fb[buf][j], fa[buf][i], c, sc_b[j], sc_a[i]);
+                } else {
+                    acc[i][j] = Op::mma(fb[buf][j], fa[buf][i], c);
+                }
+            }
+    };
+
+    auto epilogue = [&](const TileCursor& c) {
+        char* Cb = (char*)p.C + c.batch * p.stride_c;
+        const int m_base = c.tm * BM + wm * WTM + l32;
+        const int n_base = c.tn * BN + wn * WTN + 4 * hi;
+        const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (p.N & 3) == 0;
+        if (full) {
+            // interior tile: one 4-wide store per (block, r / 4), no masks
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                TOut* row = (TOut*)Cb + (int64_t)(m_base + i * 32) * p.N + n_base;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        store4<TOut>(row + j * 32 + 8 * q, acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                     acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
+            // edge tile: rows past M and columns past N are not written
+            const bool vec = (p.N & 3) == 0;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = m_base + i * 32;
+                if (m >= p.M) continue;
+                TOut* row = (TOut*)Cb + (int64_t)m * p.N;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = n_base + j * 32 + 8 * q;
+                        if (vec && n + 3 < p.N) {
+                            store4<TOut>(row + n, acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                         acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < p.N) row[n + e] = convert_out<TOut>(acc[i][j][4 * q + e]);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- prologue: the first S slices in flight, slice 0 resident ---------
+    TileCursor ic = {0, 0, 0, 0, 0};
+    locate(ic);
+    TileCursor cc = ic;
+    for (int g = 0; g < S && g < total; ++g) {
+        issue(ic, g);
+        advance(ic);
+    }
+    if (total >= S)
+        wait_vmcnt<(S - 1) * LOADS>();
+    else
+        wait_vmcnt<0>();
+    barrier_lds();
+    read_frags(0, lds, 0);
+    if constexpr (Op::kScaled) load_scales(cc, sc_a, sc_b);
+
+    bool after_epilogue = false;
+    // One slice g of the current tile: K steps with double-buffered
+    // fragments, the stage hand-off folded into the last step.  ZERO marks
+    // the tile's first slice, whose first MFMAs take a zero accumulator.
+    auto slice = [&](int g, auto ZERO) {
+        const char* st = lds + (g % S) * STAGE;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            const int cur = s & 1, nxt = cur ^ 1;
+            if (s + 1 < KSTEPS) {
+                read_frags(nxt, st, s + 1);
+            } else {
+                // Hand-off.  This slice's fragments are all in registers; once
+                // slice g + 1 has landed and every wave has passed the barrier,
+                // stage g % S is free for slice g + S and the first fragments
+                // of slice g + 1 can be read while this K step's MFMAs run.
+                __builtin_amdgcn_sched_barrier(0);
+                if (S > 2 && !after_epilogue && g + S - 1 < total)
+                    wait_vmcnt<(S > 2 ? (S - 2) * LOADS : 0)>();
+                else
+                    wait_vmcnt<0>();
+                barrier_lds();
+                __builtin_amdgcn_sched_barrier(0);
+                if (g + S < total) {
+                    issue(ic, g % S);
+                    advance(ic);
+                }
+                if (g + 1 < total) read_frags(nxt, lds + ((g + 1) % S) * STAGE, 0);
+            }
+            if constexpr (decltype(ZERO)::value) {
+                if (s == 0)
+                    mma_block(cur, s, std::true_type{});
+                else
+                    mma_block(cur, s, std::false_type{});
+            } else {
+                mma_block(cur, s, std::false_type{});
+            }
+        }
+        after_epilogue = false;
+    };
+
+    int g = 0;
+    for (int tl = 0; tl < my_tiles; ++tl) {
+        if constexpr (Op::kScaled) {
+            TileCursor nc = cc;
+            advance(nc);
+            if (g + 1 < total) load_scales(nc, nx_a, nx_b);
+        }
+        slice(g, std::true_type{});
+        if constexpr (Op::kScaled) {
+            advance(cc);
+#pragma unroll
+            for (int i = 0; i < FM; ++i) sc_a[i] = nx_a[i];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) sc_b[j] = nx_b[j];
+        }
+        ++g;
+        for (int kk = 1; kk < p.ksteps; ++kk, ++g) {
+            if constexpr (Op::kScaled) {
+                TileCursor nc = cc;
+                advance(nc);
+                if (g + 1 < total) load_scales(nc, nx_a, nx_b);
+            }
+            slice(g, std::false_type{});
+            if constexpr (Op::kScaled) {
+                advance(cc);
+#pragma unroll
+                for (int i = 0; i < FM; ++i) sc_a[i] = nx_a[i];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) sc_b[j] = nx_b[j];
+            }
+        }
+        // Epilogue of this tile, while the copies of the next tile's first
+        // slices and the reads of its first fragments are in flight.
+        TileCursor ec = {tl, 0, 0, 0, 0};
+        locate(ec);
+        __builtin_amdgcn_sched_barrier(0);
+        epilogue(ec);
+        __builtin_amdgcn_sched_barrier(0);
+        after_epilogue = true;
+    }
+}
+
+}  // namespace tcm

@@ -1,0 +1,34 @@
+// Kernel instances and launcher for the MXFP8 (E4M3 + E8M0 per 32) product.
+#include "gemm_kernel.h"
+
+namespace tcm {
+
+// LDS rows of a 128-deep fp8 slice are 128 bytes (8 chunks).
+constexpr int kSwizzle8 = 0;
+
+template <typename TOut, int BM, int BN, bool WORDS>
+static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((tiled_gemm_kernel<OpMXFP8, TOut, BM, BN, 128, 2, 1, kSwizzle8, WORDS>),
+                       dim3(grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename TOut, bool WORDS>
+static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t st) {
+    switch (v) {
+    case V_MX256x256: return launch_one<TOut, 256, 256, WORDS>(a, grid, st);
+    case V_MX128x128: return launch_one<TOut, 128, 128, WORDS>(a, grid, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_mx(int32_t v, int32_t out_dtype, bool scale_words, const GemmArgs& a,
+                          int grid, hipStream_t st) {
+    if (out_dtype == 1)
+        return scale_words ? by_variant<__bf16, true>(v, a, grid, st)
+                           : by_variant<__bf16, false>(v, a, grid, st);
+    return scale_words ? by_variant<float, true>(v, a, grid, st)
+                       : by_variant<float, false>(v, a, grid, st);
+}
+
+}  // namespace tcm

@@ -1,0 +1,276 @@
+// C ABI of libtcm: argument validation, planning and dispatch.  Every
+// argument is checked on the host before any HIP call, in this order: dtype
+// pair, sizes, pointers, supported range, alignment.
+#include <limits.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/tcm.h"
+#include "tcm_internal.h"
+
+namespace tcm {
+
+VariantInfo variant_info(int32_t v) {
+    switch (v) {
+    case V_T256x256: return {256, 256, 64, 2, 1, 2};
+    case V_T128x256: return {128, 256, 64, 2, 1, 2};
+    case V_T128x128: return {128, 128, 64, 2, 2, 2};
+    case V_T128x64: return {128, 64, 64, 2, 3, 2};
+    case V_MX256x256: return {256, 256, 128, 2, 1, 1};
+    case V_MX128x128: return {128, 128, 128, 2, 1, 1};
+    }
+    return {0, 0, 0, 0, 0, 0};
+}
+
+}  // namespace tcm
+
+namespace {
+
+using namespace tcm;
+
+constexpr int64_t kMaxK = int64_t(1) << 20;     // keeps buffer offsets within 32 bits
+constexpr int64_t kMaxMN = int64_t(1) << 30;    // row indices stay in int32
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    int cus = 0;
+    bool gfx950 = false;
+    hipError_t err = hipSuccess;
+};
+
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+tcm_status device_info(DeviceInfo* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TCM_ERR_NO_DEVICE;
+    std::call_once(g_dev_once[dev], [dev] {
+        hipDeviceProp_t prop;
+        DeviceInfo& d = g_dev[dev];
+        d.err = hipGetDeviceProperties(&prop, dev);
+        if (d.err == hipSuccess) {
+            d.cus = prop.multiProcessorCount;
+            d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        }
+    });
+    *out = g_dev[dev];
+    if (out->err != hipSuccess || !out->gfx950 || out->cus <= 0) return TCM_ERR_NO_DEVICE;
+    return TCM_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t c) {
+    int64_t t;
+    return !__builtin_mul_overflow(a, b, &t) && !__builtin_mul_overflow(t, c, &t) &&
+           t < (int64_t(1) << 62);
+}
+
+int elem_bytes(tcm_dtype d) {
+    switch (d) {
+    case TCM_F16:
+    case TCM_BF16: return 2;
+    case TCM_F32: return 4;
+    case TCM_E4M3:
+    case TCM_E8M0: return 1;
+    }
+    return 0;
+}
+
+// Sizes shared by every entry point.  *empty is set when there is nothing to
+// write (batch, M or N is zero).
+tcm_status check_sizes(int64_t batch, int64_t M, int64_t N, int64_t K, bool* empty) {
+    if (batch < 0 || M < 0 || N < 0 || K < 0) return TCM_ERR_INVALID_SHAPE;
+    if (!mul_ok(batch, M, K) || !mul_ok(batch, N, K) || !mul_ok(batch, M, N))
+        return TCM_ERR_INVALID_SHAPE;
+    *empty = batch == 0 || M == 0 || N == 0;
+    return TCM_OK;
+}
+
+tcm_status check_range(int64_t batch, int64_t M, int64_t N, int64_t K) {
+    if (K > kMaxK || M > kMaxMN || N > kMaxMN) return TCM_ERR_UNSUPPORTED_SHAPE;
+    // tile counts with the smallest tile must fit in int32
+    if (batch * cdiv(M, 128) * cdiv(N, 64) > INT32_MAX) return TCM_ERR_UNSUPPORTED_SHAPE;
+    return TCM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tile choice: the largest tile whose tile count still gives every CU at
+// least one tile with little padding; small problems take the smallest tile.
+int32_t choose_variant(int64_t batch, int64_t M, int64_t N, bool mx, int cus) {
+    static const int32_t plain[] = {V_T256x256, V_T128x256, V_T128x128, V_T128x64};
+    static const int32_t mxv[] = {V_MX256x256, V_MX128x128};
+    const int32_t* cand = mx ? mxv : plain;
+    const int n = mx ? 2 : 4;
+    for (int i = 0; i < n; ++i) {
+        VariantInfo vi = variant_info(cand[i]);
+        int64_t tiles = batch * cdiv(M, vi.tile_m) * cdiv(N, vi.tile_n);
+        double fill = double(batch) * M * N / (double(tiles) * vi.tile_m * vi.tile_n);
+        if (tiles >= cus && fill >= 0.9) return cand[i];
+    }
+    return cand[n - 1];
+}
+
+tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool mx, int cus,
+                     tcm_plan* plan, GemmArgs* args) {
+    int32_t v = choose_variant(batch, M, N, mx, cus);
+    VariantInfo vi = variant_info(v);
+    int64_t tm = cdiv(M, vi.tile_m), tn = cdiv(N, vi.tile_n);
+    int64_t tiles = batch * tm * tn;
+    int64_t slots = int64_t(cus) * vi.occupancy;
+    int64_t grid = tiles < slots ? tiles : slots;
+    int32_t stage = (vi.tile_m + vi.tile_n) * vi.tile_k * vi.elem_bytes;
+    if (plan) {
+        plan->tile_m = vi.tile_m;
+        plan->tile_n = vi.tile_n;
+        plan->tile_k = vi.tile_k;
+        plan->stages = vi.stages;
+        plan->threads = kThreads;
+        plan->stage_bytes = stage;
+        plan->lds_bytes = stage * vi.stages;
+        plan->grid = (int32_t)grid;
+        plan->tiles = tiles;
+        plan->kernel = v;
+    }
+    if (args) {
+        memset(args, 0, sizeof(*args));
+        args->M = (int32_t)M;
+        args->N = (int32_t)N;
+        args->K = (int32_t)K;
+        args->batch = (int32_t)batch;
+        args->tiles_m = (int32_t)tm;
+        args->tiles_n = (int32_t)tn;
+        args->tiles_per_batch = (int32_t)(tm * tn);
+        args->total_tiles = (int32_t)tiles;
+        args->ksteps = K > 0 ? (int32_t)cdiv(K, vi.tile_k) : 1;
+        args->group_m = 4;
+    }
+    return TCM_OK;
+}
+
+bool plain_pair(tcm_dtype in, tcm_dtype out) {
+    return (in == TCM_F16 || in == TCM_BF16) && (out == TCM_F32 || out == TCM_BF16);
+}
+
+tcm_status run_plain(const void* A, const void* B, void* Out, int64_t batch, int64_t M, int64_t N,
+                     int64_t K, tcm_dtype dtype, tcm_dtype out_dtype, void* stream) {
+    if (!plain_pair(dtype, out_dtype)) return TCM_ERR_UNSUPPORTED_DTYPE;
+    bool empty = false;
+    tcm_status s = check_sizes(batch, M, N, K, &empty);
+    if (s != TCM_OK || empty) return s;
+    if (!Out || (K > 0 && (!A || !B))) return TCM_ERR_NULL_POINTER;
+    if ((s = check_range(batch, M, N, K)) != TCM_OK) return s;
+    const int es = elem_bytes(dtype);
+    if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) || (K * es) % 16 != 0)
+        return TCM_ERR_MISALIGNED;
+    DeviceInfo dev;
+    if ((s = device_info(&dev)) != TCM_OK) return s;
+    tcm_plan plan;
+    GemmArgs a;
+    make_plan(batch, M, N, K, false, dev.cus, &plan, &a);
+    a.A = A;
+    a.B = B;
+    a.C = Out;
+    a.stride_a = M * K * es;
+    a.stride_b = N * K * es;
+    a.stride_c = M * N * elem_bytes(out_dtype);
+    hipError_t e = launch_gemm_tn(plan.kernel, (int32_t)dtype, (int32_t)out_dtype, a, plan.grid,
+                                  (hipStream_t)stream);
+    return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+tcm_status tcm_gemm_tn(const void* A, const void* B, void* Out, int64_t M, int64_t N, int64_t K,
+                       tcm_dtype dtype, tcm_dtype out_dtype, void* stream) {
+    return run_plain(A, B, Out, 1, M, N, K, dtype, out_dtype, stream);
+}
+
+tcm_status tcm_batched_gemm_tn(const void* A, const void* B, void* Out, int64_t batch, int64_t M,
+                               int64_t N, int64_t K, tcm_dtype dtype, tcm_dtype out_dtype,
+                               void* stream) {
+    return run_plain(A, B, Out, batch, M, N, K, dtype, out_dtype, stream);
+}
+
+tcm_status tcm_gemm_mx_fp8(const void* A, const void* B, const void* scale_A, const void* scale_B,
+                           void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
+                           void* stream) {
+    if (!(out_dtype == TCM_F32 || out_dtype == TCM_BF16)) return TCM_ERR_UNSUPPORTED_DTYPE;
+    bool empty = false;
+    tcm_status s = check_sizes(1, M, N, K, &empty);
+    if (s != TCM_OK || empty) return s;
+    if (!Out || (K > 0 && (!A || !B || !scale_A || !scale_B))) return TCM_ERR_NULL_POINTER;
+    if ((s = check_range(1, M, N, K)) != TCM_OK) return s;
+    if (K % 32 != 0) return TCM_ERR_UNSUPPORTED_SHAPE;
+    if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) || K % 16 != 0)
+        return TCM_ERR_MISALIGNED;
+    DeviceInfo dev;
+    if ((s = device_info(&dev)) != TCM_OK) return s;
+    tcm_plan plan;
+    GemmArgs a;
+    make_plan(1, M, N, K, true, dev.cus, &plan, &a);
+    a.A = A;
+    a.B = B;
+    a.SA = scale_A;
+    a.SB = scale_B;
+    a.C = Out;
+    a.stride_a = M * K;
+    a.stride_b = N * K;
+    a.stride_c = M * N * elem_bytes(out_dtype);
+    // 32-bit scale reads need every row's K/32 bytes to be whole words.
+    const bool words = K > 0 && K % 128 == 0 && (reinterpret_cast<uintptr_t>(scale_A) & 3u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(scale_B) & 3u) == 0;
+    hipError_t e = launch_gemm_mx(plan.kernel, (int32_t)out_dtype, words, a, plan.grid,
+                                  (hipStream_t)stream);
+    return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
+}
+
+tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
+                         tcm_dtype out_dtype, int mx, int num_cus, tcm_plan* plan) {
+    if (!plan) return TCM_ERR_NULL_POINTER;
+    if (mx ? !(out_dtype == TCM_F32 || out_dtype == TCM_BF16) : !plain_pair(dtype, out_dtype))
+        return TCM_ERR_UNSUPPORTED_DTYPE;
+    bool empty = false;
+    tcm_status s = check_sizes(batch, M, N, K, &empty);
+    if (s != TCM_OK) return s;
+    if ((s = check_range(batch, M, N, K)) != TCM_OK) return s;
+    if (mx && K % 32 != 0) return TCM_ERR_UNSUPPORTED_SHAPE;
+    if (num_cus <= 0) {
+        DeviceInfo dev;
+        if ((s = device_info(&dev)) != TCM_OK) return s;
+        num_cus = dev.cus;
+    }
+    make_plan(batch < 1 ? 1 : batch, M < 1 ? 1 : M, N < 1 ? 1 : N, K, mx != 0, num_cus, plan,
+              nullptr);
+    if (empty) {
+        plan->grid = 0;
+        plan->tiles = 0;
+    }
+    return TCM_OK;
+}
+
+const char* tcm_status_string(tcm_status s) {
+    switch (s) {
+    case TCM_OK: return "TCM_OK: success";
+    case TCM_ERR_NULL_POINTER: return "TCM_ERR_NULL_POINTER: a required pointer is NULL";
+    case TCM_ERR_INVALID_SHAPE: return "TCM_ERR_INVALID_SHAPE: negative size or size overflow";
+    case TCM_ERR_UNSUPPORTED_SHAPE:
+        return "TCM_ERR_UNSUPPORTED_SHAPE: size outside the supported range (K <= 2^20, M and N "
+               "<= 2^30, MX K a multiple of 32)";
+    case TCM_ERR_MISALIGNED:
+        return "TCM_ERR_MISALIGNED: pointers and operand rows must be 16-byte aligned";
+    case TCM_ERR_UNSUPPORTED_DTYPE: return "TCM_ERR_UNSUPPORTED_DTYPE: dtype pair not supported";
+    case TCM_ERR_NO_DEVICE: return "TCM_ERR_NO_DEVICE: no gfx950 HIP device is current";
+    case TCM_ERR_HIP: return "TCM_ERR_HIP: a HIP runtime call or kernel launch failed";
+    }
+    return "TCM_ERR_UNKNOWN: unknown status code";
+}
+
+}  // extern "C"

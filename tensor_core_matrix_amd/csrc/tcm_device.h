@@ -1,0 +1,106 @@
+// Device-side building blocks of the gfx950 (CDNA4) tiled product kernels:
+// buffer resources, direct global->LDS copies, explicit wait counters and the
+// MFMA / epilogue primitives.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "tcm_internal.h"
+
+namespace tcm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kWaveSize = 64;
+// A buffer offset that is past every buffer's num_records: buffer loads at it
+// return zeros (used for the K tail).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+#define TCM_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Raw buffer resource over `bytes` bytes at `base`; loads past `bytes` give 0.
+// Word 3 = 0x00020000 selects a 32-bit data format, which untyped loads need
+// to return data at all on gfx9-family parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes per lane from the buffer straight into LDS, bypassing VGPRs.  The
+// 64 lanes of the wave fill 1 KiB of LDS contiguously from `lds_wave_base`
+// (lane l writes bytes [16 l, 16 l + 16)); only the global side is gathered.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base,
+                                              uint32_t voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCM_LDS_PTR(lds_wave_base), 16, voffset, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier after this wave's LDS reads have returned.  Unlike
+// __syncthreads() it does not wait for outstanding global loads, so the
+// copies of later stages stay in flight across it.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+template <typename TOut>
+__device__ __forceinline__ TOut convert_out(float x);
+template <>
+__device__ __forceinline__ float convert_out<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 convert_out<__bf16>(float x) { return to_bf16(x); }
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Four consecutive outputs of one row (8 bytes bf16 / 16 bytes fp32).
+template <typename TOut>
+__device__ __forceinline__ void store4(TOut* dst, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
+    *(f32x4_t*)dst = (f32x4_t){a, b, c, d};
+}
+template <>
+__device__ __forceinline__ void store4<__bf16>(__bf16* dst, float a, float b, float c, float d) {
+    *(bf16x4_t*)dst = (bf16x4_t){to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)};
+}
+
+// XCD-aware workgroup order.  Workgroups are dealt round-robin to the 8 XCDs
+// (workgroup b runs on XCD b % 8), each with its own L2.  Renumbering so that
+// the G/8 workgroups of one XCD take consecutive logical ids makes them work on
+// neighbouring output tiles, which share A rows and B rows in that L2.
+__device__ __forceinline__ int logical_block(int b, int G) {
+    if (G % 8 != 0) return b;
+    return (b % 8) * (G / 8) + b / 8;
+}
+
+// Grouped tile order: tiles advance down `group_m` tile rows before moving to
+// the next tile column, so concurrently running tiles share operand rows.
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int t, int& batch, int& tm,
+                                            int& tn) {
+    batch = t / p.tiles_per_batch;
+    int r = t - batch * p.tiles_per_batch;
+    int gsz = p.group_m * p.tiles_n;
+    int grp = r / gsz;
+    int first = grp * p.group_m;
+    int gm = min(p.group_m, p.tiles_m - first);
+    int rr = r - grp * gsz;
+    tm = first + rr % gm;
+    tn = rr / gm;
+}
+
+}  // namespace tcm

@@ -1,0 +1,53 @@
+// Host/device shared definitions of libtcm (not part of the public ABI).
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace tcm {
+
+constexpr int kThreads = 256;  // four 64-lane waves per workgroup, one per SIMD
+
+// Arguments of one launch of the tiled product kernels.  Sizes are per
+// problem; the byte strides step from one batched problem to the next.
+struct GemmArgs {
+    const void* A;
+    const void* B;
+    const void* SA;  // E8M0 scales (MX only)
+    const void* SB;
+    void* C;
+    int32_t M, N, K;
+    int32_t batch;
+    int64_t stride_a, stride_b, stride_c;  // bytes
+    int32_t tiles_m, tiles_n;
+    int32_t tiles_per_batch;
+    int32_t total_tiles;
+    int32_t ksteps;   // K slices per tile (at least 1, so K == 0 writes zeros)
+    int32_t group_m;  // tile rows per group of the grouped tile order
+};
+
+// Kernel variants.  The id is reported by tcm_plan_gemm.
+enum Variant : int32_t {
+    V_T256x256 = 0,   // 256x256x64, 2-stage ring, 1 workgroup per CU
+    V_T128x256 = 1,   // 128x256x64, 2-stage ring
+    V_T128x128 = 2,   // 128x128x64, 2-stage ring, 2 workgroups per CU
+    V_T128x64 = 3,    // 128x64x64, 2-stage ring, 3 workgroups per CU
+    V_MX256x256 = 10, // MXFP8 256x256x128, 2-stage ring
+    V_MX128x128 = 11, // MXFP8 128x128x128, 2-stage ring
+};
+
+struct VariantInfo {
+    int32_t tile_m, tile_n, tile_k, stages, occupancy;
+    int32_t elem_bytes;
+};
+
+VariantInfo variant_info(int32_t v);
+
+// Launchers (one per translation unit).  dtype codes follow tcm_dtype.
+hipError_t launch_gemm_tn(int32_t variant, int32_t in_dtype, int32_t out_dtype, const GemmArgs& a,
+                          int grid, hipStream_t stream);
+hipError_t launch_gemm_mx(int32_t variant, int32_t out_dtype, bool scale_words, const GemmArgs& a,
+                          int grid, hipStream_t stream);
+
+}  // namespace tcm

@@ -1,0 +1,121 @@
+"""The C ABI on the CPU: the library loads, exports what include/tcm.h
+declares, rejects invalid calls with the documented status before touching a
+device, and plans the launches it would make.  No compute call runs here."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import tensor_core_matrix_amd as tcm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tcm.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "page_figures.json")
+
+OK, NULLP, BADSHAPE, UNSUP_SHAPE, MISALIGNED, UNSUP_DTYPE, NO_DEVICE, HIP = range(8)
+A, B, C, SA, SB = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000  # 16-byte aligned stand-ins
+
+
+def test_exports_every_declared_symbol():
+    decl = set(re.findall(r"\b(tcm_\w+)\s*\(", open(HEADER).read()))
+    assert decl == set(tcm.EXPORTS)
+    L = tcm.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = tcm.lib()
+    for s in range(8):
+        txt = L.tcm_status_string(s).decode()
+        assert txt.startswith("TCM_") and ":" in txt
+    assert "UNKNOWN" in L.tcm_status_string(99).decode()
+
+
+def call_plain(a=A, b=B, c=C, M=64, N=64, K=64, dt=tcm.BF16, odt=tcm.BF16):
+    return tcm.lib().tcm_gemm_tn(a, b, c, M, N, K, dt, odt, None)
+
+
+def test_dtype_pairs_rejected():
+    for dt, odt in [(tcm.F32, tcm.F32), (tcm.E4M3, tcm.BF16), (tcm.BF16, tcm.F16),
+                    (tcm.BF16, tcm.E4M3), (7, tcm.F32)]:
+        assert call_plain(dt=dt, odt=odt) == UNSUP_DTYPE
+    assert tcm.lib().tcm_gemm_mx_fp8(A, B, SA, SB, C, 64, 64, 64, tcm.F16, None) == UNSUP_DTYPE
+
+
+def test_shapes_rejected():
+    assert call_plain(M=-1) == BADSHAPE
+    assert call_plain(K=-8) == BADSHAPE
+    assert call_plain(M=1 << 40, N=1 << 40) == BADSHAPE          # M*N overflows
+    assert call_plain(M=1 << 31, K=8) == UNSUP_SHAPE              # beyond 2^30 rows
+    assert call_plain(K=(1 << 20) + 8) == UNSUP_SHAPE
+    L = tcm.lib()
+    assert L.tcm_batched_gemm_tn(A, B, C, -2, 8, 8, 8, tcm.BF16, tcm.F32, None) == BADSHAPE
+    assert L.tcm_gemm_mx_fp8(A, B, SA, SB, C, 64, 64, 48, tcm.BF16, None) == UNSUP_SHAPE
+
+
+def test_empty_calls_are_no_ops():
+    # nothing to write: OK without any pointer or device
+    assert call_plain(a=None, b=None, c=None, M=0) == OK
+    assert call_plain(a=None, b=None, c=None, N=0) == OK
+    assert tcm.lib().tcm_batched_gemm_tn(None, None, None, 0, 8, 8, 8, tcm.BF16,
+                                         tcm.F32, None) == OK
+
+
+def test_null_pointers_rejected():
+    assert call_plain(a=None) == NULLP
+    assert call_plain(b=None) == NULLP
+    assert call_plain(c=None) == NULLP
+    L = tcm.lib()
+    assert L.tcm_gemm_mx_fp8(A, B, None, SB, C, 64, 64, 64, tcm.BF16, None) == NULLP
+    assert L.tcm_gemm_mx_fp8(A, B, SA, None, C, 64, 64, 64, tcm.BF16, None) == NULLP
+
+
+def test_alignment_rejected():
+    assert call_plain(a=A + 2) == MISALIGNED
+    assert call_plain(b=B + 8) == MISALIGNED
+    assert call_plain(c=C + 4) == MISALIGNED
+    assert call_plain(K=60) == MISALIGNED            # 120-byte rows
+    L = tcm.lib()
+    assert L.tcm_gemm_mx_fp8(A + 1, B, SA, SB, C, 64, 64, 64, tcm.BF16, None) == MISALIGNED
+    # scale tensors need no alignment: a valid call gets past validation
+    assert L.tcm_gemm_mx_fp8(A, B, SA + 1, SB + 3, C, 64, 64, 64, tcm.BF16, None) in (OK, NO_DEVICE)
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        has_gpu = False
+    if has_gpu:
+        pytest.skip("a GPU is present")
+    assert call_plain() == NO_DEVICE
+
+
+def test_plan_stage_bytes_match_page():
+    fig = json.load(open(GOLDEN))["stage_bytes"]
+    p = tcm.plan(fig["tile_m"], fig["tile_n"], fig["tile_k"], tcm.BF16, tcm.F32, batch=1024)
+    assert (p["tile_m"], p["tile_n"], p["tile_k"]) == (128, 256, 64)
+    assert p["stage_bytes"] == fig["stage_KiB"] * 1024
+    assert p["lds_bytes"] == p["stages"] * p["stage_bytes"] <= 160 * 1024
+
+
+def test_plans_of_the_workloads():
+    # single tile, one workgroup
+    p = tcm.plan(128, 64, 64, tcm.F16, tcm.F32)
+    assert p["grid"] == 1 and p["tiles"] == 1 and (p["tile_m"], p["tile_n"]) == (128, 64)
+    # 4096^3: one 256 x 256 tile per CU
+    p = tcm.plan(4096, 4096, 4096)
+    assert (p["tile_m"], p["tile_n"], p["grid"], p["tiles"]) == (256, 256, 256, 256)
+    # 8192^3: persistent, four tiles per workgroup
+    p = tcm.plan(8192, 8192, 8192)
+    assert (p["tile_m"], p["tile_n"], p["grid"], p["tiles"]) == (256, 256, 256, 1024)
+    assert p["lds_bytes"] <= 160 * 1024
+    # MXFP8 8192^3: 256 x 256 tiles, 128-deep slices (64 KiB per stage)
+    p = tcm.plan(8192, 8192, 8192, mx=True)
+    assert (p["tile_m"], p["tile_k"], p["stage_bytes"]) == (256, 128, 64 * 1024)
+    # empty problem plans nothing
+    assert tcm.plan(0, 8, 8)["grid"] == 0
