@@ -72,6 +72,12 @@ def timed(fn, steps, warmup, torch):
 
 
 def prepare(name, torch, inp, tcm):
+    if name == "copy":
+        # plain device copy of 1 GiB: reference reading for the traffic counters
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        w = inp.Workload("copy", 1, 1, 1, 0, "bf16", "bf16", 0, "uniform")
+        return w, (lambda: dst.copy_(src)), 2 * src.numel() * 4, (src, dst)
     w = inp.WORKLOADS[name]
     x = {k: v.to("cuda") for k, v in inp.make(w).items()}
     odt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
@@ -166,6 +172,10 @@ def main() -> int:
         if name == "tile_f16":
             steps = max(steps, 200)
         ms = timed(fn, steps, args.warmup, torch)
+        if name == "copy":
+            print(f"[bench] copy 1 GiB -> 1 GiB: {ms:.4f} ms/call, "
+                  f"{nbytes / (ms * 1e-3) / 1e9:.1f} GB/s", file=sys.stderr, flush=True)
+            return 0
         tflops = w.flops / (ms * 1e-3) / 1e12
         results[name] = {
             "ms": ms, "tflops": tflops, "steps": steps,

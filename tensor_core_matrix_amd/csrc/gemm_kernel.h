@@ -63,9 +63,10 @@ struct OpF16 {
 };
 
 // MXFP8: E4M3 x E4M3 with one E8M0 scale per 32 K values per row, applied by
-// the scaled MFMA.  Each lane holds 32 consecutive K values of its row -- one
-// scale block -- and supplies that block's scale byte; `SEL` picks the byte
-// of the 32-bit scale register.
+// the scaled MFMA.  Of the 64 K values of one MFMA, block 0 sits in bytes
+// 0..15 of lanes l and l + 32 and block 1 in bytes 16..31; lane l + 32 b
+// supplies the scale of block b of row l % 32.  `SEL` picks the byte of the
+// 32-bit scale register.
 struct OpMXFP8 {
     static constexpr int kElemBytes = 1;
     static constexpr int kK = 64;
@@ -178,8 +179,11 @@ __global__ __launch_bounds__(kThreads, OCC) void tiled_gemm_kernel(GemmArgs p) {
             int ch = (2 * s + hi) ^ xr;
             f = *(const frag_t*)(base + ch * 16);
         } else {
-            int ch0 = (4 * s + 2 * hi) ^ xr;
-            int ch1 = (4 * s + 2 * hi + 1) ^ xr;
+            // 64 K values per MFMA form two scale blocks of 32.  The scaled
+            // MFMA takes block 0 from bytes 0..15 of both half-waves and block
+            // 1 from bytes 16..31, so half-wave h reads K chunks h and 2 + h.
+            int ch0 = (4 * s + hi) ^ xr;
+            int ch1 = (4 * s + 2 + hi) ^ xr;
             i32x4_t lo = *(const i32x4_t*)(base + ch0 * 16);
             i32x4_t up = *(const i32x4_t*)(base + ch1 * 16);
             f = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);

@@ -3,14 +3,17 @@
 
 namespace tcm {
 
-// LDS rows of a 64-deep bf16 slice are 128 bytes (8 chunks); the chunk XOR
-// uses row bits selected by this shift.
-constexpr int kSwizzle16 = 0;
+// The 16-byte chunk XOR of an LDS row uses row bits selected by a shift: rows
+// of a 64-deep bf16 slice are 128 bytes (8 chunks, row bits 0..2), rows of a
+// 32-deep slice 64 bytes (4 chunks, row bits 1..2, so that the 8 rows read
+// together by 8 lanes land on 8 different 16-byte bank groups).
+template <int BK>
+constexpr int swizzle_shift() { return BK == 64 ? 0 : 1; }
 
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, kSwizzle16>), dim3(grid),
-                       dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, swizzle_shift<BK>()>),
+                       dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -21,6 +24,8 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_T128x256: return launch_one<Op, TOut, 128, 256, 64, 2, 1>(a, grid, st);
     case V_T128x128: return launch_one<Op, TOut, 128, 128, 64, 2, 2>(a, grid, st);
     case V_T128x64: return launch_one<Op, TOut, 128, 64, 64, 2, 3>(a, grid, st);
+    case V_T256x256_K32S4: return launch_one<Op, TOut, 256, 256, 32, 4, 1>(a, grid, st);
+    case V_T256x256_K32S5: return launch_one<Op, TOut, 256, 256, 32, 5, 1>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

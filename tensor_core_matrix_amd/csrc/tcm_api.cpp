@@ -2,6 +2,7 @@
 // argument is checked on the host before any HIP call, in this order: dtype
 // pair, sizes, pointers, supported range, alignment.
 #include <limits.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -20,6 +21,8 @@ VariantInfo variant_info(int32_t v) {
     case V_T128x256: return {128, 256, 64, 2, 1, 2};
     case V_T128x128: return {128, 128, 64, 2, 2, 2};
     case V_T128x64: return {128, 64, 64, 2, 3, 2};
+    case V_T256x256_K32S4: return {256, 256, 32, 4, 1, 2};
+    case V_T256x256_K32S5: return {256, 256, 32, 5, 1, 2};
     case V_MX256x256: return {256, 256, 128, 2, 1, 1};
     case V_MX128x128: return {128, 128, 128, 2, 1, 1};
     }
@@ -100,9 +103,21 @@ tcm_status check_range(int64_t batch, int64_t M, int64_t N, int64_t K) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// TCM_FORCE_VARIANT=<id> (read once) forces a kernel variant of the matching
+// family, for tuning sweeps; unset, the heuristic below chooses.
+int32_t forced_variant() {
+    static const int32_t v = [] {
+        const char* e = getenv("TCM_FORCE_VARIANT");
+        return e && *e ? (int32_t)atoi(e) : (int32_t)-1;
+    }();
+    return v;
+}
+
 // Tile choice: the largest tile whose tile count still gives every CU at
 // least one tile with little padding; small problems take the smallest tile.
 int32_t choose_variant(int64_t batch, int64_t M, int64_t N, bool mx, int cus) {
+    const int32_t f = forced_variant();
+    if (f >= 0 && variant_info(f).tile_m > 0 && (f >= V_MX256x256) == mx) return f;
     static const int32_t plain[] = {V_T256x256, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MX256x256, V_MX128x128};
     const int32_t* cand = mx ? mxv : plain;
