@@ -85,7 +85,8 @@ struct TileCursor {
 
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int SWZ,
           bool SCALE_WORDS = false>
-__global__ __launch_bounds__(kThreads, OCC) void tiled_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void tiled_gemm_kernel(GemmArgs p) {
     constexpr int ESZ = Op::kElemBytes;
     constexpr int RB = BK * ESZ;   // bytes of one operand row's K slice
     constexpr int CPR = RB / 16;   // 16-byte chunks per row
@@ -146,25 +147,48 @@ __global__ __launch_bounds__(kThreads, OCC) void tiled_gemm_kernel(GemmArgs p) {
         }
     };
 
-    // Issue the copies of slice (cursor) into ring stage `st`.
-    auto issue = [&](const TileCursor& c, int st) {
-        const int rows_a = min(BM, p.M - c.tm * BM);
-        const int rows_b = min(BN, p.N - c.tn * BN);
-        const char* abase = (const char*)p.A + c.batch * p.stride_a + (int64_t)c.tm * BM * K * ESZ;
-        const char* bbase = (const char*)p.B + c.batch * p.stride_b + (int64_t)c.tn * BN * K * ESZ;
-        __amdgpu_buffer_rsrc_t ra = make_rsrc(abase, (uint32_t)rows_a * (uint32_t)K * ESZ);
-        __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase, (uint32_t)rows_b * (uint32_t)K * ESZ);
-        const int k0 = c.kk * BK;
-        const bool in_k = k0 + cp_k < K;
-        const uint32_t off0 = in_k ? cp_off + (uint32_t)k0 * ESZ : kOutOfRange;
+    // The copy stream ("producer"): the next slice to copy and the buffer
+    // resources of its tile, rebuilt only when the stream enters a new tile.
+    TileCursor fc = {0, 0, 0, 0, 0};
+    __amdgpu_buffer_rsrc_t ra, rb;
+    auto feed_resources = [&]() {
+        const int rows_a = min(BM, p.M - fc.tm * BM);
+        const int rows_b = min(BN, p.N - fc.tn * BN);
+        const char* abase = (const char*)p.A + fc.batch * p.stride_a + (int64_t)fc.tm * BM * K * ESZ;
+        const char* bbase = (const char*)p.B + fc.batch * p.stride_b + (int64_t)fc.tn * BN * K * ESZ;
+        ra = make_rsrc(abase, (uint32_t)rows_a * (uint32_t)K * ESZ);
+        rb = make_rsrc(bbase, (uint32_t)rows_b * (uint32_t)K * ESZ);
+    };
+    auto feed_advance = [&]() {
+        if (++fc.kk == p.ksteps) {
+            fc.kk = 0;
+            if (++fc.tl < my_tiles) {
+                locate(fc);
+                feed_resources();
+            }
+        }
+    };
+    // Per-copy buffer offsets of the stream's current slice, computed outside
+    // the hot region.  A slice past the last one (`live` false) and 16-byte
+    // chunks past K get out-of-range offsets: those copies touch no memory
+    // and write zeros into a stage that is never read again.
+    constexpr int MAX_LOADS = A_LOADS > B_LOADS ? A_LOADS : B_LOADS;
+    uint32_t foff[MAX_LOADS];
+    auto feed_offsets = [&](bool live) {
+        const int k0 = fc.kk * BK;
+        const uint32_t off0 =
+            (live && k0 + cp_k < K) ? cp_off + (uint32_t)k0 * ESZ : kOutOfRange;
+#pragma unroll
+        for (int i = 0; i < MAX_LOADS; ++i) foff[i] = off0 + i * cp_step;
+    };
+    // Copies of the stream's current slice into ring stage `st`.
+    auto issue = [&](int st) {
         char* sa = lds + st * STAGE;
         char* sb = sa + A_BYTES;
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i)
-            copy16_to_lds(ra, sa + (4 * i + wave) * 1024, off0 + (in_k ? i * cp_step : 0));
+        for (int i = 0; i < A_LOADS; ++i) copy16_to_lds(ra, sa + (4 * i + wave) * 1024, foff[i]);
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i)
-            copy16_to_lds(rb, sb + (4 * i + wave) * 1024, off0 + (in_k ? i * cp_step : 0));
+        for (int i = 0; i < B_LOADS; ++i) copy16_to_lds(rb, sb + (4 * i + wave) * 1024, foff[i]);
     };
 
     // ---- per-lane fragment geometry ---------------------------------------
@@ -236,25 +260,35 @@ __global__ __launch_bounds__(kThreads, OCC) void tiled_gemm_kernel(GemmArgs p) {
     f32x16_t acc[FM][FN];
     // ZERO (a std::integral_constant) selects the first MFMA of a tile, which
     // takes an all-zero accumulator input instead of clearing the registers.
-    auto mma_block = [&](int buf, int s, auto ZERO) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                f32x16_t c;
-                if constexpr (decltype(ZERO)::value)
-                    c = (f32x16_t){};
-                else
-                    c = acc[i][j];
-                if constexpr (Op::kScaled) {
-                    if (s == 0)
-                        acc[i][j] = Op::template mma<0>(fb[buf][j], fa[buf][i], c, sc_b[j], sc_a[i]);
-                    else
-                        acc[i][j] = Op::template mma<2>(fb[buf][j], fa[buf][i], c, sc_b[j], sc_a[i]);
-                } else {
-                    acc[i][j] = Op::mma(fb[buf][j], fa[buf][i], c);
-                }
-            }
+    // Single-element forms of the three streams of a K step.
+    auto mma_one = [&](int buf, int s, int x, auto ZERO) {
+        const int i = x / FN, j = x % FN;
+        f32x16_t c;
+        if constexpr (decltype(ZERO)::value)
+            c = (f32x16_t){};
+        else
+            c = acc[i][j];
+        if constexpr (Op::kScaled) {
+            if (s == 0)
+                acc[i][j] = Op::template mma<0>(fb[buf][j], fa[buf][i], c, sc_b[j], sc_a[i]);
+            else
+                acc[i][j] = Op::template mma<2>(fb[buf][j], fa[buf][i], c, sc_b[j], sc_a[i]);
+        } else {
+            acc[i][j] = Op::mma(fb[buf][j], fa[buf][i], c);
+        }
+    };
+    auto read_one = [&](int buf, const char* st, int s, int x) {
+        if (x < FM)
+            fa[buf][x] = read_frag(st + a_frag + x * 32 * RB, s);
+        else
+            fb[buf][x - FM] = read_frag(st + b_frag + (x - FM) * 32 * RB, s);
+    };
+    auto copy_one = [&](int st, int x) {
+        char* sa = lds + st * STAGE;
+        if (x < A_LOADS)
+            copy16_to_lds(ra, sa + (4 * x + wave) * 1024, foff[x]);
+        else
+            copy16_to_lds(rb, sa + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024, foff[x - A_LOADS]);
     };
 
     auto epilogue = [&](const TileCursor& c) {
@@ -303,70 +337,90 @@ __global__ __launch_bounds__(kThreads, OCC) void tiled_gemm_kernel(GemmArgs p) {
         }
     };
 
+    // ---- schedule of one K step ---------------------------------------------
+    // The issue order inside a K step is pinned: MFMA x, then copy x (hand-off
+    // step only), then fragment read x, with a scheduling barrier after each
+    // triple.  Each MFMA occupies the matrix core for many cycles, so the
+    // reads and copies of a triple issue in its shadow and the next MFMA is
+    // ready when the matrix core frees up.
+    constexpr int N_MFMA = FM * FN;
+    constexpr int N_FRAG = FM + FN;
+    auto kstep = [&](int buf, int s, const char* rd_st, int rd_s, int copy_st, auto NCOPY,
+                     auto ZERO) {
+        constexpr int NC = decltype(NCOPY)::value;
+        constexpr int NX = N_MFMA > N_FRAG ? (N_MFMA > NC ? N_MFMA : NC)
+                                           : (N_FRAG > NC ? N_FRAG : NC);
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+            if (x < N_MFMA) mma_one(buf, s, x, ZERO);
+            if (x < NC) copy_one(copy_st, x);
+            if (x < N_FRAG) read_one(buf ^ 1, rd_st, rd_s, x);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     // ---- prologue: the first S slices in flight, slice 0 resident ---------
-    TileCursor ic = {0, 0, 0, 0, 0};
-    locate(ic);
-    TileCursor cc = ic;
-    for (int g = 0; g < S && g < total; ++g) {
-        issue(ic, g);
-        advance(ic);
+    locate(fc);
+    feed_resources();
+    TileCursor cc = fc;
+    int fg = 0;  // global slice index of the copy stream
+#pragma unroll
+    for (int g = 0; g < S; ++g, ++fg) {
+        feed_offsets(fg < total);
+        issue(g);
+        feed_advance();
     }
-    if (total >= S)
-        wait_vmcnt<(S - 1) * LOADS>();
-    else
-        wait_vmcnt<0>();
+    feed_offsets(fg < total);
+    wait_vmcnt<(S - 1) * LOADS>();
     barrier_lds();
     read_frags(0, lds, 0);
     if constexpr (Op::kScaled) load_scales(cc, sc_a, sc_b);
 
-    bool after_epilogue = false;
-    // One slice g of the current tile: K steps with double-buffered
-    // fragments, the stage hand-off folded into the last step.  ZERO marks
-    // the tile's first slice, whose first MFMAs take a zero accumulator.
+    // One slice g: K steps with double-buffered fragments.  The stage
+    // hand-off sits before the last K step: once this wave's copies of slice
+    // g + 1 have landed and every wave has passed the barrier, stage g % S is
+    // free for the copies of slice g + S, and the first fragments of slice
+    // g + 1 are read while the last K step's MFMAs run.  ZERO marks a tile's
+    // first slice, whose first MFMAs take a zero accumulator.
     auto slice = [&](int g, auto ZERO) {
         const char* st = lds + (g % S) * STAGE;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            const int cur = s & 1, nxt = cur ^ 1;
-            if (s + 1 < KSTEPS) {
-                read_frags(nxt, st, s + 1);
-            } else {
-                // Hand-off.  This slice's fragments are all in registers; once
-                // slice g + 1 has landed and every wave has passed the barrier,
-                // stage g % S is free for slice g + S and the first fragments
-                // of slice g + 1 can be read while this K step's MFMAs run.
-                __builtin_amdgcn_sched_barrier(0);
-                if (S > 2 && !after_epilogue && g + S - 1 < total)
-                    wait_vmcnt<(S > 2 ? (S - 2) * LOADS : 0)>();
-                else
-                    wait_vmcnt<0>();
-                barrier_lds();
-                __builtin_amdgcn_sched_barrier(0);
-                if (g + S < total) {
-                    issue(ic, g % S);
-                    advance(ic);
-                }
-                if (g + 1 < total) read_frags(nxt, lds + ((g + 1) % S) * STAGE, 0);
-            }
-            if constexpr (decltype(ZERO)::value) {
-                if (s == 0)
-                    mma_block(cur, s, std::true_type{});
-                else
-                    mma_block(cur, s, std::false_type{});
-            } else {
-                mma_block(cur, s, std::false_type{});
-            }
-        }
-        after_epilogue = false;
-    };
-
-    int g = 0;
-    for (int tl = 0; tl < my_tiles; ++tl) {
+        const char* st_next = lds + ((g + 1) % S) * STAGE;
         if constexpr (Op::kScaled) {
             TileCursor nc = cc;
             advance(nc);
             if (g + 1 < total) load_scales(nc, nx_a, nx_b);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr auto NONE = std::integral_constant<int, 0>{};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            const int cur = s & 1;
+            if (s + 1 < KSTEPS) {
+                if (decltype(ZERO)::value && s == 0)
+                    kstep(cur, s, st, s + 1, 0, NONE, std::true_type{});
+                else
+                    kstep(cur, s, st, s + 1, 0, NONE, std::false_type{});
+            } else {
+                if (S > 2 && g + S - 1 < total)
+                    wait_vmcnt<(S > 2 ? (S - 2) * LOADS : 0)>();
+                else
+                    wait_vmcnt<0>();
+                barrier_lds();
+                __builtin_amdgcn_sched_barrier(0);
+                constexpr auto COPIES = std::integral_constant<int, LOADS>{};
+                if (decltype(ZERO)::value && s == 0)
+                    kstep(cur, s, st_next, 0, g % S, COPIES, std::true_type{});
+                else
+                    kstep(cur, s, st_next, 0, g % S, COPIES, std::false_type{});
+            }
+        }
+        feed_advance();
+        ++fg;
+        feed_offsets(fg < total);
+    };
+
+    int g = 0;
+    for (int tl = 0; tl < my_tiles; ++tl) {
         slice(g, std::true_type{});
         if constexpr (Op::kScaled) {
             advance(cc);
@@ -377,11 +431,6 @@ __global__ __launch_bounds__(kThreads, OCC) void tiled_gemm_kernel(GemmArgs p) {
         }
         ++g;
         for (int kk = 1; kk < p.ksteps; ++kk, ++g) {
-            if constexpr (Op::kScaled) {
-                TileCursor nc = cc;
-                advance(nc);
-                if (g + 1 < total) load_scales(nc, nx_a, nx_b);
-            }
             slice(g, std::false_type{});
             if constexpr (Op::kScaled) {
                 advance(cc);
@@ -398,7 +447,6 @@ __global__ __launch_bounds__(kThreads, OCC) void tiled_gemm_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         epilogue(ec);
         __builtin_amdgcn_sched_barrier(0);
-        after_epilogue = true;
     }
 }
 
