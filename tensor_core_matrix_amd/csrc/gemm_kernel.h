@@ -20,8 +20,8 @@
 //  * Stage hand-off: the "full" condition is this wave's own vmcnt wait plus
 //    the workgroup barrier; the "empty" condition is the same barrier, since
 //    every wave has read its fragments of the previous slice before it.
-//  * XOR-swizzled LDS rows so that the 16-byte fragment reads of 64 lanes
-//    spread over all banks (the swizzled shared layouts of "Blackwell Tensor
+//  * XOR-swizzled LDS rows so that each group of 16 lanes of a 16-byte
+//    fragment read spreads over all 64 banks (the swizzled shared layouts of "Blackwell Tensor
 //    Cores", The Accumulator's Lifetime, redesigned for LDS banks).
 //  * Four waves in a 2 x 2 arrangement, each owning a (BM/2) x (BN/2) block of
 //    32 x 32 MFMA accumulators; the first slice of a tile starts from zero and

@@ -3,8 +3,10 @@
 
 namespace tcm {
 
-// LDS rows of a 128-deep fp8 slice are 128 bytes (8 chunks).
-constexpr int kSwizzle8 = 0;
+// LDS rows of a 128-deep fp8 slice are 128 bytes (8 chunks); as for 64-deep
+// bf16 slices the chunk is XORed with (row / 2) % 8 so that the 16 rows read
+// together by 16 lanes hit 16 different 16-byte bank groups.
+constexpr int kSwizzle8 = 1;
 
 template <typename TOut, int BM, int BN, bool WORDS>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {

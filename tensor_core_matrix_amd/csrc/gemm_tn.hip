@@ -3,12 +3,15 @@
 
 namespace tcm {
 
-// The 16-byte chunk XOR of an LDS row uses row bits selected by a shift: rows
-// of a 64-deep bf16 slice are 128 bytes (8 chunks, row bits 0..2), rows of a
-// 32-deep slice 64 bytes (4 chunks, row bits 1..2, so that the 8 rows read
-// together by 8 lanes land on 8 different 16-byte bank groups).
+// The 16-byte chunk XOR of an LDS row uses row bits selected by a shift.  A
+// 16-byte fragment read is served 16 lanes (16 consecutive rows) at a time
+// across 64 four-byte banks (256 bytes), so the 16 rows of a group must land
+// on 16 different 16-byte bank groups: with 128-byte rows (64-deep bf16
+// slices) row r covers groups 8 (r % 2) + chunk, and the chunk is XORed with
+// (r / 2) % 8; with 64-byte rows (32-deep slices) row r covers groups
+// 4 (r % 4) + chunk, and the chunk is XORed with (r / 4) % 4.
 template <int BK>
-constexpr int swizzle_shift() { return BK == 64 ? 0 : 1; }
+constexpr int swizzle_shift() { return BK == 64 ? 1 : 2; }
 
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
