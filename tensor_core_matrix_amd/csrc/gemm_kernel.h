@@ -84,7 +84,7 @@ struct TileCursor {
 };
 
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int SWZ,
-          bool SCALE_WORDS = false>
+          bool SCALE_WORDS = false, int NSPLIT = 1>
 __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void tiled_gemm_kernel(GemmArgs p) {
     constexpr int ESZ = Op::kElemBytes;
@@ -104,6 +104,8 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert(KSTEPS % 2 == 0, "fragment double buffer alternates per K step");
     static_assert(((4 * ROWS_PER_WAVE_COPY) >> SWZ) % CPR == 0, "copy chunk independent of i");
     static_assert((S - 1) * LOADS < 64, "vmcnt range");
+    static_assert(NSPLIT >= 1 && NSPLIT <= KSTEPS && LOADS % NSPLIT == 0, "copy split");
+    constexpr int PART = LOADS / NSPLIT;  // copies per part
     static_assert(CPR == 4 || CPR == 8, "row slice must be 64 or 128 bytes");
     static_assert(A_BYTES % (kThreads * 16) == 0 && B_BYTES % (kThreads * 16) == 0, "copy split");
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
@@ -338,40 +340,54 @@ void tiled_gemm_kernel(GemmArgs p) {
     };
 
     // ---- schedule of one K step ---------------------------------------------
-    // The issue order inside a K step is pinned: MFMA x, then copy x (hand-off
-    // step only), then fragment read x, with a scheduling barrier after each
-    // triple.  Each MFMA occupies the matrix core for many cycles, so the
-    // reads and copies of a triple issue in its shadow and the next MFMA is
-    // ready when the matrix core frees up.
+    // The issue order inside a K step is pinned: MFMA x, then copy x (when the
+    // step carries copies), then fragment read x, with a scheduling barrier
+    // after each triple.  Each MFMA occupies the matrix core for many cycles,
+    // so the reads and copies of a triple issue in its shadow and the next
+    // MFMA is ready when the matrix core frees up.
     constexpr int N_MFMA = FM * FN;
     constexpr int N_FRAG = FM + FN;
-    auto kstep = [&](int buf, int s, const char* rd_st, int rd_s, int copy_st, auto NCOPY,
-                     auto ZERO) {
+    auto kstep = [&](int buf, int s, const char* rd_st, int rd_s, int copy_st, int copy_base,
+                     auto NCOPY, auto ZERO) {
         constexpr int NC = decltype(NCOPY)::value;
         constexpr int NX = N_MFMA > N_FRAG ? (N_MFMA > NC ? N_MFMA : NC)
                                            : (N_FRAG > NC ? N_FRAG : NC);
 #pragma unroll
         for (int x = 0; x < NX; ++x) {
             if (x < N_MFMA) mma_one(buf, s, x, ZERO);
-            if (x < NC) copy_one(copy_st, x);
+            if (x < NC) copy_one(copy_st, copy_base + x);
             if (x < N_FRAG) read_one(buf ^ 1, rd_st, rd_s, x);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // ---- prologue: the first S slices in flight, slice 0 resident ---------
+    // ---- the copy stream's schedule -----------------------------------------
+    // The copies of slice g + S go out in NSPLIT parts: part 0 in slice g's
+    // hand-off step (right after the barrier frees stage g % S), parts
+    // 1 .. NSPLIT-1 in the first K steps of slice g + 1.  Spreading them keeps
+    // the per-CU request rate within what the vector L1 can pass to L2; a
+    // burst of a whole stage fills the address FIFOs and stalls MFMA issue.
+    int fg = 0;  // global slice index of the copy stream
+    auto feed_next = [&]() {
+        feed_advance();
+        ++fg;
+        feed_offsets(fg < total);
+    };
+
+    // ---- prologue: slices 0 .. S-2 and part 0 of slice S-1 in flight -------
     locate(fc);
     feed_resources();
     TileCursor cc = fc;
-    int fg = 0;  // global slice index of the copy stream
+    feed_offsets(true);
 #pragma unroll
-    for (int g = 0; g < S; ++g, ++fg) {
-        feed_offsets(fg < total);
+    for (int g = 0; g < S - 1; ++g) {
         issue(g);
-        feed_advance();
+        feed_next();
     }
-    feed_offsets(fg < total);
-    wait_vmcnt<(S - 1) * LOADS>();
+#pragma unroll
+    for (int x = 0; x < PART; ++x) copy_one(S - 1, x);
+    if constexpr (NSPLIT == 1) feed_next();
+    wait_vmcnt<(S - 2) * LOADS + PART>();
     barrier_lds();
     read_frags(0, lds, 0);
     if constexpr (Op::kScaled) load_scales(cc, sc_a, sc_b);
@@ -382,6 +398,7 @@ void tiled_gemm_kernel(GemmArgs p) {
     // free for the copies of slice g + S, and the first fragments of slice
     // g + 1 are read while the last K step's MFMAs run.  ZERO marks a tile's
     // first slice, whose first MFMAs take a zero accumulator.
+    bool after_epilogue = false;
     auto slice = [&](int g, auto ZERO) {
         const char* st = lds + (g % S) * STAGE;
         const char* st_next = lds + ((g + 1) % S) * STAGE;
@@ -392,31 +409,41 @@ void tiled_gemm_kernel(GemmArgs p) {
         }
         __builtin_amdgcn_sched_barrier(0);
         constexpr auto NONE = std::integral_constant<int, 0>{};
+        constexpr auto ONE_PART = std::integral_constant<int, PART>{};
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             const int cur = s & 1;
+            const bool zero = decltype(ZERO)::value && s == 0;
             if (s + 1 < KSTEPS) {
-                if (decltype(ZERO)::value && s == 0)
-                    kstep(cur, s, st, s + 1, 0, NONE, std::true_type{});
-                else
-                    kstep(cur, s, st, s + 1, 0, NONE, std::false_type{});
+                if (s + 1 < NSPLIT) {
+                    // a later part of slice g - 1 + S, into stage (g - 1) % S
+                    const int cst = (g + S - 1) % S;
+                    if (zero)
+                        kstep(cur, s, st, s + 1, cst, (s + 1) * PART, ONE_PART, std::true_type{});
+                    else
+                        kstep(cur, s, st, s + 1, cst, (s + 1) * PART, ONE_PART, std::false_type{});
+                    if (s + 2 == NSPLIT) feed_next();
+                } else {
+                    if (zero)
+                        kstep(cur, s, st, s + 1, 0, 0, NONE, std::true_type{});
+                    else
+                        kstep(cur, s, st, s + 1, 0, 0, NONE, std::false_type{});
+                }
             } else {
-                if (S > 2 && g + S - 1 < total)
+                if (S > 2 && !after_epilogue && g + S - 1 < total)
                     wait_vmcnt<(S > 2 ? (S - 2) * LOADS : 0)>();
                 else
                     wait_vmcnt<0>();
+                after_epilogue = false;
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
-                constexpr auto COPIES = std::integral_constant<int, LOADS>{};
-                if (decltype(ZERO)::value && s == 0)
-                    kstep(cur, s, st_next, 0, g % S, COPIES, std::true_type{});
+                if (zero)
+                    kstep(cur, s, st_next, 0, g % S, 0, ONE_PART, std::true_type{});
                 else
-                    kstep(cur, s, st_next, 0, g % S, COPIES, std::false_type{});
+                    kstep(cur, s, st_next, 0, g % S, 0, ONE_PART, std::false_type{});
             }
         }
-        feed_advance();
-        ++fg;
-        feed_offsets(fg < total);
+        if constexpr (NSPLIT == 1) feed_next();
     };
 
     int g = 0;
@@ -447,6 +474,7 @@ void tiled_gemm_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         epilogue(ec);
         __builtin_amdgcn_sched_barrier(0);
+        after_epilogue = true;
     }
 }
 

@@ -13,10 +13,11 @@ namespace tcm {
 template <int BK>
 constexpr int swizzle_shift() { return BK == 64 ? 1 : 2; }
 
-template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC>
+template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int NSPLIT = 1>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, swizzle_shift<BK>()>),
-                       dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(
+        (tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, swizzle_shift<BK>(), false, NSPLIT>),
+        dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -27,8 +28,9 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_T128x256: return launch_one<Op, TOut, 128, 256, 64, 2, 1>(a, grid, st);
     case V_T128x128: return launch_one<Op, TOut, 128, 128, 64, 2, 2>(a, grid, st);
     case V_T128x64: return launch_one<Op, TOut, 128, 64, 64, 2, 3>(a, grid, st);
-    case V_T256x256_K32S4: return launch_one<Op, TOut, 256, 256, 32, 4, 1>(a, grid, st);
-    case V_T256x256_K32S5: return launch_one<Op, TOut, 256, 256, 32, 5, 1>(a, grid, st);
+    case V_T256x256_K32S4: return launch_one<Op, TOut, 256, 256, 32, 4, 1, 2>(a, grid, st);
+    case V_T256x256_K32S5: return launch_one<Op, TOut, 256, 256, 32, 5, 1, 2>(a, grid, st);
+    case V_T256x256_SPLIT2: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 2>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

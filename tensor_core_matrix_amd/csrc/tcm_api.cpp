@@ -23,6 +23,7 @@ VariantInfo variant_info(int32_t v) {
     case V_T128x64: return {128, 64, 64, 2, 3, 2};
     case V_T256x256_K32S4: return {256, 256, 32, 4, 1, 2};
     case V_T256x256_K32S5: return {256, 256, 32, 5, 1, 2};
+    case V_T256x256_SPLIT2: return {256, 256, 64, 2, 1, 2};
     case V_MX256x256: return {256, 256, 128, 2, 1, 1};
     case V_MX128x128: return {128, 128, 128, 2, 1, 1};
     }
@@ -103,14 +104,12 @@ tcm_status check_range(int64_t batch, int64_t M, int64_t N, int64_t K) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// TCM_FORCE_VARIANT=<id> (read once) forces a kernel variant of the matching
-// family, for tuning sweeps; unset, the heuristic below chooses.
+// TCM_FORCE_VARIANT=<id> (read at every call) forces a kernel variant of the
+// matching family, for tuning sweeps and per-variant tests; unset or invalid,
+// the heuristic below chooses.
 int32_t forced_variant() {
-    static const int32_t v = [] {
-        const char* e = getenv("TCM_FORCE_VARIANT");
-        return e && *e ? (int32_t)atoi(e) : (int32_t)-1;
-    }();
-    return v;
+    const char* e = getenv("TCM_FORCE_VARIANT");
+    return e && *e ? (int32_t)atoi(e) : (int32_t)-1;
 }
 
 // Tile choice: the largest tile whose tile count still gives every CU at

@@ -35,6 +35,7 @@ enum Variant : int32_t {
     V_T128x64 = 3,    // 128x64x64, 2-stage ring, 3 workgroups per CU
     V_T256x256_K32S4 = 4,  // 256x256x32, 4-stage ring
     V_T256x256_K32S5 = 5,  // 256x256x32, 5-stage ring (all 160 KiB of LDS)
+    V_T256x256_SPLIT2 = 6, // 256x256x64, 2-stage ring, copies split over 2 K steps
     V_MX256x256 = 10, // MXFP8 256x256x128, 2-stage ring
     V_MX128x128 = 11, // MXFP8 128x128x128, 2-stage ring
 };

@@ -294,3 +294,58 @@ def test_repeat_runs_bitwise_identical():
     o2 = tcm.gemm_tn(a, b, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+# ------------------------------------------------------ every kernel variant
+PLAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6]
+MX_VARIANTS = [10, 11]
+
+
+@pytest.fixture
+def force_variant(monkeypatch):
+    def _set(v):
+        monkeypatch.setenv("TCM_FORCE_VARIANT", str(v))
+    return _set
+
+
+@pytest.mark.parametrize("v", PLAIN_VARIANTS)
+def test_each_plain_variant(v, force_variant):
+    """Every tile / ring variant, forced: a ragged multi-tile shape with several
+    tiles per workgroup, bf16 and fp32 outputs, plus an exact case."""
+    force_variant(v)
+    M, N, K = 1100, 600, 1000
+    g = inp.generator(200 + v)
+    a = inp.normal((M, K), g, 1.0, torch.bfloat16)
+    b = inp.normal((N, K), g, 1.0, torch.bfloat16)
+    ref, s = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    for odt in ("f32", "bf16"):
+        assert_parity(run_plain(a, b, odt), ref, s, odt, f"variant {v} {odt}")
+    q = inp.quarter_integers((640, 512), g, torch.float16)
+    r = inp.quarter_integers((384, 512), g, torch.float16)
+    qref, _ = orc.gemm_tn(orc.F16, inp.raw(q), inp.raw(r))
+    assert np.array_equal(_np(run_plain(q, r, "f32")), qref)
+
+
+@pytest.mark.parametrize("v", MX_VARIANTS)
+def test_each_mx_variant(v, force_variant):
+    force_variant(v)
+    M, N, K = 700, 520, 640
+    g = inp.generator(300 + v)
+    a = inp.e4m3_normal((M, K), g)
+    b = inp.e4m3_normal((N, K), g)
+    sa = inp.e8m0_scales((M, K // 32), g)
+    sb = inp.e8m0_scales((N, K // 32), g)
+    ref, s = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb))
+    for odt in ("f32", "bf16"):
+        assert_parity(run_mx(a, b, sa, sb, odt), ref, s, odt, f"mx variant {v} {odt}")
+
+
+def test_batched_workload_through_large_tiles(force_variant):
+    """The batched problems forced through the 256 x 256 persistent kernel
+    (half of every tile lies past M = 128)."""
+    force_variant(0)
+    g = inp.generator(301)
+    a = inp.uniform((64, 128, 64), g, torch.bfloat16)
+    b = inp.uniform((64, 256, 64), g, torch.bfloat16)
+    ref, s = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    assert_parity(run_plain(a, b, "f32", batched=True), ref, s, "f32", "batched via 256x256")
