@@ -117,7 +117,7 @@ int32_t forced_variant() {
 int32_t choose_variant(int64_t batch, int64_t M, int64_t N, bool mx, int cus) {
     const int32_t f = forced_variant();
     if (f >= 0 && variant_info(f).tile_m > 0 && (f >= V_MX256x256) == mx) return f;
-    static const int32_t plain[] = {V_T256x256, V_T128x256, V_T128x128, V_T128x64};
+    static const int32_t plain[] = {V_T256x256_SPLIT2, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MX256x256, V_MX128x128};
     const int32_t* cand = mx ? mxv : plain;
     const int n = mx ? 2 : 4;
