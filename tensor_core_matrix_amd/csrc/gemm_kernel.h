@@ -84,7 +84,7 @@ struct TileCursor {
 };
 
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int SWZ,
-          bool SCALE_WORDS = false, int NSPLIT = 1>
+          bool SCALE_WORDS = false, int NSPLIT = 1, bool EPI_LDS = false>
 __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void tiled_gemm_kernel(GemmArgs p) {
     constexpr int ESZ = Op::kElemBytes;
@@ -113,7 +113,12 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert((32 >> SWZ) % CPR == 0, "swizzle must depend on the row within 32 only");
     static_assert(!Op::kScaled || (BK == 128 && S == 2), "MX path: 128-deep slices, 2 stages");
 
-    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
+    // Epilogue staging: one 32-row block of a wave's output at a time, in a
+    // wave-private LDS area after the ring.
+    constexpr int STG_ROWB = WTN * (int)sizeof(TOut);  // bytes of one staged row
+    constexpr int STG_BYTES = EPI_LDS ? 32 * STG_ROWB : 0;
+    static_assert(S * STAGE + 4 * STG_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE + 4 * STG_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -298,6 +303,46 @@ void tiled_gemm_kernel(GemmArgs p) {
         const int m_base = c.tm * BM + wm * WTM + l32;
         const int n_base = c.tn * BN + wn * WTN + 4 * hi;
         const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (p.N & 3) == 0;
+        if constexpr (EPI_LDS) {
+            // Interior tiles go through LDS: each 32-row block of the wave's
+            // output is written to the wave's staging area in the MFMA layout,
+            // read back as 16-byte row pieces, and stored so that every store
+            // instruction writes whole 256-byte row segments (4 rows for
+            // bf16, 2 for fp32) instead of 16-byte pieces of 32 rows.
+            if (full && (p.N * (int)sizeof(TOut)) % 16 == 0) {
+                constexpr int CHK = STG_ROWB / 16;          // 16-byte chunks per staged row
+                constexpr int RPI = kWaveSize * 16 / STG_ROWB;  // rows per store instruction
+                char* stg = lds + S * STAGE + wave * STG_BYTES;
+                const int row_l = l32;                       // staged row this lane writes
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x16_t& a4 = acc[i][j];
+                            const int col = j * 32 + 8 * q + 4 * hi;  // column within the wave tile
+                            const int byte = col * (int)sizeof(TOut);
+                            const int chunk = (byte / 16) ^ (row_l & (CHK - 1));
+                            char* dst = stg + row_l * STG_ROWB + chunk * 16 + byte % 16;
+                            store4<TOut>((TOut*)dst, a4[4 * q], a4[4 * q + 1], a4[4 * q + 2],
+                                         a4[4 * q + 3]);
+                        }
+                    // same-wave LDS writes then reads: the wave's own order holds
+#pragma unroll
+                    for (int t = 0; t < 32 / RPI; ++t) {
+                        const int r = t * RPI + lane / CHK;
+                        const int ck = lane % CHK;
+                        const i32x4_t d = *(const i32x4_t*)(stg + r * STG_ROWB +
+                                                            ((ck ^ (r & (CHK - 1))) * 16));
+                        char* g = Cb + ((int64_t)(c.tm * BM + wm * WTM + i * 32 + r) * p.N +
+                                        c.tn * BN + wn * WTN) * (int64_t)sizeof(TOut) + ck * 16;
+                        *(i32x4_t*)g = d;
+                    }
+                }
+                return;
+            }
+        }
         if (full) {
             // interior tile: one 4-wide store per (block, r / 4), no masks
 #pragma unroll

@@ -10,8 +10,10 @@ constexpr int kSwizzle8 = 1;
 
 template <typename TOut, int BM, int BN, bool WORDS>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((tiled_gemm_kernel<OpMXFP8, TOut, BM, BN, 128, 2, 1, kSwizzle8, WORDS>),
-                       dim3(grid), dim3(kThreads), 0, st, a);
+    constexpr bool epi = 2 * (BM + BN) * 128 + 4 * 32 * (BN / 2) * (int)sizeof(TOut) <= 160 * 1024;
+    hipLaunchKernelGGL(
+        (tiled_gemm_kernel<OpMXFP8, TOut, BM, BN, 128, 2, 1, kSwizzle8, WORDS, 1, epi>),
+        dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 

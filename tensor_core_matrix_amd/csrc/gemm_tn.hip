@@ -13,10 +13,19 @@ namespace tcm {
 template <int BK>
 constexpr int swizzle_shift() { return BK == 64 ? 1 : 2; }
 
-template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int NSPLIT = 1>
+// Output staging through LDS is used where the ring leaves room for it: 32
+// rows of each wave's output tile per wave, next to the ring.
+template <typename TOut, int BM, int BN, int BK, int S>
+constexpr bool epilogue_fits() {
+    return S * (BM + BN) * BK * 2 + 4 * 32 * (BN / 2) * (int)sizeof(TOut) <= 160 * 1024;
+}
+
+template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int NSPLIT = 1,
+          bool EPI = true>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
+    constexpr bool epi = EPI && OCC == 1 && epilogue_fits<TOut, BM, BN, BK, S>();
     hipLaunchKernelGGL(
-        (tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, swizzle_shift<BK>(), false, NSPLIT>),
+        (tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, swizzle_shift<BK>(), false, NSPLIT, epi>),
         dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
@@ -24,7 +33,7 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
 template <class Op, typename TOut>
 static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t st) {
     switch (v) {
-    case V_T256x256: return launch_one<Op, TOut, 256, 256, 64, 2, 1>(a, grid, st);
+    case V_T256x256: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 1, false>(a, grid, st);
     case V_T128x256: return launch_one<Op, TOut, 128, 256, 64, 2, 1>(a, grid, st);
     case V_T128x128: return launch_one<Op, TOut, 128, 128, 64, 2, 2>(a, grid, st);
     case V_T128x64: return launch_one<Op, TOut, 128, 64, 64, 2, 3>(a, grid, st);
