@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s and % of MFMA dense peak (bf16 8192³; MXFP8 8192³)"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}   # dense MFMA, MI355X
 HBM_GBS = 8000.0
-KERNEL_SOURCES = ["gemm_kernel.h", "tcm_device.h", "tcm_internal.h", "gemm_tn.hip",
+KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pingpong.h", "tcm_device.h", "tcm_internal.h", "gemm_tn.hip",
                   "gemm_mx.hip", "tcm_api.cpp"]
 
 

@@ -1,5 +1,5 @@
 // Kernel instances and launcher for the MXFP8 (E4M3 + E8M0 per 32) product.
-#include "gemm_kernel.h"
+#include "gemm_pingpong.h"
 
 namespace tcm {
 
@@ -8,12 +8,19 @@ namespace tcm {
 // together by 16 lanes hit 16 different 16-byte bank groups.
 constexpr int kSwizzle8 = 1;
 
-template <typename TOut, int BM, int BN, bool WORDS>
+template <typename TOut, int BM, int BN, bool WORDS, int NSPLIT = 1>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     constexpr bool epi = 2 * (BM + BN) * 128 + 4 * 32 * (BN / 2) * (int)sizeof(TOut) <= 160 * 1024;
     hipLaunchKernelGGL(
-        (tiled_gemm_kernel<OpMXFP8, TOut, BM, BN, 128, 2, 1, kSwizzle8, WORDS, 1, epi>),
+        (tiled_gemm_kernel<OpMXFP8, TOut, BM, BN, 128, 2, 1, kSwizzle8, WORDS, NSPLIT, epi>),
         dim3(grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename TOut, bool WORDS>
+static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, WORDS>), dim3(grid), dim3(kPPThreads), 0,
+                       st, a);
     return hipGetLastError();
 }
 
@@ -22,6 +29,8 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     switch (v) {
     case V_MX256x256: return launch_one<TOut, 256, 256, WORDS>(a, grid, st);
     case V_MX128x128: return launch_one<TOut, 128, 128, WORDS>(a, grid, st);
+    case V_MX256x256_SPLIT2: return launch_one<TOut, 256, 256, WORDS, 2>(a, grid, st);
+    case V_MXPP256: return launch_pp<TOut, WORDS>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

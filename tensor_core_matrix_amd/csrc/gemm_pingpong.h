@@ -1,0 +1,340 @@
+// Ping-pong variant of the tiled product kernel for gfx950: a 256 x 256
+// output tile, eight waves, two per SIMD, taking turns on the matrix core.
+//
+// "Hopper and Blackwell GEMM" (Concept) describes two consumer warpgroups
+// taking turns so that one group's epilogue hides under the other's MMAs,
+// and a producer that only issues loads.  On CDNA4 every wave of a kernel
+// gets the same register budget, so a producer-only wave cannot sit beside
+// waves holding a 256-register accumulator.  Here the two roles alternate
+// within each wave instead:
+//
+//  * Group 0 (waves 0-3) owns output rows 0-127 of the tile, group 1 (waves
+//    4-7) rows 128-255; wave w of a group owns columns 64 (w % 4) .. +63.
+//    Each wave holds a 128 x 64 fp32 accumulator (128 registers) and all
+//    fragments of one K slice (96 registers).
+//  * Time is cut into half-periods separated by workgroup barriers.  In
+//    half 2j group 0 runs the MFMAs of slice j while group 1 reads its
+//    fragments of slice j from LDS; in half 2j+1 group 1 runs slice j while
+//    group 0 reads its fragments of slice j+1 and issues the copies of slice
+//    j+2.  A wave in its MFMA half issues nothing but MFMAs, so stalls of the
+//    copy and read instructions (full address FIFOs, LDS latency) fall on the
+//    other wave and the matrix core of each SIMD stays busy.
+//  * Two-stage LDS ring of 64-deep (bf16) / 128-deep (fp8) slices.  Stage
+//    j % 2 is read in halves 2j-1 (group 0) and 2j (group 1); the copies of
+//    slice j+2 into it are issued in half 2j+1 by group 0, which waits for
+//    them at the end of its next MFMA half, before anyone reads them.
+//  * The epilogue of a tile runs in each wave's memory half right after its
+//    last MFMA half -- while the other group computes -- staged through a
+//    wave-private LDS area so that every store writes whole 128-byte row
+//    segments.  This is the two-accumulator overlap of the pages, with the
+//    second accumulator set held by the other group's waves.
+#pragma once
+
+#include <type_traits>
+
+#include "gemm_kernel.h"
+
+namespace tcm {
+
+constexpr int kPPThreads = 512;  // eight waves
+
+template <class Op, typename TOut, bool SCALE_WORDS = false>
+__global__ __launch_bounds__(kPPThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void pingpong_gemm_kernel(GemmArgs p) {
+    constexpr int BM = 256, BN = 256, S = 2;
+    constexpr int ESZ = Op::kElemBytes;
+    constexpr int BK = 128 / ESZ;  // 128-byte LDS rows: 64 bf16 / 128 fp8
+    constexpr int RB = 128;
+    constexpr int CPR = 8;
+    constexpr int SWZ = 1;  // chunk ^= (row / 2) % 8: 16 rows of a read group, 16 bank groups
+    constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB, STAGE = A_BYTES + B_BYTES;
+    constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32;
+    constexpr int KSTEPS = BK / Op::kK;
+    constexpr int CPL = Op::kK * ESZ / 32;
+    constexpr int N_FRAG = FM + FN;
+    // copies: group 0's four waves move a whole stage, 16 KiB each
+    constexpr int A_LOADS = A_BYTES / (4 * kWaveSize * 16);
+    constexpr int B_LOADS = B_BYTES / (4 * kWaveSize * 16);
+    constexpr int LOADS = A_LOADS + B_LOADS;
+    constexpr int ROWS_PER_WAVE_COPY = kWaveSize * 16 / RB;
+    // epilogue staging: 32 rows x 64 columns per wave (bf16 only)
+    constexpr bool EPI_LDS = sizeof(TOut) == 2;
+    constexpr int STG_ROWB = WTN * (int)sizeof(TOut);
+    constexpr int STG_BYTES = EPI_LDS ? 32 * STG_ROWB : 0;
+    static_assert(S * STAGE + 8 * STG_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(LOADS < 64, "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE + 8 * STG_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, sub = wave & 3;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    const int G = gridDim.x;
+    const int lid = logical_block(blockIdx.x, G);
+    if (lid >= p.total_tiles) return;
+    const int my_tiles = (p.total_tiles - 1 - lid) / G + 1;
+    const int T = my_tiles * p.ksteps;  // slices of this workgroup
+    const int K = p.K;
+
+    auto locate = [&](TileCursor& c) { tile_coords(p, c.tl * G + lid, c.batch, c.tm, c.tn); };
+    auto advance = [&](TileCursor& c) {
+        if (++c.kk == p.ksteps) {
+            c.kk = 0;
+            if (++c.tl < my_tiles) locate(c);
+        }
+    };
+
+    // ---- copy stream (group 0 only) ------------------------------------------
+    const int cp_row = sub * ROWS_PER_WAVE_COPY + lane / CPR;
+    const int cp_chunk = (lane % CPR) ^ ((cp_row >> SWZ) & (CPR - 1));
+    const uint32_t cp_off = (uint32_t)cp_row * (uint32_t)K * ESZ + cp_chunk * 16;
+    const int cp_k = cp_chunk * (16 / ESZ);
+    const uint32_t cp_step = 4u * ROWS_PER_WAVE_COPY * (uint32_t)K * ESZ;
+    TileCursor fc = {0, 0, 0, 0, 0};
+    __amdgpu_buffer_rsrc_t ra, rb;
+    auto feed_resources = [&]() {
+        const int rows_a = min(BM, p.M - fc.tm * BM);
+        const int rows_b = min(BN, p.N - fc.tn * BN);
+        const char* abase = (const char*)p.A + fc.batch * p.stride_a + (int64_t)fc.tm * BM * K * ESZ;
+        const char* bbase = (const char*)p.B + fc.batch * p.stride_b + (int64_t)fc.tn * BN * K * ESZ;
+        ra = make_rsrc(abase, (uint32_t)rows_a * (uint32_t)K * ESZ);
+        rb = make_rsrc(bbase, (uint32_t)rows_b * (uint32_t)K * ESZ);
+    };
+    int fg = 0;  // slice the copy stream is on
+    // Copies of slice fg into its stage; past the last slice every offset is
+    // out of range (no memory touched, the stage is never read again).
+    auto issue = [&]() {
+        const int k0 = fc.kk * BK;
+        const uint32_t off0 =
+            (fg < T && k0 + cp_k < K) ? cp_off + (uint32_t)k0 * ESZ : kOutOfRange;
+        char* sa = lds + (fg % S) * STAGE;
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i)
+            copy16_to_lds(ra, sa + (4 * i + sub) * 1024, off0 + i * cp_step);
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i)
+            copy16_to_lds(rb, sa + A_BYTES + (4 * i + sub) * 1024, off0 + i * cp_step);
+        if (++fc.kk == p.ksteps) {
+            fc.kk = 0;
+            if (++fc.tl < my_tiles) {
+                locate(fc);
+                feed_resources();
+            }
+        }
+        ++fg;
+    };
+
+    // ---- fragments of one slice ------------------------------------------------
+    const int xr = (l32 >> SWZ) & (CPR - 1);
+    const uint32_t a_frag = (uint32_t)(grp * WTM + l32) * RB;
+    const uint32_t b_frag = (uint32_t)A_BYTES + (uint32_t)(sub * WTN + l32) * RB;
+    typedef typename Op::frag_t frag_t;
+    frag_t fa[KSTEPS][FM], fb[KSTEPS][FN];
+    auto read_frag = [&](const char* base, int s) -> frag_t {
+        frag_t f;
+        if constexpr (CPL == 1) {
+            f = *(const frag_t*)(base + (((2 * s + hi) ^ xr) * 16));
+        } else {
+            // scaled MFMA: block 0 of the 64 K values in bytes 0..15 of both
+            // half-waves, block 1 in bytes 16..31
+            i32x4_t lo = *(const i32x4_t*)(base + (((4 * s + hi) ^ xr) * 16));
+            i32x4_t up = *(const i32x4_t*)(base + (((4 * s + 2 + hi) ^ xr) * 16));
+            f = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        return f;
+    };
+    auto read_slice = [&](int j) {
+        const char* st = lds + (j % S) * STAGE;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) fa[s][i] = read_frag(st + a_frag + i * 32 * RB, s);
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) fb[s][jj] = read_frag(st + b_frag + jj * 32 * RB, s);
+        }
+    };
+
+    // ---- MX scales of one slice -------------------------------------------------
+    int sc_a[Op::kScaled ? FM : 1], sc_b[Op::kScaled ? FN : 1];
+    auto load_scales = [&](const TileCursor& c) {
+        if constexpr (Op::kScaled) {
+            const int kblocks = K / 32;
+            const int kb0 = c.kk * (BK / 32);
+#pragma unroll
+            for (int f = 0; f < FM + FN; ++f) {
+                const bool is_a = f < FM;
+                const int idx = is_a ? f : f - FM;
+                const int lim = is_a ? p.M : p.N;
+                int row = (is_a ? c.tm * BM + grp * WTM : c.tn * BN + sub * WTN) + idx * 32 + l32;
+                row = min(row, lim - 1);
+                const uint8_t* src = (const uint8_t*)(is_a ? p.SA : p.SB) + (int64_t)row * kblocks;
+                int v;
+                if constexpr (SCALE_WORDS) {
+                    uint32_t w = *(const uint32_t*)(src + kb0);
+                    v = (int)(w >> (8 * hi));
+                } else {
+                    int q0 = kb0 + hi, q2 = kb0 + 2 + hi;
+                    int b0 = q0 < kblocks ? src[q0] : 127;
+                    int b2 = q2 < kblocks ? src[q2] : 127;
+                    v = b0 | (b2 << 16);
+                }
+                if (is_a) sc_a[idx] = v; else sc_b[idx] = v;
+            }
+        }
+    };
+
+    // ---- MFMAs of one slice -------------------------------------------------------
+    f32x16_t acc[FM][FN];
+    auto compute = [&](auto ZERO) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    f32x16_t c;
+                    if constexpr (decltype(ZERO)::value) {
+                        if (s == 0) c = (f32x16_t){};
+                        else c = acc[i][j];
+                    } else {
+                        c = acc[i][j];
+                    }
+                    if constexpr (Op::kScaled) {
+                        if (s == 0)
+                            acc[i][j] = Op::template mma<0>(fb[s][j], fa[s][i], c, sc_b[j], sc_a[i]);
+                        else
+                            acc[i][j] = Op::template mma<2>(fb[s][j], fa[s][i], c, sc_b[j], sc_a[i]);
+                    } else {
+                        acc[i][j] = Op::mma(fb[s][j], fa[s][i], c);
+                    }
+                }
+    };
+
+    // ---- epilogue of this wave's 128 x 64 block --------------------------------
+    auto epilogue = [&](const TileCursor& c) {
+        char* Cb = (char*)p.C + c.batch * p.stride_c;
+        const int row0 = c.tm * BM + grp * WTM;
+        const int col0 = c.tn * BN + sub * WTN;
+        const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N;
+        if constexpr (EPI_LDS) {
+            if (full && (p.N * (int)sizeof(TOut)) % 16 == 0) {
+                constexpr int CHK = STG_ROWB / 16;
+                constexpr int RPI = kWaveSize * 16 / STG_ROWB;
+                char* stg = lds + S * STAGE + wave * STG_BYTES;
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x16_t& a4 = acc[i][j];
+                            const int byte = (j * 32 + 8 * q + 4 * hi) * (int)sizeof(TOut);
+                            const int chunk = (byte / 16) ^ (l32 & (CHK - 1));
+                            store4<TOut>((TOut*)(stg + l32 * STG_ROWB + chunk * 16 + byte % 16),
+                                         a4[4 * q], a4[4 * q + 1], a4[4 * q + 2], a4[4 * q + 3]);
+                        }
+#pragma unroll
+                    for (int t = 0; t < 32 / RPI; ++t) {
+                        const int r = t * RPI + lane / CHK;
+                        const int ck = lane % CHK;
+                        const i32x4_t d =
+                            *(const i32x4_t*)(stg + r * STG_ROWB + ((ck ^ (r & (CHK - 1))) * 16));
+                        char* g = Cb + ((int64_t)(row0 + i * 32 + r) * p.N + col0) *
+                                           (int64_t)sizeof(TOut) + ck * 16;
+                        *(i32x4_t*)g = d;
+                    }
+                }
+                return;
+            }
+        }
+        const bool vec = (p.N & 3) == 0;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = row0 + i * 32 + l32;
+            if (m >= p.M) continue;
+            TOut* row = (TOut*)Cb + (int64_t)m * p.N;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = col0 + j * 32 + 8 * q + 4 * hi;
+                    if (vec && n + 3 < p.N) {
+                        store4<TOut>(row + n, acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                     acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N) row[n + e] = convert_out<TOut>(acc[i][j][4 * q + e]);
+                    }
+                }
+        }
+    };
+
+    // ---- prologue: slice 0 resident ----------------------------------------------
+    locate(fc);
+    feed_resources();
+    if (grp == 0) {
+        issue();           // slice 0
+        wait_vmcnt<0>();
+    }
+    barrier_lds();
+
+    // ---- half-periods -------------------------------------------------------------
+    // Group 0 reads slice j (and issues the copies of slice j + 1) in half
+    // 2j - 1 and computes it in half 2j; group 1 reads slice j in half 2j and
+    // computes it in half 2j + 1.  Each group runs one plain loop
+    //     memory half (epilogue of a finished tile, fragments of slice j),
+    //     barrier, MFMA half (slice j), barrier
+    // with group 1 one half behind, so both execute 2T + 2 barriers.
+    auto run = [&](auto GROUP0) {
+        constexpr bool G0 = decltype(GROUP0)::value;
+        TileCursor cc = {0, 0, 0, 0, 0};
+        locate(cc);
+        if constexpr (!G0) __builtin_amdgcn_s_barrier();  // half -1: group 0 reads slice 0
+        for (int j = 0; j < T; ++j) {
+            // ---- memory half
+            if (j > 0 && cc.kk == 0) {
+                // the previous slice finished a tile: convert and store it
+                // while the other group computes
+                TileCursor ec = {cc.tl - 1, 0, 0, 0, 0};
+                locate(ec);
+                epilogue(ec);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (Op::kScaled) load_scales(cc);
+            read_slice(j);
+            if constexpr (G0) issue();  // copies of slice j + 1
+            if constexpr (Op::kScaled) {
+                if constexpr (G0)
+                    wait_vmcnt<LOADS>();  // scales precede this half's copies
+                else
+                    wait_vmcnt<0>();
+            }
+            barrier_lds();
+            // ---- MFMA half
+            if (cc.kk == 0)
+                compute(std::true_type{});
+            else
+                compute(std::false_type{});
+            advance(cc);
+            // group 0's copies of slice j + 1 land before the stage is read
+            if constexpr (G0) wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+        }
+        // epilogue of the last tile, then the halves that keep barrier counts equal
+        TileCursor ec = {my_tiles - 1, 0, 0, 0, 0};
+        locate(ec);
+        epilogue(ec);
+        barrier_lds();
+        if constexpr (G0) __builtin_amdgcn_s_barrier();
+    };
+    if (grp == 0)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
+}
+
+}  // namespace tcm

@@ -1,5 +1,5 @@
 // Kernel instances and launcher for the float16 / bfloat16 TN product.
-#include "gemm_kernel.h"
+#include "gemm_pingpong.h"
 
 namespace tcm {
 
@@ -31,6 +31,12 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
 }
 
 template <class Op, typename TOut>
+static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((pingpong_gemm_kernel<Op, TOut>), dim3(grid), dim3(kPPThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <class Op, typename TOut>
 static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t st) {
     switch (v) {
     case V_T256x256: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 1, false>(a, grid, st);
@@ -40,6 +46,8 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_T256x256_K32S4: return launch_one<Op, TOut, 256, 256, 32, 4, 1, 2>(a, grid, st);
     case V_T256x256_K32S5: return launch_one<Op, TOut, 256, 256, 32, 5, 1, 2>(a, grid, st);
     case V_T256x256_SPLIT2: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 2>(a, grid, st);
+    case V_T256x256_SPLIT4: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 4>(a, grid, st);
+    case V_PP256: return launch_pp<Op, TOut>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

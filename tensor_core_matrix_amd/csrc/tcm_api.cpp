@@ -17,17 +17,21 @@ namespace tcm {
 
 VariantInfo variant_info(int32_t v) {
     switch (v) {
-    case V_T256x256: return {256, 256, 64, 2, 1, 2};
-    case V_T128x256: return {128, 256, 64, 2, 1, 2};
-    case V_T128x128: return {128, 128, 64, 2, 2, 2};
-    case V_T128x64: return {128, 64, 64, 2, 3, 2};
-    case V_T256x256_K32S4: return {256, 256, 32, 4, 1, 2};
-    case V_T256x256_K32S5: return {256, 256, 32, 5, 1, 2};
-    case V_T256x256_SPLIT2: return {256, 256, 64, 2, 1, 2};
-    case V_MX256x256: return {256, 256, 128, 2, 1, 1};
-    case V_MX128x128: return {128, 128, 128, 2, 1, 1};
+    case V_T256x256: return {256, 256, 64, 2, 1, 2, kThreads};
+    case V_T128x256: return {128, 256, 64, 2, 1, 2, kThreads};
+    case V_T128x128: return {128, 128, 64, 2, 2, 2, kThreads};
+    case V_T128x64: return {128, 64, 64, 2, 3, 2, kThreads};
+    case V_T256x256_K32S4: return {256, 256, 32, 4, 1, 2, kThreads};
+    case V_T256x256_K32S5: return {256, 256, 32, 5, 1, 2, kThreads};
+    case V_T256x256_SPLIT2: return {256, 256, 64, 2, 1, 2, kThreads};
+    case V_T256x256_SPLIT4: return {256, 256, 64, 2, 1, 2, kThreads};
+    case V_MX256x256: return {256, 256, 128, 2, 1, 1, kThreads};
+    case V_MX128x128: return {128, 128, 128, 2, 1, 1, kThreads};
+    case V_MX256x256_SPLIT2: return {256, 256, 128, 2, 1, 1, kThreads};
+    case V_PP256: return {256, 256, 64, 2, 1, 2, 512};
+    case V_MXPP256: return {256, 256, 128, 2, 1, 1, 512};
     }
-    return {0, 0, 0, 0, 0, 0};
+    return {0, 0, 0, 0, 0, 0, kThreads};
 }
 
 }  // namespace tcm
@@ -144,7 +148,7 @@ tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool mx, in
         plan->tile_n = vi.tile_n;
         plan->tile_k = vi.tile_k;
         plan->stages = vi.stages;
-        plan->threads = kThreads;
+        plan->threads = vi.threads;
         plan->stage_bytes = stage;
         plan->lds_bytes = stage * vi.stages;
         plan->grid = (int32_t)grid;

@@ -297,8 +297,8 @@ def test_repeat_runs_bitwise_identical():
 
 
 # ------------------------------------------------------ every kernel variant
-PLAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6]
-MX_VARIANTS = [10, 11]
+PLAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8]
+MX_VARIANTS = [10, 11, 12, 13]
 
 
 @pytest.fixture
