@@ -17,10 +17,10 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename TOut, bool WORDS>
+template <typename TOut, bool WORDS, int UNIT_K, int S>
 static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, WORDS>), dim3(grid), dim3(kPPThreads), 0,
-                       st, a);
+    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, UNIT_K, S, WORDS>), dim3(grid),
+                       dim3(kPPThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -30,7 +30,8 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_MX256x256: return launch_one<TOut, 256, 256, WORDS>(a, grid, st);
     case V_MX128x128: return launch_one<TOut, 128, 128, WORDS>(a, grid, st);
     case V_MX256x256_SPLIT2: return launch_one<TOut, 256, 256, WORDS, 2>(a, grid, st);
-    case V_MXPP256: return launch_pp<TOut, WORDS>(a, grid, st);
+    case V_MXPP256: return launch_pp<TOut, WORDS, 128, 2>(a, grid, st);
+    case V_MXPP256_K64S4: return launch_pp<TOut, WORDS, 64, 4>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

@@ -5,29 +5,32 @@
 // taking turns so that one group's epilogue hides under the other's MMAs,
 // and a producer that only issues loads.  On CDNA4 every wave of a kernel
 // gets the same register budget, so a producer-only wave cannot sit beside
-// waves holding a 256-register accumulator.  Here the two roles alternate
-// within each wave instead:
+// waves holding a large accumulator.  Here the roles alternate within each
+// wave instead:
 //
 //  * Group 0 (waves 0-3) owns output rows 0-127 of the tile, group 1 (waves
 //    4-7) rows 128-255; wave w of a group owns columns 64 (w % 4) .. +63.
-//    Each wave holds a 128 x 64 fp32 accumulator (128 registers) and all
-//    fragments of one K slice (96 registers).
-//  * Time is cut into half-periods separated by workgroup barriers.  In
-//    half 2j group 0 runs the MFMAs of slice j while group 1 reads its
-//    fragments of slice j from LDS; in half 2j+1 group 1 runs slice j while
-//    group 0 reads its fragments of slice j+1 and issues the copies of slice
-//    j+2.  A wave in its MFMA half issues nothing but MFMAs, so stalls of the
-//    copy and read instructions (full address FIFOs, LDS latency) fall on the
-//    other wave and the matrix core of each SIMD stays busy.
-//  * Two-stage LDS ring of 64-deep (bf16) / 128-deep (fp8) slices.  Stage
-//    j % 2 is read in halves 2j-1 (group 0) and 2j (group 1); the copies of
-//    slice j+2 into it are issued in half 2j+1 by group 0, which waits for
-//    them at the end of its next MFMA half, before anyone reads them.
+//    Each wave holds a 128 x 64 fp32 accumulator (128 registers) and the
+//    fragments of one K unit.
+//  * K is walked in units of UNIT_K.  Time is cut into half-periods separated
+//    by workgroup barriers: in half 2u group 0 runs the MFMAs of unit u while
+//    group 1 reads its fragments of unit u from LDS; in half 2u+1 group 1 runs
+//    unit u while group 0 reads unit u+1.  A wave in its MFMA half issues
+//    nothing but MFMAs, so the stalls of reads and copies (LDS latency, full
+//    address FIFOs) fall on the other wave and the matrix core of each SIMD
+//    stays busy.
+//  * An S-stage LDS ring of units.  Unit v is read in halves 2v-1 and 2v, so
+//    its stage is free from half 2v+1 on; the copies of unit v+S into it are
+//    issued in the memory halves of unit v+1 (both groups sharing them when
+//    S >= 3, group 0 alone when S = 2) and waited for by their issuing waves
+//    just before the barrier that precedes the first read of unit v+S.  With
+//    S = 4 a copy has four half-periods to land and each memory half issues
+//    a quarter of what a two-stage ring would need in one.
 //  * The epilogue of a tile runs in each wave's memory half right after its
 //    last MFMA half -- while the other group computes -- staged through a
-//    wave-private LDS area so that every store writes whole 128-byte row
-//    segments.  This is the two-accumulator overlap of the pages, with the
-//    second accumulator set held by the other group's waves.
+//    wave-private LDS area so that every store writes whole row segments.
+//    This is the two-accumulator overlap of the pages, the second
+//    accumulator set being the other group's.
 #pragma once
 
 #include <type_traits>
@@ -38,31 +41,38 @@ namespace tcm {
 
 constexpr int kPPThreads = 512;  // eight waves
 
-template <class Op, typename TOut, bool SCALE_WORDS = false>
+template <class Op, typename TOut, int UNIT_K, int S, bool SCALE_WORDS = false>
 __global__ __launch_bounds__(kPPThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pingpong_gemm_kernel(GemmArgs p) {
-    constexpr int BM = 256, BN = 256, S = 2;
+    constexpr int BM = 256, BN = 256;
     constexpr int ESZ = Op::kElemBytes;
-    constexpr int BK = 128 / ESZ;  // 128-byte LDS rows: 64 bf16 / 128 fp8
-    constexpr int RB = 128;
-    constexpr int CPR = 8;
-    constexpr int SWZ = 1;  // chunk ^= (row / 2) % 8: 16 rows of a read group, 16 bank groups
+    constexpr int BK = UNIT_K;
+    constexpr int RB = BK * ESZ;        // bytes of one operand row's K unit
+    constexpr int CPR = RB / 16;        // 16-byte chunks per row
+    // chunk ^= row bits chosen so that the 16 rows read together by 16 lanes
+    // fall on 16 different 16-byte bank groups (64 banks of 4 bytes)
+    constexpr int SWZ = CPR == 8 ? 1 : 2;
     constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB, STAGE = A_BYTES + B_BYTES;
     constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32;
     constexpr int KSTEPS = BK / Op::kK;
     constexpr int CPL = Op::kK * ESZ / 32;
-    constexpr int N_FRAG = FM + FN;
-    // copies: group 0's four waves move a whole stage, 16 KiB each
-    constexpr int A_LOADS = A_BYTES / (4 * kWaveSize * 16);
-    constexpr int B_LOADS = B_BYTES / (4 * kWaveSize * 16);
-    constexpr int LOADS = A_LOADS + B_LOADS;
-    constexpr int ROWS_PER_WAVE_COPY = kWaveSize * 16 / RB;
+    // copies: 1 KiB per wave instruction; shared by both groups when S >= 3
+    constexpr int COPY_GROUPS = S >= 3 ? 2 : 1;
+    constexpr int NCW = 4 * COPY_GROUPS;               // copying waves
+    constexpr int A_COPIES = A_BYTES / 1024;
+    constexpr int PW = STAGE / 1024 / NCW;             // copies per wave per unit
+    constexpr int RPC = 1024 / RB;                     // rows per copy instruction
     // epilogue staging: 32 rows x 64 columns per wave (bf16 only)
     constexpr bool EPI_LDS = sizeof(TOut) == 2;
     constexpr int STG_ROWB = WTN * (int)sizeof(TOut);
     constexpr int STG_BYTES = EPI_LDS ? 32 * STG_ROWB : 0;
+    static_assert(CPR == 4 || CPR == 8, "64- or 128-byte rows");
+    static_assert(KSTEPS >= 1 && KSTEPS <= 4, "K steps per unit");
+    static_assert(!Op::kScaled || KSTEPS <= 2, "scale bytes per register");
+    static_assert((STAGE / 1024) % NCW == 0, "copy split");
     static_assert(S * STAGE + 8 * STG_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(LOADS < 64, "vmcnt range");
+    static_assert(S * PW < 64, "vmcnt range");
+    static_assert((32 >> SWZ) % CPR == 0, "swizzle depends on the row within 32 only");
 
     __shared__ __attribute__((aligned(1024))) char lds[S * STAGE + 8 * STG_BYTES];
 
@@ -76,7 +86,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
     const int lid = logical_block(blockIdx.x, G);
     if (lid >= p.total_tiles) return;
     const int my_tiles = (p.total_tiles - 1 - lid) / G + 1;
-    const int T = my_tiles * p.ksteps;  // slices of this workgroup
+    const int T = my_tiles * p.ksteps;  // K units of this workgroup
     const int K = p.K;
 
     auto locate = [&](TileCursor& c) { tile_coords(p, c.tl * G + lid, c.batch, c.tm, c.tn); };
@@ -87,12 +97,27 @@ void pingpong_gemm_kernel(GemmArgs p) {
         }
     };
 
-    // ---- copy stream (group 0 only) ------------------------------------------
-    const int cp_row = sub * ROWS_PER_WAVE_COPY + lane / CPR;
-    const int cp_chunk = (lane % CPR) ^ ((cp_row >> SWZ) & (CPR - 1));
-    const uint32_t cp_off = (uint32_t)cp_row * (uint32_t)K * ESZ + cp_chunk * 16;
-    const int cp_k = cp_chunk * (16 / ESZ);
-    const uint32_t cp_step = 4u * ROWS_PER_WAVE_COPY * (uint32_t)K * ESZ;
+    // ---- copy stream: this wave's share of every unit --------------------------
+    // Copy t of this wave is instruction q = cw + t * NCW of the unit (cw =
+    // this wave's index among the copying waves): LDS bytes [1024 q, +1024)
+    // of the stage, i.e. rows RPC qq .. RPC qq + RPC - 1 of A (qq = q while
+    // q < A_COPIES) or of B (qq = q - A_COPIES).  The rows of one wave's
+    // copies are NCW RPC apart and the swizzle repeats every CPR << SWZ rows,
+    // so a lane's chunk is the same in all of them: one lane offset serves
+    // every copy, and each copy adds the wave-uniform row offset RPC qq K.
+    const int cw = COPY_GROUPS == 2 ? wave : sub;
+    static_assert((NCW * RPC) % (CPR << SWZ) == 0 && (A_COPIES * RPC) % (CPR << SWZ) == 0,
+                  "chunk independent of the copy");
+    const int cp_row = lane / CPR;
+    const int sw_row = cw * RPC + cp_row;  // congruent to every copied row of the lane
+    const int cp_chunk = (lane % CPR) ^ ((sw_row >> SWZ) & (CPR - 1));
+    const uint32_t cp_lane_off = (uint32_t)cp_row * (uint32_t)K * ESZ + cp_chunk * 16;
+    const int cp_k = cp_chunk * (16 / ESZ);  // first K element of the lane's chunk
+    auto copy_row_off = [&](int t) -> uint32_t {
+        const int q = cw + t * NCW;
+        const int qq = q < A_COPIES ? q : q - A_COPIES;
+        return (uint32_t)(qq * RPC) * (uint32_t)K * ESZ;
+    };
     TileCursor fc = {0, 0, 0, 0, 0};
     __amdgpu_buffer_rsrc_t ra, rb;
     auto feed_resources = [&]() {
@@ -103,20 +128,21 @@ void pingpong_gemm_kernel(GemmArgs p) {
         ra = make_rsrc(abase, (uint32_t)rows_a * (uint32_t)K * ESZ);
         rb = make_rsrc(bbase, (uint32_t)rows_b * (uint32_t)K * ESZ);
     };
-    int fg = 0;  // slice the copy stream is on
-    // Copies of slice fg into its stage; past the last slice every offset is
-    // out of range (no memory touched, the stage is never read again).
+    int fu = 0;  // unit the copy stream is on
+    // This wave's copies of unit fu into its stage.  Past the last unit every
+    // offset is out of range: nothing is read and a stage that is never read
+    // again receives zeros.
     auto issue = [&]() {
         const int k0 = fc.kk * BK;
-        const uint32_t off0 =
-            (fg < T && k0 + cp_k < K) ? cp_off + (uint32_t)k0 * ESZ : kOutOfRange;
-        char* sa = lds + (fg % S) * STAGE;
+        char* st = lds + (fu % S) * STAGE;
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i)
-            copy16_to_lds(ra, sa + (4 * i + sub) * 1024, off0 + i * cp_step);
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i)
-            copy16_to_lds(rb, sa + A_BYTES + (4 * i + sub) * 1024, off0 + i * cp_step);
+        for (int t = 0; t < PW; ++t) {
+            const int q = cw + t * NCW;
+            const uint32_t off = (fu < T && k0 + cp_k < K)
+                                     ? cp_lane_off + copy_row_off(t) + (uint32_t)k0 * ESZ
+                                     : kOutOfRange;
+            copy16_to_lds(q < A_COPIES ? ra : rb, st + q * 1024, off);
+        }
         if (++fc.kk == p.ksteps) {
             fc.kk = 0;
             if (++fc.tl < my_tiles) {
@@ -124,10 +150,10 @@ void pingpong_gemm_kernel(GemmArgs p) {
                 feed_resources();
             }
         }
-        ++fg;
+        ++fu;
     };
 
-    // ---- fragments of one slice ------------------------------------------------
+    // ---- fragments of one unit -------------------------------------------------
     const int xr = (l32 >> SWZ) & (CPR - 1);
     const uint32_t a_frag = (uint32_t)(grp * WTM + l32) * RB;
     const uint32_t b_frag = (uint32_t)A_BYTES + (uint32_t)(sub * WTN + l32) * RB;
@@ -146,8 +172,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
         }
         return f;
     };
-    auto read_slice = [&](int j) {
-        const char* st = lds + (j % S) * STAGE;
+    auto read_unit = [&](int u) {
+        const char* st = lds + (u % S) * STAGE;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
@@ -157,7 +183,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
         }
     };
 
-    // ---- MX scales of one slice -------------------------------------------------
+    // ---- MX scales of one unit: byte 2s of the register serves K step s ---------
     int sc_a[Op::kScaled ? FM : 1], sc_b[Op::kScaled ? FN : 1];
     auto load_scales = [&](const TileCursor& c) {
         if constexpr (Op::kScaled) {
@@ -173,20 +199,23 @@ void pingpong_gemm_kernel(GemmArgs p) {
                 const uint8_t* src = (const uint8_t*)(is_a ? p.SA : p.SB) + (int64_t)row * kblocks;
                 int v;
                 if constexpr (SCALE_WORDS) {
-                    uint32_t w = *(const uint32_t*)(src + kb0);
-                    v = (int)(w >> (8 * hi));
+                    // rows of K/32 bytes are whole words: the unit's bytes sit in one word
+                    uint32_t w = *(const uint32_t*)(src + (kb0 & ~3));
+                    v = (int)(w >> (8 * ((kb0 & 3) + hi)));
                 } else {
-                    int q0 = kb0 + hi, q2 = kb0 + 2 + hi;
-                    int b0 = q0 < kblocks ? src[q0] : 127;
-                    int b2 = q2 < kblocks ? src[q2] : 127;
-                    v = b0 | (b2 << 16);
+                    int q0 = kb0 + hi;
+                    v = q0 < kblocks ? src[q0] : 127;
+                    if constexpr (KSTEPS > 1) {
+                        int q2 = kb0 + 2 + hi;
+                        v |= (q2 < kblocks ? src[q2] : 127) << 16;
+                    }
                 }
                 if (is_a) sc_a[idx] = v; else sc_b[idx] = v;
             }
         }
     };
 
-    // ---- MFMAs of one slice -------------------------------------------------------
+    // ---- MFMAs of one unit --------------------------------------------------------
     f32x16_t acc[FM][FN];
     auto compute = [&](auto ZERO) {
 #pragma unroll
@@ -221,6 +250,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
         const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N;
         if constexpr (EPI_LDS) {
             if (full && (p.N * (int)sizeof(TOut)) % 16 == 0) {
+                // each 32-row block: MFMA layout -> staging -> whole row pieces
                 constexpr int CHK = STG_ROWB / 16;
                 constexpr int RPI = kWaveSize * 16 / STG_ROWB;
                 char* stg = lds + S * STAGE + wave * STG_BYTES;
@@ -273,31 +303,33 @@ void pingpong_gemm_kernel(GemmArgs p) {
         }
     };
 
-    // ---- prologue: slice 0 resident ----------------------------------------------
+    // ---- prologue: units 0 .. S-2 resident -------------------------------------------
     locate(fc);
     feed_resources();
-    if (grp == 0) {
-        issue();           // slice 0
+    const bool copier = COPY_GROUPS == 2 || grp == 0;
+    if (copier) {
+#pragma unroll
+        for (int u = 0; u < S - 1; ++u) issue();
         wait_vmcnt<0>();
     }
     barrier_lds();
 
     // ---- half-periods -------------------------------------------------------------
-    // Group 0 reads slice j (and issues the copies of slice j + 1) in half
-    // 2j - 1 and computes it in half 2j; group 1 reads slice j in half 2j and
-    // computes it in half 2j + 1.  Each group runs one plain loop
-    //     memory half (epilogue of a finished tile, fragments of slice j),
-    //     barrier, MFMA half (slice j), barrier
-    // with group 1 one half behind, so both execute 2T + 2 barriers.
+    // Group 0 reads unit u in half 2u-1 and computes it in half 2u; group 1
+    // reads it in half 2u and computes it in half 2u+1.  Each group runs one
+    // plain loop -- memory half, barrier, MFMA half, barrier -- group 1 one
+    // half behind, so both execute 2T + 2 barriers.  The memory half of unit
+    // u also issues this wave's copies of unit u + S - 1.
     auto run = [&](auto GROUP0) {
         constexpr bool G0 = decltype(GROUP0)::value;
+        constexpr bool COPIES = G0 || COPY_GROUPS == 2;
         TileCursor cc = {0, 0, 0, 0, 0};
         locate(cc);
-        if constexpr (!G0) __builtin_amdgcn_s_barrier();  // half -1: group 0 reads slice 0
-        for (int j = 0; j < T; ++j) {
+        if constexpr (!G0) __builtin_amdgcn_s_barrier();  // half -1: group 0 reads unit 0
+        for (int u = 0; u < T; ++u) {
             // ---- memory half
-            if (j > 0 && cc.kk == 0) {
-                // the previous slice finished a tile: convert and store it
+            if (u > 0 && cc.kk == 0) {
+                // the previous unit finished a tile: convert and store it
                 // while the other group computes
                 TileCursor ec = {cc.tl - 1, 0, 0, 0, 0};
                 locate(ec);
@@ -305,13 +337,16 @@ void pingpong_gemm_kernel(GemmArgs p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (Op::kScaled) load_scales(cc);
-            read_slice(j);
-            if constexpr (G0) issue();  // copies of slice j + 1
+            read_unit(u);
+            if constexpr (COPIES) issue();
+            // Waits before the barrier.  Scales (MX) precede this half's
+            // copies, and loads return in order, so vmcnt(PW) covers them.
+            // Group 1's older copies: the share of unit u + 1, which group 0
+            // reads in the next half, has (S - 2) * PW copies issued after it.
             if constexpr (Op::kScaled) {
-                if constexpr (G0)
-                    wait_vmcnt<LOADS>();  // scales precede this half's copies
-                else
-                    wait_vmcnt<0>();
+                wait_vmcnt<COPIES ? PW : 0>();
+            } else if constexpr (!G0 && COPY_GROUPS == 2) {
+                wait_vmcnt<(S - 2) * PW>();
             }
             barrier_lds();
             // ---- MFMA half
@@ -320,8 +355,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
             else
                 compute(std::false_type{});
             advance(cc);
-            // group 0's copies of slice j + 1 land before the stage is read
-            if constexpr (G0) wait_vmcnt<0>();
+            // group 0's share of unit u + 1 lands before its next memory half
+            if constexpr (G0) wait_vmcnt<(S - 2) * PW>();
             __builtin_amdgcn_s_barrier();
         }
         // epilogue of the last tile, then the halves that keep barrier counts equal

@@ -30,9 +30,10 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <class Op, typename TOut>
+template <class Op, typename TOut, int UNIT_K, int S>
 static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((pingpong_gemm_kernel<Op, TOut>), dim3(grid), dim3(kPPThreads), 0, st, a);
+    hipLaunchKernelGGL((pingpong_gemm_kernel<Op, TOut, UNIT_K, S>), dim3(grid), dim3(kPPThreads), 0,
+                       st, a);
     return hipGetLastError();
 }
 
@@ -47,7 +48,8 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_T256x256_K32S5: return launch_one<Op, TOut, 256, 256, 32, 5, 1, 2>(a, grid, st);
     case V_T256x256_SPLIT2: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 2>(a, grid, st);
     case V_T256x256_SPLIT4: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 4>(a, grid, st);
-    case V_PP256: return launch_pp<Op, TOut>(a, grid, st);
+    case V_PP256: return launch_pp<Op, TOut, 64, 2>(a, grid, st);
+    case V_PP256_K32S4: return launch_pp<Op, TOut, 32, 4>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

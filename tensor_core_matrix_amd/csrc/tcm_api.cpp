@@ -29,7 +29,9 @@ VariantInfo variant_info(int32_t v) {
     case V_MX128x128: return {128, 128, 128, 2, 1, 1, kThreads};
     case V_MX256x256_SPLIT2: return {256, 256, 128, 2, 1, 1, kThreads};
     case V_PP256: return {256, 256, 64, 2, 1, 2, 512};
+    case V_PP256_K32S4: return {256, 256, 32, 4, 1, 2, 512};
     case V_MXPP256: return {256, 256, 128, 2, 1, 1, 512};
+    case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 1, 512};
     }
     return {0, 0, 0, 0, 0, 0, kThreads};
 }
@@ -116,6 +118,16 @@ int32_t forced_variant() {
     return e && *e ? (int32_t)atoi(e) : (int32_t)-1;
 }
 
+// TCM_MAX_GRID=<n> (read at every call) caps the number of persistent
+// workgroups, so that small problems also run several tiles per workgroup
+// (tests of the tile hand-over); unset or not positive, the grid is
+// min(tiles, CUs x occupancy).
+int64_t max_grid() {
+    const char* e = getenv("TCM_MAX_GRID");
+    const long long g = e && *e ? atoll(e) : 0;
+    return g > 0 ? (int64_t)g : INT64_MAX;
+}
+
 // Tile choice: the largest tile whose tile count still gives every CU at
 // least one tile with little padding; small problems take the smallest tile.
 int32_t choose_variant(int64_t batch, int64_t M, int64_t N, bool mx, int cus) {
@@ -142,6 +154,8 @@ tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool mx, in
     int64_t tiles = batch * tm * tn;
     int64_t slots = int64_t(cus) * vi.occupancy;
     int64_t grid = tiles < slots ? tiles : slots;
+    const int64_t cap = max_grid();
+    if (grid > cap) grid = cap;
     int32_t stage = (vi.tile_m + vi.tile_n) * vi.tile_k * vi.elem_bytes;
     if (plan) {
         plan->tile_m = vi.tile_m;

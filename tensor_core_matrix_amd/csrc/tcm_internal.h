@@ -37,11 +37,13 @@ enum Variant : int32_t {
     V_T256x256_K32S5 = 5,  // 256x256x32, 5-stage ring (all 160 KiB of LDS)
     V_T256x256_SPLIT2 = 6, // 256x256x64, 2-stage ring, copies split over 2 K steps
     V_T256x256_SPLIT4 = 7, // 256x256x64, 2-stage ring, copies split over 4 K steps
-    V_PP256 = 8,           // 256x256x64, eight waves taking turns (ping-pong)
+    V_PP256 = 8,           // 256x256x64, eight waves taking turns (ping-pong), 2-stage ring
+    V_PP256_K32S4 = 9,     // 256x256x32 ping-pong, 4-stage ring, copies shared by all waves
     V_MX256x256 = 10, // MXFP8 256x256x128, 2-stage ring
     V_MX128x128 = 11, // MXFP8 128x128x128, 2-stage ring
     V_MX256x256_SPLIT2 = 12, // MXFP8 256x256x128, copies split over 2 K steps
     V_MXPP256 = 13,          // MXFP8 256x256x128, eight waves taking turns (ping-pong)
+    V_MXPP256_K64S4 = 14,    // MXFP8 256x256x64 ping-pong, 4-stage ring
 };
 
 struct VariantInfo {

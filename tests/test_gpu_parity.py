@@ -297,14 +297,18 @@ def test_repeat_runs_bitwise_identical():
 
 
 # ------------------------------------------------------ every kernel variant
-PLAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8]
-MX_VARIANTS = [10, 11, 12, 13]
+PLAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9]
+MX_VARIANTS = [10, 11, 12, 13, 14]
 
 
 @pytest.fixture
 def force_variant(monkeypatch):
-    def _set(v):
+    def _set(v, max_grid=None):
         monkeypatch.setenv("TCM_FORCE_VARIANT", str(v))
+        if max_grid is None:
+            monkeypatch.delenv("TCM_MAX_GRID", raising=False)
+        else:
+            monkeypatch.setenv("TCM_MAX_GRID", str(max_grid))
     return _set
 
 
@@ -324,6 +328,11 @@ def test_each_plain_variant(v, force_variant):
     r = inp.quarter_integers((384, 512), g, torch.float16)
     qref, _ = orc.gemm_tn(orc.F16, inp.raw(q), inp.raw(r))
     assert np.array_equal(_np(run_plain(q, r, "f32")), qref)
+    # three persistent workgroups: every workgroup walks several tiles, the
+    # last of them ragged in M and N
+    force_variant(v, max_grid=3)
+    for odt in ("f32", "bf16"):
+        assert_parity(run_plain(a, b, odt), ref, s, odt, f"variant {v} {odt} grid 3")
 
 
 @pytest.mark.parametrize("v", MX_VARIANTS)
@@ -338,6 +347,17 @@ def test_each_mx_variant(v, force_variant):
     ref, s = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb))
     for odt in ("f32", "bf16"):
         assert_parity(run_mx(a, b, sa, sb, odt), ref, s, odt, f"mx variant {v} {odt}")
+    # K = 19 scale blocks (byte-wise scale reads, a 32-deep K tail) and three
+    # persistent workgroups walking several tiles each
+    K2 = 608
+    a2 = inp.e4m3_normal((M, K2), g)
+    b2 = inp.e4m3_normal((N, K2), g)
+    sa2 = inp.e8m0_scales((M, K2 // 32), g)
+    sb2 = inp.e8m0_scales((N, K2 // 32), g)
+    ref2, s2 = orc.gemm_mx(inp.raw(a2), inp.raw(b2), inp.raw(sa2), inp.raw(sb2))
+    force_variant(v, max_grid=3)
+    for odt in ("f32", "bf16"):
+        assert_parity(run_mx(a2, b2, sa2, sb2, odt), ref2, s2, odt, f"mx variant {v} {odt} K {K2}")
 
 
 def test_batched_workload_through_large_tiles(force_variant):
