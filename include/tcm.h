@@ -118,7 +118,9 @@ typedef struct tcm_plan {
     int32_t stages;                 /* depth of the LDS operand ring */
     int32_t threads;                /* threads per workgroup */
     int32_t stage_bytes;            /* LDS bytes of one stage (A tile + B tile) */
-    int32_t lds_bytes;              /* LDS bytes per workgroup */
+    int32_t lds_bytes;              /* LDS bytes of the operand ring (stages x stage_bytes);
+                                       output staging and MX scale buffers add to it, within
+                                       the 160 KiB of a compute unit */
     int32_t grid;                   /* workgroups launched (persistent when < tiles) */
     int64_t tiles;                  /* output tiles over all problems */
     int32_t kernel;                 /* internal kernel variant id */

@@ -329,6 +329,7 @@ void tiled_gemm_kernel(GemmArgs p) {
                                          a4[4 * q + 3]);
                         }
                     // same-wave LDS writes then reads: the wave's own order holds
+                    wave_lds_exchange();
 #pragma unroll
                     for (int t = 0; t < 32 / RPI; ++t) {
                         const int r = t * RPI + lane / CHK;
@@ -339,6 +340,7 @@ void tiled_gemm_kernel(GemmArgs p) {
                                         c.tn * BN + wn * WTN) * (int64_t)sizeof(TOut) + ck * 16;
                         *(i32x4_t*)g = d;
                     }
+                    wave_lds_exchange();
                 }
                 return;
             }

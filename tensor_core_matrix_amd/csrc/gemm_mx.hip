@@ -17,32 +17,41 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename TOut, bool WORDS, int UNIT_K, int S>
+template <typename TOut, int MODE, int UNIT_K, int S>
 static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, UNIT_K, S, WORDS>), dim3(grid),
+    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, UNIT_K, S, MODE>), dim3(grid),
                        dim3(kPPThreads), 0, st, a);
     return hipGetLastError();
 }
 
-template <typename TOut, bool WORDS>
+// MODE: 0 scale rows read byte by byte, 1 as 32-bit words, 2 as 16-byte pieces
+// (the tiled kernels read words in modes 1 and 2).
+template <typename TOut, int MODE>
 static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t st) {
+    constexpr bool WORDS = MODE >= 1;
     switch (v) {
     case V_MX256x256: return launch_one<TOut, 256, 256, WORDS>(a, grid, st);
     case V_MX128x128: return launch_one<TOut, 128, 128, WORDS>(a, grid, st);
     case V_MX256x256_SPLIT2: return launch_one<TOut, 256, 256, WORDS, 2>(a, grid, st);
-    case V_MXPP256: return launch_pp<TOut, WORDS, 128, 2>(a, grid, st);
-    case V_MXPP256_K64S4: return launch_pp<TOut, WORDS, 64, 4>(a, grid, st);
+    case V_MXPP256: return launch_pp<TOut, MODE, 128, 2>(a, grid, st);
+    case V_MXPP256_K64S4: return launch_pp<TOut, MODE, 64, 4>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_mx(int32_t v, int32_t out_dtype, bool scale_words, const GemmArgs& a,
+template <typename TOut>
+static hipError_t by_mode(int32_t v, int32_t mode, const GemmArgs& a, int grid, hipStream_t st) {
+    switch (mode) {
+    case 2: return by_variant<TOut, 2>(v, a, grid, st);
+    case 1: return by_variant<TOut, 1>(v, a, grid, st);
+    default: return by_variant<TOut, 0>(v, a, grid, st);
+    }
+}
+
+hipError_t launch_gemm_mx(int32_t v, int32_t out_dtype, int32_t scale_mode, const GemmArgs& a,
                           int grid, hipStream_t st) {
-    if (out_dtype == 1)
-        return scale_words ? by_variant<__bf16, true>(v, a, grid, st)
-                           : by_variant<__bf16, false>(v, a, grid, st);
-    return scale_words ? by_variant<float, true>(v, a, grid, st)
-                       : by_variant<float, false>(v, a, grid, st);
+    if (out_dtype == 1) return by_mode<__bf16>(v, scale_mode, a, grid, st);
+    return by_mode<float>(v, scale_mode, a, grid, st);
 }
 
 }  // namespace tcm

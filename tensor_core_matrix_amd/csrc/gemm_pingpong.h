@@ -41,7 +41,10 @@ namespace tcm {
 
 constexpr int kPPThreads = 512;  // eight waves
 
-template <class Op, typename TOut, int UNIT_K, int S, bool SCALE_WORDS = false>
+// SCALE_MODE (MX only) says how the E8M0 rows may be read: 0 byte by byte,
+// 1 as 32-bit words (K a multiple of 128, word-aligned arrays), 2 as 16-byte
+// pieces (K a multiple of 512, 16-byte-aligned arrays).
+template <class Op, typename TOut, int UNIT_K, int S, int SCALE_MODE = 0>
 __global__ __launch_bounds__(kPPThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256;
@@ -52,7 +55,22 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // chunk ^= row bits chosen so that the 16 rows read together by 16 lanes
     // fall on 16 different 16-byte bank groups (64 banks of 4 bytes)
     constexpr int SWZ = CPR == 8 ? 1 : 2;
-    constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB, STAGE = A_BYTES + B_BYTES;
+    constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB, DATA = A_BYTES + B_BYTES;
+    // MX scales reach the MFMA waves through LDS, copied by the same DMA as
+    // the operands, so that no wave waits on a global load.  With 16-byte
+    // pieces (SC_CHUNK) one DMA per wave brings 16 blocks of 64 rows, the
+    // scales of UPC units, into one of two chunk buffers after the ring;
+    // with 32-bit words (SC_LDS) every stage ends with one word per A and B
+    // row, the 4 blocks that hold the unit's blocks.  A DMA lane touches one
+    // row, so fewer, wider pieces keep the address unit free for operands.
+    constexpr bool SCALE_WORDS = SCALE_MODE >= 1;
+    constexpr bool SC_CHUNK = Op::kScaled && SCALE_MODE == 2 && S >= 3;
+    constexpr bool SC_LDS = Op::kScaled && SCALE_MODE == 1 && S >= 3;
+    constexpr int SC_BYTES = SC_LDS ? (BM + BN) * 4 : 0;
+    constexpr int STAGE = DATA + SC_BYTES;
+    constexpr int UPC = 16 / (BK / 32);                       // units per scale chunk
+    constexpr int CHUNK_BYTES = (BM + BN) * 16;
+    constexpr int SC_CHUNK_TOTAL = SC_CHUNK ? 2 * CHUNK_BYTES : 0;
     constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32;
     constexpr int KSTEPS = BK / Op::kK;
     constexpr int CPL = Op::kK * ESZ / 32;
@@ -60,21 +78,29 @@ void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int COPY_GROUPS = S >= 3 ? 2 : 1;
     constexpr int NCW = 4 * COPY_GROUPS;               // copying waves
     constexpr int A_COPIES = A_BYTES / 1024;
-    constexpr int PW = STAGE / 1024 / NCW;             // copies per wave per unit
+    constexpr int PW = DATA / 1024 / NCW;              // operand copies per wave per unit
+    constexpr int OPS = PW + (SC_LDS ? 1 : 0);         // DMA operations per wave per unit
     constexpr int RPC = 1024 / RB;                     // rows per copy instruction
-    // epilogue staging: 32 rows x 64 columns per wave (bf16 only)
+    // epilogue staging: 32 (or, where the ring leaves less room, 16) rows x
+    // 64 columns per wave (bf16 only)
     constexpr bool EPI_LDS = sizeof(TOut) == 2;
     constexpr int STG_ROWB = WTN * (int)sizeof(TOut);
-    constexpr int STG_BYTES = EPI_LDS ? 32 * STG_ROWB : 0;
+    constexpr int RING = S * STAGE + SC_CHUNK_TOTAL;
+    constexpr int STG_ROWS = RING + 8 * 32 * STG_ROWB <= 160 * 1024 ? 32 : 16;
+    constexpr int STG_BYTES = EPI_LDS ? STG_ROWS * STG_ROWB : 0;
     static_assert(CPR == 4 || CPR == 8, "64- or 128-byte rows");
     static_assert(KSTEPS >= 1 && KSTEPS <= 4, "K steps per unit");
     static_assert(!Op::kScaled || KSTEPS <= 2, "scale bytes per register");
-    static_assert((STAGE / 1024) % NCW == 0, "copy split");
-    static_assert(S * STAGE + 8 * STG_BYTES <= 160 * 1024, "LDS budget");
-    static_assert(S * PW < 64, "vmcnt range");
+    static_assert((DATA / 1024) % NCW == 0, "copy split");
+    static_assert(STAGE % 1024 == 0, "stage alignment");
+    static_assert(RING + 8 * STG_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(S * OPS < 64, "vmcnt range");
+    static_assert(!(SC_LDS || SC_CHUNK) || NCW == 8,
+                  "one scale DMA per wave: 4 x 64 A rows, 4 x 64 B rows");
+    static_assert(!SC_CHUNK || UPC >= 2, "a chunk lands two halves after its DMA");
     static_assert((32 >> SWZ) % CPR == 0, "swizzle depends on the row within 32 only");
 
-    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE + 8 * STG_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds[RING + 8 * STG_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -119,7 +145,9 @@ void pingpong_gemm_kernel(GemmArgs p) {
         return (uint32_t)(qq * RPC) * (uint32_t)K * ESZ;
     };
     TileCursor fc = {0, 0, 0, 0, 0};
-    __amdgpu_buffer_rsrc_t ra, rb;
+    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+    const int kblocks = K / 32;
+    const uint32_t sc_lane_off = (uint32_t)((wave & 3) * 64 + lane) * (uint32_t)kblocks;
     auto feed_resources = [&]() {
         const int rows_a = min(BM, p.M - fc.tm * BM);
         const int rows_b = min(BN, p.N - fc.tn * BN);
@@ -127,6 +155,40 @@ void pingpong_gemm_kernel(GemmArgs p) {
         const char* bbase = (const char*)p.B + fc.batch * p.stride_b + (int64_t)fc.tn * BN * K * ESZ;
         ra = make_rsrc(abase, (uint32_t)rows_a * (uint32_t)K * ESZ);
         rb = make_rsrc(bbase, (uint32_t)rows_b * (uint32_t)K * ESZ);
+        if constexpr (SC_LDS) {
+            const uint8_t* sab = (const uint8_t*)p.SA + (int64_t)fc.tm * BM * kblocks;
+            const uint8_t* sbb = (const uint8_t*)p.SB + (int64_t)fc.tn * BN * kblocks;
+            rsa = make_rsrc(sab, (uint32_t)rows_a * (uint32_t)kblocks);
+            rsb = make_rsrc(sbb, (uint32_t)rows_b * (uint32_t)kblocks);
+        }
+    };
+    // scale chunks: cursor on the first unit of the next chunk to copy
+    TileCursor scc = {0, 0, 0, 0, 0};
+    __amdgpu_buffer_rsrc_t rca, rcb;
+    auto chunk_resources = [&]() {
+        const int rows_a = min(BM, p.M - scc.tm * BM);
+        const int rows_b = min(BN, p.N - scc.tn * BN);
+        rca = make_rsrc((const uint8_t*)p.SA + (int64_t)scc.tm * BM * kblocks,
+                        (uint32_t)rows_a * (uint32_t)kblocks);
+        rcb = make_rsrc((const uint8_t*)p.SB + (int64_t)scc.tn * BN * kblocks,
+                        (uint32_t)rows_b * (uint32_t)kblocks);
+    };
+    int cu = 0;  // first unit of the chunk the scale stream is on
+    // wave w copies 16 blocks of A rows 64 w .. (w < 4) or of B rows 64 (w - 4) ..
+    auto issue_chunk = [&]() {
+        const uint32_t off = cu < T ? sc_lane_off + (uint32_t)(scc.kk * (BK / 32)) : kOutOfRange;
+        copy16_to_lds(wave < 4 ? rca : rcb, lds + S * STAGE + ((cu / UPC) & 1) * CHUNK_BYTES +
+                                                wave * 1024,
+                      off);
+        cu += UPC;
+        scc.kk += UPC;
+        if (scc.kk >= p.ksteps) {
+            scc.kk = 0;
+            if (++scc.tl < my_tiles) {
+                locate(scc);
+                chunk_resources();
+            }
+        }
     };
     int fu = 0;  // unit the copy stream is on
     // This wave's copies of unit fu into its stage.  Past the last unit every
@@ -142,6 +204,13 @@ void pingpong_gemm_kernel(GemmArgs p) {
                                      ? cp_lane_off + copy_row_off(t) + (uint32_t)k0 * ESZ
                                      : kOutOfRange;
             copy16_to_lds(q < A_COPIES ? ra : rb, st + q * 1024, off);
+        }
+        if constexpr (SC_LDS) {
+            // wave w copies the words of A rows 64 w .. (w < 4) or of B rows
+            // 64 (w - 4) ..; rows past M or N read as zero
+            const uint32_t word = (uint32_t)(fc.kk * (BK / 32)) & ~3u;
+            const uint32_t off = fu < T ? sc_lane_off + word : kOutOfRange;
+            copy4_to_lds(wave < 4 ? rsa : rsb, st + DATA + wave * 256, off);
         }
         if (++fc.kk == p.ksteps) {
             fc.kk = 0;
@@ -185,9 +254,33 @@ void pingpong_gemm_kernel(GemmArgs p) {
 
     // ---- MX scales of one unit: byte 2s of the register serves K step s ---------
     int sc_a[Op::kScaled ? FM : 1], sc_b[Op::kScaled ? FN : 1];
-    auto load_scales = [&](const TileCursor& c) {
-        if constexpr (Op::kScaled) {
-            const int kblocks = K / 32;
+    auto load_scales = [&](const TileCursor& c, int u) {
+        if constexpr (SC_CHUNK) {
+            // the unit's blocks: bytes b (+ 2) + hi of the row's 16, b = its
+            // first block within the chunk
+            const int b = (c.kk * (BK / 32)) & 15;
+            const char* sc = lds + S * STAGE + ((u / UPC) & 1) * CHUNK_BYTES + (b & ~3);
+            const int sh = 8 * ((b & 3) + hi);
+#pragma unroll
+            for (int f = 0; f < FM + FN; ++f) {
+                const bool is_a = f < FM;
+                const int idx = is_a ? f : f - FM;
+                const int row = (is_a ? grp * WTM : BM + sub * WTN) + idx * 32 + l32;
+                const int v = (int)(*(const uint32_t*)(sc + row * 16) >> sh);
+                if (is_a) sc_a[idx] = v; else sc_b[idx] = v;
+            }
+        } else if constexpr (SC_LDS) {
+            const char* sc = lds + (u % S) * STAGE + DATA;
+            const int sh = 8 * (((c.kk * (BK / 32)) & 3) + hi);
+#pragma unroll
+            for (int f = 0; f < FM + FN; ++f) {
+                const bool is_a = f < FM;
+                const int idx = is_a ? f : f - FM;
+                const int row = (is_a ? grp * WTM : BM + sub * WTN) + idx * 32 + l32;
+                const int v = (int)(*(const uint32_t*)(sc + row * 4) >> sh);
+                if (is_a) sc_a[idx] = v; else sc_b[idx] = v;
+            }
+        } else if constexpr (Op::kScaled) {
             const int kb0 = c.kk * (BK / 32);
 #pragma unroll
             for (int f = 0; f < FM + FN; ++f) {
@@ -250,31 +343,43 @@ void pingpong_gemm_kernel(GemmArgs p) {
         const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N;
         if constexpr (EPI_LDS) {
             if (full && (p.N * (int)sizeof(TOut)) % 16 == 0) {
-                // each 32-row block: MFMA layout -> staging -> whole row pieces
+                // each block of STG_ROWS rows: MFMA layout -> staging ->
+                // whole row pieces (lane l holds row l % 32 of a 32-row block)
                 constexpr int CHK = STG_ROWB / 16;
                 constexpr int RPI = kWaveSize * 16 / STG_ROWB;
-                char* stg = lds + S * STAGE + wave * STG_BYTES;
+                char* stg = lds + RING + wave * STG_BYTES;
+                const int srow = l32 % STG_ROWS;
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
 #pragma unroll
-                    for (int j = 0; j < FN; ++j)
+                    for (int h = 0; h < 32 / STG_ROWS; ++h) {
+                        if (STG_ROWS == 32 || l32 / STG_ROWS == h) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const f32x16_t& a4 = acc[i][j];
-                            const int byte = (j * 32 + 8 * q + 4 * hi) * (int)sizeof(TOut);
-                            const int chunk = (byte / 16) ^ (l32 & (CHK - 1));
-                            store4<TOut>((TOut*)(stg + l32 * STG_ROWB + chunk * 16 + byte % 16),
-                                         a4[4 * q], a4[4 * q + 1], a4[4 * q + 2], a4[4 * q + 3]);
+                            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const f32x16_t& a4 = acc[i][j];
+                                    const int byte = (j * 32 + 8 * q + 4 * hi) * (int)sizeof(TOut);
+                                    const int chunk = (byte / 16) ^ (srow & (CHK - 1));
+                                    store4<TOut>(
+                                        (TOut*)(stg + srow * STG_ROWB + chunk * 16 + byte % 16),
+                                        a4[4 * q], a4[4 * q + 1], a4[4 * q + 2], a4[4 * q + 3]);
+                                }
                         }
+                        wave_lds_exchange();
 #pragma unroll
-                    for (int t = 0; t < 32 / RPI; ++t) {
-                        const int r = t * RPI + lane / CHK;
-                        const int ck = lane % CHK;
-                        const i32x4_t d =
-                            *(const i32x4_t*)(stg + r * STG_ROWB + ((ck ^ (r & (CHK - 1))) * 16));
-                        char* g = Cb + ((int64_t)(row0 + i * 32 + r) * p.N + col0) *
-                                           (int64_t)sizeof(TOut) + ck * 16;
-                        *(i32x4_t*)g = d;
+                        for (int t = 0; t < STG_ROWS / RPI; ++t) {
+                            const int r = t * RPI + lane / CHK;
+                            const int ck = lane % CHK;
+                            const i32x4_t d = *(const i32x4_t*)(stg + r * STG_ROWB +
+                                                                ((ck ^ (r & (CHK - 1))) * 16));
+                            char* g = Cb +
+                                      ((int64_t)(row0 + i * 32 + h * STG_ROWS + r) * p.N + col0) *
+                                          (int64_t)sizeof(TOut) +
+                                      ck * 16;
+                            *(i32x4_t*)g = d;
+                        }
+                        wave_lds_exchange();
                     }
                 }
                 return;
@@ -306,6 +411,11 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // ---- prologue: units 0 .. S-2 resident -------------------------------------------
     locate(fc);
     feed_resources();
+    if constexpr (SC_CHUNK) {
+        locate(scc);
+        chunk_resources();
+        issue_chunk();  // chunk 0; chunk c + 1 follows in the memory halves of unit UPC c
+    }
     const bool copier = COPY_GROUPS == 2 || grp == 0;
     if (copier) {
 #pragma unroll
@@ -336,17 +446,23 @@ void pingpong_gemm_kernel(GemmArgs p) {
                 epilogue(ec);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (Op::kScaled) load_scales(cc);
+            if constexpr (Op::kScaled) load_scales(cc, u);
             read_unit(u);
+            if constexpr (SC_CHUNK) {
+                // the other buffer held the chunk before this one, which both
+                // groups finished reading in earlier halves
+                if (u == cu - UPC) issue_chunk();
+            }
             if constexpr (COPIES) issue();
-            // Waits before the barrier.  Scales (MX) precede this half's
-            // copies, and loads return in order, so vmcnt(PW) covers them.
-            // Group 1's older copies: the share of unit u + 1, which group 0
-            // reads in the next half, has (S - 2) * PW copies issued after it.
-            if constexpr (Op::kScaled) {
-                wait_vmcnt<COPIES ? PW : 0>();
+            // Waits before the barrier.  Scales loaded to registers precede
+            // this half's copies, and loads return in order, so vmcnt(OPS)
+            // covers them.  Group 1's older copies: the share of unit u + 1,
+            // which group 0 reads in the next half, has (S - 2) * OPS
+            // operations issued after it.
+            if constexpr (Op::kScaled && !SC_LDS && !SC_CHUNK) {
+                wait_vmcnt<COPIES ? OPS : 0>();
             } else if constexpr (!G0 && COPY_GROUPS == 2) {
-                wait_vmcnt<(S - 2) * PW>();
+                wait_vmcnt<(S - 2) * OPS>();
             }
             barrier_lds();
             // ---- MFMA half
@@ -356,7 +472,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
                 compute(std::false_type{});
             advance(cc);
             // group 0's share of unit u + 1 lands before its next memory half
-            if constexpr (G0) wait_vmcnt<(S - 2) * PW>();
+            if constexpr (G0) wait_vmcnt<(S - 2) * OPS>();
             __builtin_amdgcn_s_barrier();
         }
         // epilogue of the last tile, then the halves that keep barrier counts equal

@@ -134,7 +134,7 @@ int32_t choose_variant(int64_t batch, int64_t M, int64_t N, bool mx, int cus) {
     const int32_t f = forced_variant();
     if (f >= 0 && variant_info(f).tile_m > 0 && (f >= V_MX256x256) == mx) return f;
     static const int32_t plain[] = {V_T256x256_SPLIT2, V_T128x256, V_T128x128, V_T128x64};
-    static const int32_t mxv[] = {V_MX256x256, V_MX128x128};
+    static const int32_t mxv[] = {V_MXPP256_K64S4, V_MX128x128};
     const int32_t* cand = mx ? mxv : plain;
     const int n = mx ? 2 : 4;
     for (int i = 0; i < n; ++i) {
@@ -256,10 +256,15 @@ tcm_status tcm_gemm_mx_fp8(const void* A, const void* B, const void* scale_A, co
     a.stride_a = M * K;
     a.stride_b = N * K;
     a.stride_c = M * N * elem_bytes(out_dtype);
-    // 32-bit scale reads need every row's K/32 bytes to be whole words.
-    const bool words = K > 0 && K % 128 == 0 && (reinterpret_cast<uintptr_t>(scale_A) & 3u) == 0 &&
-                       (reinterpret_cast<uintptr_t>(scale_B) & 3u) == 0;
-    hipError_t e = launch_gemm_mx(plan.kernel, (int32_t)out_dtype, words, a, plan.grid,
+    // Wide scale reads need every row's K/32 bytes to be whole words (16-byte
+    // pieces) and the arrays aligned to match.
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(scale_A), sb = reinterpret_cast<uintptr_t>(scale_B);
+    int32_t scale_mode = 0;
+    if (K > 0 && K % 512 == 0 && ((sa | sb) & 15u) == 0)
+        scale_mode = 2;
+    else if (K > 0 && K % 128 == 0 && ((sa | sb) & 3u) == 0)
+        scale_mode = 1;
+    hipError_t e = launch_gemm_mx(plan.kernel, (int32_t)out_dtype, scale_mode, a, plan.grid,
                                   (hipStream_t)stream);
     return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
 }

@@ -40,6 +40,13 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCM_LDS_PTR(lds_wave_base), 16, voffset, 0, 0, 0);
 }
 
+// 4 bytes per lane from the buffer into LDS: the wave fills 256 bytes
+// contiguously from `lds_wave_base` (lane l writes bytes [4 l, 4 l + 4)).
+__device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base,
+                                             uint32_t voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCM_LDS_PTR(lds_wave_base), 4, voffset, 0, 0, 0);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -53,6 +60,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Lanes of one wave exchanging data through LDS.  The hardware runs a wave's
+// LDS operations in issue order, so no wait is needed between a lane's write
+// and another lane's read; but the compiler reasons lane by lane and may move
+// or forward a load across such a write (it sank the read-back of a staging
+// area into a branch taken by only the writing lanes).  This compiler-only
+// fence keeps every memory access on its side.
+__device__ __forceinline__ void wave_lds_exchange() { asm volatile("" ::: "memory"); }
 
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }

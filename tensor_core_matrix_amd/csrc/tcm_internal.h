@@ -57,7 +57,9 @@ VariantInfo variant_info(int32_t v);
 // Launchers (one per translation unit).  dtype codes follow tcm_dtype.
 hipError_t launch_gemm_tn(int32_t variant, int32_t in_dtype, int32_t out_dtype, const GemmArgs& a,
                           int grid, hipStream_t stream);
-hipError_t launch_gemm_mx(int32_t variant, int32_t out_dtype, bool scale_words, const GemmArgs& a,
+// scale_mode: how E8M0 rows may be read -- 0 bytes, 1 32-bit words (K % 128 == 0,
+// word-aligned arrays), 2 16-byte pieces (K % 512 == 0, 16-byte-aligned arrays).
+hipError_t launch_gemm_mx(int32_t variant, int32_t out_dtype, int32_t scale_mode, const GemmArgs& a,
                           int grid, hipStream_t stream);
 
 }  // namespace tcm

@@ -114,8 +114,10 @@ def test_plans_of_the_workloads():
     p = tcm.plan(8192, 8192, 8192)
     assert (p["tile_m"], p["tile_n"], p["grid"], p["tiles"]) == (256, 256, 256, 1024)
     assert p["lds_bytes"] <= 160 * 1024
-    # MXFP8 8192^3: 256 x 256 tiles, 128-deep slices (64 KiB per stage)
+    # MXFP8 8192^3: 256 x 256 tiles, eight waves taking turns, a ring of four
+    # 64-deep units (32 KiB each)
     p = tcm.plan(8192, 8192, 8192, mx=True)
-    assert (p["tile_m"], p["tile_k"], p["stage_bytes"]) == (256, 128, 64 * 1024)
+    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"]) == \
+        (256, 64, 32 * 1024, 4, 512)
     # empty problem plans nothing
     assert tcm.plan(0, 8, 8)["grid"] == 0

@@ -358,6 +358,16 @@ def test_each_mx_variant(v, force_variant):
     force_variant(v, max_grid=3)
     for odt in ("f32", "bf16"):
         assert_parity(run_mx(a2, b2, sa2, sb2, odt), ref2, s2, odt, f"mx variant {v} {odt} K {K2}")
+    # K = 1536: scale rows of 48 bytes, read as 16-byte pieces; three chunks
+    # of 512 K per tile, several tiles per workgroup
+    K3 = 1536
+    a3 = inp.e4m3_normal((M, K3), g)
+    b3 = inp.e4m3_normal((N, K3), g)
+    sa3 = inp.e8m0_scales((M, K3 // 32), g)
+    sb3 = inp.e8m0_scales((N, K3 // 32), g)
+    ref3, s3 = orc.gemm_mx(inp.raw(a3), inp.raw(b3), inp.raw(sa3), inp.raw(sb3))
+    for odt in ("f32", "bf16"):
+        assert_parity(run_mx(a3, b3, sa3, sb3, odt), ref3, s3, odt, f"mx variant {v} {odt} K {K3}")
 
 
 def test_batched_workload_through_large_tiles(force_variant):
