@@ -97,7 +97,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
     static_assert(S * OPS < 64, "vmcnt range");
     static_assert(!(SC_LDS || SC_CHUNK) || NCW == 8,
                   "one scale DMA per wave: 4 x 64 A rows, 4 x 64 B rows");
-    static_assert(!SC_CHUNK || UPC >= 2, "a chunk lands two halves after its DMA");
+    static_assert(!SC_CHUNK || UPC == 8, "a chunk lands two halves after its DMA; 64-deep units");
     static_assert((32 >> SWZ) % CPR == 0, "swizzle depends on the row within 32 only");
 
     __shared__ __attribute__((aligned(1024))) char lds[RING + 8 * STG_BYTES];
@@ -254,20 +254,33 @@ void pingpong_gemm_kernel(GemmArgs p) {
 
     // ---- MX scales of one unit: byte 2s of the register serves K step s ---------
     int sc_a[Op::kScaled ? FM : 1], sc_b[Op::kScaled ? FN : 1];
+    // chunk mode: the 8 scale bytes a lane needs from its row's 16 (blocks
+    // 2 k + hi, k = unit within the chunk), byte k of a 64-bit value
+    uint64_t pk[SC_CHUNK ? FM + FN : 1];
     auto load_scales = [&](const TileCursor& c, int u) {
         if constexpr (SC_CHUNK) {
-            // the unit's blocks: bytes b (+ 2) + hi of the row's 16, b = its
-            // first block within the chunk
-            const int b = (c.kk * (BK / 32)) & 15;
-            const char* sc = lds + S * STAGE + ((u / UPC) & 1) * CHUNK_BYTES + (b & ~3);
-            const int sh = 8 * ((b & 3) + hi);
+            const int k = u % UPC;
+            if (k == 0) {
+                // first unit of a chunk: one 16-byte read per fragment row
+                // (16 consecutive rows per 16 lanes: no bank conflicts), bytes
+                // hi, 2 + hi, 4 + hi, 6 + hi of each pair of words kept
+                const char* sc = lds + S * STAGE + ((u / UPC) & 1) * CHUNK_BYTES;
+                const uint32_t sel = 0x06040200u + 0x01010101u * (uint32_t)hi;
+#pragma unroll
+                for (int f = 0; f < FM + FN; ++f) {
+                    const bool is_a = f < FM;
+                    const int idx = is_a ? f : f - FM;
+                    const int row = (is_a ? grp * WTM : BM + sub * WTN) + idx * 32 + l32;
+                    const i32x4_t g = *(const i32x4_t*)(sc + row * 16);
+                    const uint32_t lo = __builtin_amdgcn_perm((uint32_t)g[1], (uint32_t)g[0], sel);
+                    const uint32_t up = __builtin_amdgcn_perm((uint32_t)g[3], (uint32_t)g[2], sel);
+                    pk[f] = ((uint64_t)up << 32) | lo;
+                }
+            }
 #pragma unroll
             for (int f = 0; f < FM + FN; ++f) {
-                const bool is_a = f < FM;
-                const int idx = is_a ? f : f - FM;
-                const int row = (is_a ? grp * WTM : BM + sub * WTN) + idx * 32 + l32;
-                const int v = (int)(*(const uint32_t*)(sc + row * 16) >> sh);
-                if (is_a) sc_a[idx] = v; else sc_b[idx] = v;
+                const int v = (int)(uint32_t)(pk[f] >> (8 * k));
+                if (f < FM) sc_a[f] = v; else sc_b[f - FM] = v;
             }
         } else if constexpr (SC_LDS) {
             const char* sc = lds + (u % S) * STAGE + DATA;
