@@ -399,10 +399,15 @@ void tiled_gemm_kernel(GemmArgs p) {
         constexpr int NC = decltype(NCOPY)::value;
         constexpr int NX = N_MFMA > N_FRAG ? (N_MFMA > NC ? N_MFMA : NC)
                                            : (N_FRAG > NC ? N_FRAG : NC);
+        // Copies go out after every second MFMA where the step has room for
+        // that (fewer back-to-back copies in the address FIFOs; measured
+        // better than back-to-back and than every fourth), the reads of the
+        // next step's fragments after the first MFMAs.
+        constexpr int CS = NC > 0 && 2 * NC <= N_MFMA ? 2 : 1;
 #pragma unroll
         for (int x = 0; x < NX; ++x) {
             if (x < N_MFMA) mma_one(buf, s, x, ZERO);
-            if (x < NC) copy_one(copy_st, copy_base + x);
+            if (x % CS == 0 && x / CS < NC) copy_one(copy_st, copy_base + x / CS);
             if (x < N_FRAG) read_one(buf ^ 1, rd_st, rd_s, x);
             __builtin_amdgcn_sched_barrier(0);
         }
