@@ -17,9 +17,9 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename TOut, int MODE, int UNIT_K, int S>
+template <typename TOut, int MODE, int UNIT_K, int S, bool CM = false>
 static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, UNIT_K, S, MODE>), dim3(grid),
+    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, UNIT_K, S, MODE, CM && MODE != 1>), dim3(grid),
                        dim3(kPPThreads), 0, st, a);
     return hipGetLastError();
 }
@@ -35,6 +35,7 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_MX256x256_SPLIT2: return launch_one<TOut, 256, 256, WORDS, 2>(a, grid, st);
     case V_MXPP256: return launch_pp<TOut, MODE, 128, 2>(a, grid, st);
     case V_MXPP256_K64S4: return launch_pp<TOut, MODE, 64, 4>(a, grid, st);
+    case V_MXPP256_K64S4_CM: return launch_pp<TOut, MODE, 64, 4, true>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

@@ -44,7 +44,9 @@ constexpr int kPPThreads = 512;  // eight waves
 // SCALE_MODE (MX only) says how the E8M0 rows may be read: 0 byte by byte,
 // 1 as 32-bit words (K a multiple of 128, word-aligned arrays), 2 as 16-byte
 // pieces (K a multiple of 512, 16-byte-aligned arrays).
-template <class Op, typename TOut, int UNIT_K, int S, int SCALE_MODE = 0>
+// COPY_IN_MFMA moves a wave's operand copies from its memory half into its
+// MFMA half, one after every second MFMA (S >= 3 only).
+template <class Op, typename TOut, int UNIT_K, int S, int SCALE_MODE = 0, bool COPY_IN_MFMA = false>
 __global__ __launch_bounds__(kPPThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256;
@@ -95,6 +97,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
     static_assert(STAGE % 1024 == 0, "stage alignment");
     static_assert(RING + 8 * STG_BYTES <= 160 * 1024, "LDS budget");
     static_assert(S * OPS < 64, "vmcnt range");
+    static_assert(!COPY_IN_MFMA || (S >= 3 && COPY_GROUPS == 2 && !SC_LDS),
+                  "copies in MFMA halves: shared copies, no per-stage scale words");
     static_assert(!(SC_LDS || SC_CHUNK) || NCW == 8,
                   "one scale DMA per wave: 4 x 64 A rows, 4 x 64 B rows");
     static_assert(!SC_CHUNK || UPC == 8, "a chunk lands two halves after its DMA; 64-deep units");
@@ -194,17 +198,17 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // This wave's copies of unit fu into its stage.  Past the last unit every
     // offset is out of range: nothing is read and a stage that is never read
     // again receives zeros.
-    auto issue = [&]() {
+    auto issue_one = [&](int t) {
         const int k0 = fc.kk * BK;
         char* st = lds + (fu % S) * STAGE;
-#pragma unroll
-        for (int t = 0; t < PW; ++t) {
-            const int q = cw + t * NCW;
-            const uint32_t off = (fu < T && k0 + cp_k < K)
-                                     ? cp_lane_off + copy_row_off(t) + (uint32_t)k0 * ESZ
-                                     : kOutOfRange;
-            copy16_to_lds(q < A_COPIES ? ra : rb, st + q * 1024, off);
-        }
+        const int q = cw + t * NCW;
+        const uint32_t off = (fu < T && k0 + cp_k < K)
+                                 ? cp_lane_off + copy_row_off(t) + (uint32_t)k0 * ESZ
+                                 : kOutOfRange;
+        copy16_to_lds(q < A_COPIES ? ra : rb, st + q * 1024, off);
+    };
+    auto issue_finish = [&]() {
+        char* st = lds + (fu % S) * STAGE;
         if constexpr (SC_LDS) {
             // wave w copies the words of A rows 64 w .. (w < 4) or of B rows
             // 64 (w - 4) ..; rows past M or N read as zero
@@ -220,6 +224,11 @@ void pingpong_gemm_kernel(GemmArgs p) {
             }
         }
         ++fu;
+    };
+    auto issue = [&]() {
+#pragma unroll
+        for (int t = 0; t < PW; ++t) issue_one(t);
+        issue_finish();
     };
 
     // ---- fragments of one unit -------------------------------------------------
@@ -323,13 +332,19 @@ void pingpong_gemm_kernel(GemmArgs p) {
 
     // ---- MFMAs of one unit --------------------------------------------------------
     f32x16_t acc[FM][FN];
-    auto compute = [&](auto ZERO) {
+    auto compute = [&](auto ZERO, auto COPY) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
+                    if constexpr (decltype(COPY)::value) {
+                        constexpr int NM = KSTEPS * FM * FN;
+                        constexpr int CSTEP = NM >= 2 * PW ? 2 : 1;
+                        const int x = (s * FM + i) * FN + j;
+                        if (x % CSTEP == 0 && x / CSTEP < PW) issue_one(x / CSTEP);
+                    }
                     f32x16_t c;
                     if constexpr (decltype(ZERO)::value) {
                         if (s == 0) c = (f32x16_t){};
@@ -345,6 +360,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
                     } else {
                         acc[i][j] = Op::mma(fb[s][j], fa[s][i], c);
                     }
+                    if constexpr (decltype(COPY)::value) __builtin_amdgcn_sched_barrier(0);
                 }
     };
 
@@ -466,7 +482,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
                 // groups finished reading in earlier halves
                 if (u == cu - UPC) issue_chunk();
             }
-            if constexpr (COPIES) issue();
+            if constexpr (COPIES && !COPY_IN_MFMA) issue();
             // Waits before the barrier.  Scales loaded to registers precede
             // this half's copies, and loads return in order, so vmcnt(OPS)
             // covers them.  Group 1's older copies: the share of unit u + 1,
@@ -475,14 +491,17 @@ void pingpong_gemm_kernel(GemmArgs p) {
             if constexpr (Op::kScaled && !SC_LDS && !SC_CHUNK) {
                 wait_vmcnt<COPIES ? OPS : 0>();
             } else if constexpr (!G0 && COPY_GROUPS == 2) {
-                wait_vmcnt<(S - 2) * OPS>();
+                // copies issued in MFMA halves: unit u + 2's share came last
+                wait_vmcnt<(S - (COPY_IN_MFMA ? 3 : 2)) * OPS>();
             }
             barrier_lds();
             // ---- MFMA half
+            constexpr auto CP = std::integral_constant<bool, COPIES && COPY_IN_MFMA>{};
             if (cc.kk == 0)
-                compute(std::true_type{});
+                compute(std::true_type{}, CP);
             else
-                compute(std::false_type{});
+                compute(std::false_type{}, CP);
+            if constexpr (COPIES && COPY_IN_MFMA) issue_finish();
             advance(cc);
             // group 0's share of unit u + 1 lands before its next memory half
             if constexpr (G0) wait_vmcnt<(S - 2) * OPS>();

@@ -30,10 +30,10 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <class Op, typename TOut, int UNIT_K, int S>
+template <class Op, typename TOut, int UNIT_K, int S, bool CM = false>
 static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((pingpong_gemm_kernel<Op, TOut, UNIT_K, S>), dim3(grid), dim3(kPPThreads), 0,
-                       st, a);
+    hipLaunchKernelGGL((pingpong_gemm_kernel<Op, TOut, UNIT_K, S, 0, CM>), dim3(grid),
+                       dim3(kPPThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -50,6 +50,7 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_T256x256_SPLIT4: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 4>(a, grid, st);
     case V_PP256: return launch_pp<Op, TOut, 64, 2>(a, grid, st);
     case V_PP256_K32S4: return launch_pp<Op, TOut, 32, 4>(a, grid, st);
+    case V_PP256_K32S4_CM: return launch_pp<Op, TOut, 32, 4, true>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

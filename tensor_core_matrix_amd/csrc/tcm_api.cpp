@@ -30,8 +30,10 @@ VariantInfo variant_info(int32_t v) {
     case V_MX256x256_SPLIT2: return {256, 256, 128, 2, 1, 1, kThreads};
     case V_PP256: return {256, 256, 64, 2, 1, 2, 512};
     case V_PP256_K32S4: return {256, 256, 32, 4, 1, 2, 512};
+    case V_PP256_K32S4_CM: return {256, 256, 32, 4, 1, 2, 512};
     case V_MXPP256: return {256, 256, 128, 2, 1, 1, 512};
     case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 1, 512};
+    case V_MXPP256_K64S4_CM: return {256, 256, 64, 4, 1, 1, 512};
     }
     return {0, 0, 0, 0, 0, 0, kThreads};
 }
@@ -132,7 +134,7 @@ int64_t max_grid() {
 // least one tile with little padding; small problems take the smallest tile.
 int32_t choose_variant(int64_t batch, int64_t M, int64_t N, bool mx, int cus) {
     const int32_t f = forced_variant();
-    if (f >= 0 && variant_info(f).tile_m > 0 && (f >= V_MX256x256) == mx) return f;
+    if (f >= 0 && variant_info(f).tile_m > 0 && (variant_info(f).elem_bytes == 1) == mx) return f;
     static const int32_t plain[] = {V_T256x256_SPLIT2, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MXPP256_K64S4, V_MX128x128};
     const int32_t* cand = mx ? mxv : plain;

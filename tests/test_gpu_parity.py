@@ -297,8 +297,8 @@ def test_repeat_runs_bitwise_identical():
 
 
 # ------------------------------------------------------ every kernel variant
-PLAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9]
-MX_VARIANTS = [10, 11, 12, 13, 14]
+PLAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 16]
+MX_VARIANTS = [10, 11, 12, 13, 14, 15]
 
 
 @pytest.fixture
