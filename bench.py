@@ -47,8 +47,11 @@ def kernel_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The shader clock ramps up over the first tens of milliseconds of load:
+    # 50 untimed calls (about 40 ms of the headline workload) reach the
+    # steady state before the 100 timed ones.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle's CPU sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")

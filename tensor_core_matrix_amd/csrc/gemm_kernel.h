@@ -83,8 +83,11 @@ struct TileCursor {
     int tl, kk, batch, tm, tn;
 };
 
+// VG selects the copy path: false, direct-to-LDS DMA (`buffer_load ... lds`);
+// true, 16-byte buffer loads into registers one slice ahead and `ds_write_b128`
+// into the ring when the stage is free (plain bf16/f16, 2-stage ring).
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int SWZ,
-          bool SCALE_WORDS = false, int NSPLIT = 1, bool EPI_LDS = false>
+          bool SCALE_WORDS = false, int NSPLIT = 1, bool EPI_LDS = false, bool VG = false>
 __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void tiled_gemm_kernel(GemmArgs p) {
     constexpr int ESZ = Op::kElemBytes;
@@ -112,6 +115,7 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert(S >= 2, "ring depth");
     static_assert((32 >> SWZ) % CPR == 0, "swizzle must depend on the row within 32 only");
     static_assert(!Op::kScaled || (BK == 128 && S == 2), "MX path: 128-deep slices, 2 stages");
+    static_assert(!VG || (!Op::kScaled && S == 2), "register-staged copies: plain types, 2 stages");
 
     // Epilogue staging: one 32-row block of a wave's output at a time, in a
     // wave-private LDS area after the ring.
@@ -175,27 +179,26 @@ void tiled_gemm_kernel(GemmArgs p) {
             }
         }
     };
-    // Per-copy buffer offsets of the stream's current slice, computed outside
-    // the hot region.  A slice past the last one (`live` false) and 16-byte
-    // chunks past K get out-of-range offsets: those copies touch no memory
-    // and write zeros into a stage that is never read again.
-    constexpr int MAX_LOADS = A_LOADS > B_LOADS ? A_LOADS : B_LOADS;
-    uint32_t foff[MAX_LOADS];
+    // Buffer offset of copy 0 of the stream's current slice, computed outside
+    // the hot region; copy i adds i * cp_step.  A slice past the last one
+    // (`live` false) and 16-byte chunks past K get out-of-range offsets
+    // (>= 2^31, beyond any tile's records even after adding i * cp_step):
+    // those copies touch no memory and write zeros into a stage that is
+    // never read again.
+    uint32_t foff0;
     auto feed_offsets = [&](bool live) {
         const int k0 = fc.kk * BK;
-        const uint32_t off0 =
-            (live && k0 + cp_k < K) ? cp_off + (uint32_t)k0 * ESZ : kOutOfRange;
-#pragma unroll
-        for (int i = 0; i < MAX_LOADS; ++i) foff[i] = off0 + i * cp_step;
+        foff0 = (live && k0 + cp_k < K) ? cp_off + (uint32_t)k0 * ESZ : kOutOfRange;
     };
+    auto foff = [&](int i) -> uint32_t { return foff0 + (uint32_t)i * cp_step; };
     // Copies of the stream's current slice into ring stage `st`.
     auto issue = [&](int st) {
         char* sa = lds + st * STAGE;
         char* sb = sa + A_BYTES;
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) copy16_to_lds(ra, sa + (4 * i + wave) * 1024, foff[i]);
+        for (int i = 0; i < A_LOADS; ++i) copy16_to_lds(ra, sa + (4 * i + wave) * 1024, foff(i));
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) copy16_to_lds(rb, sb + (4 * i + wave) * 1024, foff[i]);
+        for (int i = 0; i < B_LOADS; ++i) copy16_to_lds(rb, sb + (4 * i + wave) * 1024, foff(i));
     };
 
     // ---- per-lane fragment geometry ---------------------------------------
@@ -290,12 +293,30 @@ void tiled_gemm_kernel(GemmArgs p) {
         else
             fb[buf][x - FM] = read_frag(st + b_frag + (x - FM) * 32 * RB, s);
     };
+    // Register-staged copies: stg[x] holds copy x of the slice being written
+    // (the copy stream's slice fg); `fc`/`foff` run one slice ahead, on the
+    // slice whose loads refill stg.  Lane l of copy x writes the same LDS
+    // bytes as the DMA form would.
+    i32x4_t stg[VG ? LOADS : 1];
+    auto load_one = [&](int x) {
+        if constexpr (VG) {
+            const __amdgpu_buffer_rsrc_t r = x < A_LOADS ? ra : rb;
+            const uint32_t off = x < A_LOADS ? foff(x) : foff(x - A_LOADS);
+            stg[x] = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        }
+    };
     auto copy_one = [&](int st, int x) {
         char* sa = lds + st * STAGE;
-        if (x < A_LOADS)
-            copy16_to_lds(ra, sa + (4 * x + wave) * 1024, foff[x]);
-        else
-            copy16_to_lds(rb, sa + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024, foff[x - A_LOADS]);
+        if constexpr (VG) {
+            char* dst = x < A_LOADS ? sa + (4 * x + wave) * 1024
+                                    : sa + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024;
+            *(i32x4_t*)(dst + lane * 16) = stg[x];
+            load_one(x);
+        } else if (x < A_LOADS) {
+            copy16_to_lds(ra, sa + (4 * x + wave) * 1024, foff(x));
+        } else {
+            copy16_to_lds(rb, sa + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024, foff(x - A_LOADS));
+        }
     };
 
     auto epilogue = [&](const TileCursor& c) {
@@ -423,7 +444,7 @@ void tiled_gemm_kernel(GemmArgs p) {
     auto feed_next = [&]() {
         feed_advance();
         ++fg;
-        feed_offsets(fg < total);
+        feed_offsets(fg + (VG ? 1 : 0) < total);
     };
 
     // ---- prologue: slices 0 .. S-2 and part 0 of slice S-1 in flight -------
@@ -431,16 +452,41 @@ void tiled_gemm_kernel(GemmArgs p) {
     feed_resources();
     TileCursor cc = fc;
     feed_offsets(true);
+    if constexpr (VG) {
+        // slice 0 straight into stage 0; slice 1 into registers, the load
+        // stream moved on to slice 2, and part 0 of slice 1 written
 #pragma unroll
-    for (int g = 0; g < S - 1; ++g) {
-        issue(g);
-        feed_next();
+        for (int x = 0; x < LOADS; ++x) load_one(x);
+        char* s0 = lds;
+#pragma unroll
+        for (int x = 0; x < LOADS; ++x) {
+            char* dst = x < A_LOADS ? s0 + (4 * x + wave) * 1024
+                                    : s0 + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024;
+            *(i32x4_t*)(dst + lane * 16) = stg[x];
+        }
+        feed_advance();
+        feed_offsets(1 < total);
+#pragma unroll
+        for (int x = 0; x < LOADS; ++x) load_one(x);
+        feed_advance();
+        fg = 1;
+        feed_offsets(2 < total);
+#pragma unroll
+        for (int x = 0; x < PART; ++x) copy_one(1, x);
+        if constexpr (NSPLIT == 1) feed_next();
+        barrier_lds();
+    } else {
+#pragma unroll
+        for (int g = 0; g < S - 1; ++g) {
+            issue(g);
+            feed_next();
+        }
+#pragma unroll
+        for (int x = 0; x < PART; ++x) copy_one(S - 1, x);
+        if constexpr (NSPLIT == 1) feed_next();
+        wait_vmcnt<(S - 2) * LOADS + PART>();
+        barrier_lds();
     }
-#pragma unroll
-    for (int x = 0; x < PART; ++x) copy_one(S - 1, x);
-    if constexpr (NSPLIT == 1) feed_next();
-    wait_vmcnt<(S - 2) * LOADS + PART>();
-    barrier_lds();
     read_frags(0, lds, 0);
     if constexpr (Op::kScaled) load_scales(cc, sc_a, sc_b);
 
@@ -482,10 +528,14 @@ void tiled_gemm_kernel(GemmArgs p) {
                         kstep(cur, s, st, s + 1, 0, 0, NONE, std::false_type{});
                 }
             } else {
-                if (S > 2 && !after_epilogue && g + S - 1 < total)
+                // register-staged copies: their writes are LDS operations,
+                // covered by the barrier's lgkmcnt wait
+                if constexpr (VG) {
+                } else if (S > 2 && !after_epilogue && g + S - 1 < total) {
                     wait_vmcnt<(S > 2 ? (S - 2) * LOADS : 0)>();
-                else
+                } else {
                     wait_vmcnt<0>();
+                }
                 after_epilogue = false;
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);

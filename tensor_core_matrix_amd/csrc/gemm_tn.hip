@@ -21,11 +21,12 @@ constexpr bool epilogue_fits() {
 }
 
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int NSPLIT = 1,
-          bool EPI = true>
+          bool EPI = true, bool VG = false>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     constexpr bool epi = EPI && OCC == 1 && epilogue_fits<TOut, BM, BN, BK, S>();
     hipLaunchKernelGGL(
-        (tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, swizzle_shift<BK>(), false, NSPLIT, epi>),
+        (tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, swizzle_shift<BK>(), false, NSPLIT, epi,
+                           VG>),
         dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
@@ -48,6 +49,8 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_T256x256_K32S5: return launch_one<Op, TOut, 256, 256, 32, 5, 1, 2>(a, grid, st);
     case V_T256x256_SPLIT2: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 2>(a, grid, st);
     case V_T256x256_SPLIT4: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 4>(a, grid, st);
+    case V_T256x256_VG2: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 2, true, true>(a, grid, st);
+    case V_T256x256_VG4: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 4, true, true>(a, grid, st);
     case V_PP256: return launch_pp<Op, TOut, 64, 2>(a, grid, st);
     case V_PP256_K32S4: return launch_pp<Op, TOut, 32, 4>(a, grid, st);
     case V_PP256_K32S4_CM: return launch_pp<Op, TOut, 32, 4, true>(a, grid, st);

@@ -31,6 +31,8 @@ VariantInfo variant_info(int32_t v) {
     case V_PP256: return {256, 256, 64, 2, 1, 2, 512};
     case V_PP256_K32S4: return {256, 256, 32, 4, 1, 2, 512};
     case V_PP256_K32S4_CM: return {256, 256, 32, 4, 1, 2, 512};
+    case V_T256x256_VG2: return {256, 256, 64, 2, 1, 2, kThreads};
+    case V_T256x256_VG4: return {256, 256, 64, 2, 1, 2, kThreads};
     case V_MXPP256: return {256, 256, 128, 2, 1, 1, 512};
     case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 1, 512};
     case V_MXPP256_K64S4_CM: return {256, 256, 64, 4, 1, 1, 512};

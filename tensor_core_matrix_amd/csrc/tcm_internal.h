@@ -40,6 +40,8 @@ enum Variant : int32_t {
     V_PP256 = 8,           // 256x256x64, eight waves taking turns (ping-pong), 2-stage ring
     V_PP256_K32S4 = 9,     // 256x256x32 ping-pong, 4-stage ring, copies shared by all waves
     V_PP256_K32S4_CM = 16, // variant 9 with the copies issued between the MFMAs
+    V_T256x256_VG2 = 17,   // variant 6 with register-staged copies (loads + ds_write)
+    V_T256x256_VG4 = 18,   // variant 7 with register-staged copies
     V_MX256x256 = 10, // MXFP8 256x256x128, 2-stage ring
     V_MX128x128 = 11, // MXFP8 128x128x128, 2-stage ring
     V_MX256x256_SPLIT2 = 12, // MXFP8 256x256x128, copies split over 2 K steps
