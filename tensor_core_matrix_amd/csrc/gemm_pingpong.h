@@ -77,6 +77,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int KSTEPS = BK / Op::kK;
     constexpr int CPL = Op::kK * ESZ / 32;
     // copies: 1 KiB per wave instruction; shared by both groups when S >= 3
+    // With two stages group 1's share would have to land within the half it
+    // is issued in (measured: far slower), so group 0 copies alone.
     constexpr int COPY_GROUPS = S >= 3 ? 2 : 1;
     constexpr int NCW = 4 * COPY_GROUPS;               // copying waves
     constexpr int A_COPIES = A_BYTES / 1024;
@@ -198,14 +200,18 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // This wave's copies of unit fu into its stage.  Past the last unit every
     // offset is out of range: nothing is read and a stage that is never read
     // again receives zeros.
-    auto issue_one = [&](int t) {
+    // Offset of this lane's piece in copy 0 of unit fu; copy t adds the
+    // wave-uniform copy_row_off(t).  Out of range (>= 2^31, beyond any
+    // tile's records even with a row offset added) past the last unit and
+    // for pieces past K.
+    auto copy_base = [&]() -> uint32_t {
         const int k0 = fc.kk * BK;
-        char* st = lds + (fu % S) * STAGE;
+        return (fu < T && k0 + cp_k < K) ? cp_lane_off + (uint32_t)k0 * ESZ : kOutOfRange;
+    };
+    auto issue_one = [&](int t, uint32_t base) {
         const int q = cw + t * NCW;
-        const uint32_t off = (fu < T && k0 + cp_k < K)
-                                 ? cp_lane_off + copy_row_off(t) + (uint32_t)k0 * ESZ
-                                 : kOutOfRange;
-        copy16_to_lds(q < A_COPIES ? ra : rb, st + q * 1024, off);
+        copy16_to_lds(q < A_COPIES ? ra : rb, lds + (fu % S) * STAGE + q * 1024,
+                      base + copy_row_off(t));
     };
     auto issue_finish = [&]() {
         char* st = lds + (fu % S) * STAGE;
@@ -226,8 +232,9 @@ void pingpong_gemm_kernel(GemmArgs p) {
         ++fu;
     };
     auto issue = [&]() {
+        const uint32_t base = copy_base();
 #pragma unroll
-        for (int t = 0; t < PW; ++t) issue_one(t);
+        for (int t = 0; t < PW; ++t) issue_one(t, base);
         issue_finish();
     };
 
@@ -343,7 +350,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
                         constexpr int NM = KSTEPS * FM * FN;
                         constexpr int CSTEP = NM >= 2 * PW ? 2 : 1;
                         const int x = (s * FM + i) * FN + j;
-                        if (x % CSTEP == 0 && x / CSTEP < PW) issue_one(x / CSTEP);
+                        if (x % CSTEP == 0 && x / CSTEP < PW) issue_one(x / CSTEP, copy_base());
                     }
                     f32x16_t c;
                     if constexpr (decltype(ZERO)::value) {
@@ -485,13 +492,17 @@ void pingpong_gemm_kernel(GemmArgs p) {
             if constexpr (COPIES && !COPY_IN_MFMA) issue();
             // Waits before the barrier.  Scales loaded to registers precede
             // this half's copies, and loads return in order, so vmcnt(OPS)
-            // covers them.  Group 1's older copies: the share of unit u + 1,
-            // which group 0 reads in the next half, has (S - 2) * OPS
-            // operations issued after it.
-            if constexpr (Op::kScaled && !SC_LDS && !SC_CHUNK) {
-                wait_vmcnt<COPIES ? OPS : 0>();
-            } else if constexpr (!G0 && COPY_GROUPS == 2) {
-                // copies issued in MFMA halves: unit u + 2's share came last
+            // covers them.  Group 1's copies of unit u + 1, which group 0 reads
+            // in the next half, have (S - 2) * OPS operations issued after
+            // them ((S - 3) * OPS when copies go out in MFMA halves).
+            constexpr bool REG_SCALES = Op::kScaled && !SC_LDS && !SC_CHUNK;
+            if constexpr (G0) {
+                if constexpr (REG_SCALES) wait_vmcnt<OPS>();
+            } else if constexpr (S == 2) {
+                if constexpr (COPIES || REG_SCALES) wait_vmcnt<0>();
+            } else if constexpr (REG_SCALES) {
+                wait_vmcnt<OPS>();
+            } else {
                 wait_vmcnt<(S - (COPY_IN_MFMA ? 3 : 2)) * OPS>();
             }
             barrier_lds();
