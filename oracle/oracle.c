@@ -31,11 +31,18 @@
  *   a(i,k) = e4m3(A[i][k]) * e8m0(SA[i][k/32])
  *   b(j,k) = e4m3(B[j][k]) * e8m0(SB[j][k/32])
  *
+ * and the same with E2M1 (MXFP4, the format table's 4-bit row) elements in
+ * place of E4M3.
+ *
  * Element decoders are written from the format definitions (IEEE 754
  * binary16; bfloat16 = the upper half of binary32; OCP MX E4M3 "FN" with bias
- * 7, no infinities, S.1111.111 = NaN; E8M0 = 2^(e-127), 0xFF = NaN).  The page
- * table names these formats but does not print their bit layouts; the OCP
- * Microscaling specification cited in that page's "Go deeper" list does.
+ * 7, no infinities, S.1111.111 = NaN; OCP MX E2M1 with bias 1, no infinities
+ * or NaN; E8M0 = 2^(e-127), 0xFF = NaN).  The page table names these formats
+ * but does not print their bit layouts; the OCP Microscaling specification
+ * cited in that page's "Go deeper" list does.  E2M1 elements are stored two
+ * per byte, element 2t in the low four bits of byte t and element 2t + 1 in
+ * the high four bits (the pages fix no packing; this is the plainest
+ * little-endian reading), so a row of K elements is K/2 bytes.
  *
  * Accuracy: sequential fp64 summation errs by at most about K * 2^-53 *
  * abssum, far below any tolerance used against the GPU path.  Every MX
@@ -47,7 +54,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F16 = 0, OR_BF16 = 1, OR_F32 = 2, OR_E4M3 = 3, OR_E8M0 = 4 };
+enum { OR_F16 = 0, OR_BF16 = 1, OR_F32 = 2, OR_E4M3 = 3, OR_E8M0 = 4, OR_E2M1 = 5 };
 
 /* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits. */
 static double dec_f16(uint16_t h) {
@@ -90,6 +97,14 @@ static double dec_e4m3(uint8_t b) {
 }
 
 /* OCP E8M0: unsigned exponent only, 2^(e-127); 0xFF is NaN. */
+/* OCP E2M1: 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent field 0
+ * holds the subnormal 0.5 * m; no infinities, no NaN. */
+static double dec_e2m1(unsigned nib) {
+    int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
 static double dec_e8m0(uint8_t b) {
     if (b == 0xff)
         return NAN;
@@ -102,16 +117,19 @@ static double dec_f32(uint32_t w) {
     return (double)f;
 }
 
-static int elem_size(int dtype) {
+/* Storage bits per element. */
+static int elem_bits(int dtype) {
     switch (dtype) {
     case OR_F16:
     case OR_BF16:
-        return 2;
+        return 16;
     case OR_F32:
-        return 4;
+        return 32;
     case OR_E4M3:
     case OR_E8M0:
-        return 1;
+        return 8;
+    case OR_E2M1:
+        return 4;
     }
     return 0;
 }
@@ -128,13 +146,17 @@ static double dec_one(int dtype, const void* src, int64_t idx) {
         return dec_e4m3(((const uint8_t*)src)[idx]);
     case OR_E8M0:
         return dec_e8m0(((const uint8_t*)src)[idx]);
+    case OR_E2M1: {
+        uint8_t byte = ((const uint8_t*)src)[idx / 2];
+        return dec_e2m1((idx & 1) ? byte >> 4 : byte & 0xF);
+    }
     }
     return NAN;
 }
 
 /* Decode n stored elements of the given format into exact fp64 values. */
 int oracle_decode(int dtype, const void* src, int64_t n, double* dst) {
-    if (!elem_size(dtype) || (n > 0 && (!src || !dst)))
+    if (!elem_bits(dtype) || (n > 0 && (!src || !dst)))
         return -1;
     for (int64_t i = 0; i < n; ++i)
         dst[i] = dec_one(dtype, src, i);
@@ -249,7 +271,7 @@ int oracle_gemm_tn(int dtype, const void* A, const void* B, int64_t batch, int64
     if (!(dtype == OR_F16 || dtype == OR_BF16 || dtype == OR_F32) || !A || !B ||
         !shape_ok(batch, M, N, K))
         return -1;
-    int es = elem_size(dtype);
+    int es = elem_bits(dtype) / 8;
     for (int64_t p = 0; p < batch; ++p) {
         int rc = gemm_one(dtype, (const char*)A + p * M * K * es, (const char*)B + p * N * K * es,
                           NULL, NULL, M, N, K, ref ? ref + p * M * N : NULL,
@@ -260,33 +282,45 @@ int oracle_gemm_tn(int dtype, const void* A, const void* B, int64_t batch, int64
     return 0;
 }
 
-/* MX block-scaled GEMM: E4M3 elements, one E8M0 scale per 32 consecutive K
- * elements of every row of A (SA: M x K/32) and of B (SB: N x K/32). */
+/* MX block-scaled GEMM with elements of format `dtype` (OR_E4M3 or OR_E2M1),
+ * one E8M0 scale per 32 consecutive K elements of every row of A
+ * (SA: M x K/32) and of B (SB: N x K/32). */
+int oracle_gemm_mx_typed(int dtype, const uint8_t* A, const uint8_t* B, const uint8_t* SA,
+                         const uint8_t* SB, int64_t M, int64_t N, int64_t K, double* ref,
+                         double* abssum, int nthreads) {
+    if (!(dtype == OR_E4M3 || dtype == OR_E2M1) || !A || !B || !SA || !SB ||
+        !shape_ok(1, M, N, K) || K % 32 != 0)
+        return -1;
+    return gemm_one(dtype, A, B, SA, SB, M, N, K, ref, abssum, nthreads);
+}
+
+/* The E4M3 form. */
 int oracle_gemm_mx(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const uint8_t* SB,
                    int64_t M, int64_t N, int64_t K, double* ref, double* abssum, int nthreads) {
-    if (!A || !B || !SA || !SB || !shape_ok(1, M, N, K) || K % 32 != 0)
-        return -1;
-    return gemm_one(OR_E4M3, A, B, SA, SB, M, N, K, ref, abssum, nthreads);
+    return oracle_gemm_mx_typed(OR_E4M3, A, B, SA, SB, M, N, K, ref, abssum, nthreads);
 }
 
 /*
  * Selected entries only, for problems too large to compute whole: entry t is
  * (row ii[t], column jj[t]) of problem bb[t] (bb may be NULL for batch 1).
- * SA/SB non-NULL selects the MX definition (dtype must then be OR_E4M3).
+ * SA/SB non-NULL selects the MX definition (dtype must then be OR_E4M3 or
+ * OR_E2M1).
  */
 int oracle_entries(int dtype, const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
                    int64_t M, int64_t N, int64_t K, const int64_t* bb, const int64_t* ii,
                    const int64_t* jj, int64_t n, double* ref, double* abssum) {
-    if (!elem_size(dtype) || !A || !B || !ii || !jj || !shape_ok(1, M, N, K) ||
-        ((SA || SB) && (!SA || !SB || dtype != OR_E4M3 || K % 32 != 0)))
+    if (!elem_bits(dtype) || !A || !B || !ii || !jj || !shape_ok(1, M, N, K) ||
+        ((SA || SB) &&
+         (!SA || !SB || !(dtype == OR_E4M3 || dtype == OR_E2M1) || K % 32 != 0)) ||
+        (dtype == OR_E2M1 && (!SA || K % 2 != 0)))
         return -1;
-    int es = elem_size(dtype);
+    const int64_t bits = elem_bits(dtype);
     for (int64_t t = 0; t < n; ++t) {
         int64_t p = bb ? bb[t] : 0, i = ii[t], j = jj[t];
         if (p < 0 || i < 0 || i >= M || j < 0 || j >= N || (SA && p != 0))
             return -1;
-        const char* Ap = (const char*)A + p * M * K * es;
-        const char* Bp = (const char*)B + p * N * K * es;
+        const char* Ap = (const char*)A + p * M * K * bits / 8;
+        const char* Bp = (const char*)B + p * N * K * bits / 8;
         double s = 0.0, sa = 0.0;
         for (int64_t k = 0; k < K; ++k) {
             double prod = operand_value(dtype, Ap, SA, K, i, k) * operand_value(dtype, Bp, SB, K, j, k);

@@ -19,7 +19,8 @@ the single rounding of the fp32 result to a bf16 output.
 
 Inputs are numpy arrays holding the raw storage of the operands:
 uint16 for float16 / bfloat16 bit patterns, uint8 for E4M3 and E8M0 bytes,
-float32 for float32.
+uint8 for E2M1 pairs (two elements per byte, the even element in the low four
+bits, so an M x K operand is stored M x K/2), float32 for float32.
 """
 from __future__ import annotations
 
@@ -30,8 +31,8 @@ import threading
 
 import numpy as np
 
-F16, BF16, F32, E4M3, E8M0 = 0, 1, 2, 3, 4
-DTYPE_NAMES = {"f16": F16, "bf16": BF16, "f32": F32, "e4m3": E4M3, "e8m0": E8M0}
+F16, BF16, F32, E4M3, E8M0, E2M1 = 0, 1, 2, 3, 4, 5
+DTYPE_NAMES = {"f16": F16, "bf16": BF16, "f32": F32, "e4m3": E4M3, "e8m0": E8M0, "e2m1": E2M1}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -63,10 +64,12 @@ def _load():
             lib.oracle_gemm_tn.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, i64, dp, dp,
                                            ctypes.c_int]
             lib.oracle_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, dp, dp, ctypes.c_int]
+            lib.oracle_gemm_mx_typed.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, dp,
+                                                 dp, ctypes.c_int]
             lib.oracle_entries.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, vp, vp,
                                            vp, i64, dp, dp]
             for f in (lib.oracle_decode, lib.oracle_gemm_tn, lib.oracle_gemm_mx,
-                      lib.oracle_entries):
+                      lib.oracle_gemm_mx_typed, lib.oracle_entries):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -79,7 +82,8 @@ def default_threads() -> int:
         return max(1, os.cpu_count() or 1)
 
 
-_STORAGE = {F16: np.uint16, BF16: np.uint16, F32: np.float32, E4M3: np.uint8, E8M0: np.uint8}
+_STORAGE = {F16: np.uint16, BF16: np.uint16, F32: np.float32, E4M3: np.uint8, E8M0: np.uint8,
+            E2M1: np.uint8}
 
 
 def _raw(x: np.ndarray, dtype: int) -> np.ndarray:
@@ -95,10 +99,12 @@ def _ptr(x):
 
 
 def decode(dtype: int, raw: np.ndarray) -> np.ndarray:
-    """Exact fp64 values of stored elements (format definitions, see oracle.c)."""
+    """Exact fp64 values of stored elements (format definitions, see oracle.c).
+    E2M1 storage of shape (..., n) decodes to shape (..., 2 n)."""
     raw = _raw(raw, dtype)
-    out = np.empty(raw.shape, dtype=np.float64)
-    rc = _load().oracle_decode(dtype, _ptr(raw), raw.size, _ptr(out))
+    shape = raw.shape[:-1] + (raw.shape[-1] * 2,) if dtype == E2M1 else raw.shape
+    out = np.empty(shape, dtype=np.float64)
+    rc = _load().oracle_decode(dtype, _ptr(raw), out.size, _ptr(out))
     if rc:
         raise ValueError(f"oracle_decode failed ({rc})")
     return out
@@ -125,18 +131,20 @@ def gemm_tn(dtype: int, a: np.ndarray, b: np.ndarray, nthreads: int | None = Non
 
 
 def gemm_mx(a: np.ndarray, b: np.ndarray, sa: np.ndarray, sb: np.ndarray,
-            nthreads: int | None = None):
-    """ref, abssum for the MX block-scaled product: a M x K, b N x K E4M3 bytes;
-    sa M x K/32, sb N x K/32 E8M0 bytes."""
-    a, b, sa, sb = _raw(a, E4M3), _raw(b, E4M3), _raw(sa, E8M0), _raw(sb, E8M0)
-    M, K = a.shape
+            nthreads: int | None = None, dtype: int = E4M3):
+    """ref, abssum for the MX block-scaled product: a M x K, b N x K elements of
+    `dtype` (E4M3 bytes, or E2M1 pairs stored M x K/2 and N x K/2); sa M x K/32,
+    sb N x K/32 E8M0 bytes."""
+    a, b, sa, sb = _raw(a, dtype), _raw(b, dtype), _raw(sa, E8M0), _raw(sb, E8M0)
+    M = a.shape[0]
     N = b.shape[0]
-    if b.shape[1] != K or K % 32 or sa.shape != (M, K // 32) or sb.shape != (N, K // 32):
+    K = a.shape[1] * (2 if dtype == E2M1 else 1)
+    if b.shape[1] != a.shape[1] or K % 32 or sa.shape != (M, K // 32) or sb.shape != (N, K // 32):
         raise ValueError("bad MX shapes")
     ref = np.empty((M, N), np.float64)
     s = np.empty((M, N), np.float64)
-    rc = _load().oracle_gemm_mx(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K, _ptr(ref),
-                                _ptr(s), nthreads or default_threads())
+    rc = _load().oracle_gemm_mx_typed(dtype, _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), M, N, K,
+                                      _ptr(ref), _ptr(s), nthreads or default_threads())
     if rc:
         raise ValueError(f"oracle_gemm_mx failed ({rc})")
     return ref, s
@@ -151,6 +159,8 @@ def entries(dtype: int, a: np.ndarray, b: np.ndarray, ii, jj, bb=None, sa=None, 
     else:
         a3, b3 = a, b
     _, M, K = a3.shape
+    if dtype == E2M1:
+        K *= 2
     N = b3.shape[1]
     ii = np.ascontiguousarray(ii, dtype=np.int64)
     jj = np.ascontiguousarray(jj, dtype=np.int64)

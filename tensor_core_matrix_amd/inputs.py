@@ -19,6 +19,8 @@ problems):
 * ``mxfp8_8192`` -- A, B 8192x8192 E4M3 drawn N(0,1) then cast, one E8M0 scale
   per 32 K elements per row with exponents uniform on the integers -4..4,
   seed 4, bf16 output ("Hopper and Blackwell GEMM", block-scaling table).
+* ``mxfp4_8192`` -- the same with E2M1 elements (MXFP4, the table's 4-bit
+  row): every 4-bit code equally likely, seed 5, bf16 output.
 """
 from __future__ import annotations
 
@@ -36,10 +38,10 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str          # "f16", "bf16" or "e4m3" (MX block-scaled)
+    dtype: str          # "f16", "bf16", or "e4m3" / "e2m1" (MX block-scaled)
     out_dtype: str      # "f32" or "bf16"
     seed: int
-    dist: str           # "uniform" or "normal"
+    dist: str           # "uniform", "normal" or "codes" (every code equally likely)
     sigma: float = 1.0
     scale_exp: tuple = field(default=(-4, 4))
 
@@ -54,6 +56,7 @@ WORKLOADS = {
     "batched": Workload("batched", 1024, 128, 256, 64, "bf16", "f32", 2, "uniform"),
     "bf16_8192": Workload("bf16_8192", 1, 8192, 8192, 8192, "bf16", "bf16", 3, "normal", 0.05),
     "mxfp8_8192": Workload("mxfp8_8192", 1, 8192, 8192, 8192, "e4m3", "bf16", 4, "normal", 1.0),
+    "mxfp4_8192": Workload("mxfp4_8192", 1, 8192, 8192, 8192, "e2m1", "bf16", 5, "codes"),
 }
 
 TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
@@ -82,6 +85,14 @@ def e4m3_normal(shape, gen, sigma=1.0) -> torch.Tensor:
     return x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
 
 
+def e2m1_codes(rows: int, k: int, gen) -> torch.Tensor:
+    """rows x k E2M1 elements, every 4-bit code equally likely, stored two per
+    byte (element 2t in the low four bits of byte t): uint8 of shape
+    rows x k/2."""
+    c = torch.randint(0, 16, (rows, k), generator=gen, dtype=torch.int32)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).to(torch.uint8)
+
+
 def e8m0_scales(shape, gen, lo=-4, hi=4) -> torch.Tensor:
     """E8M0 bytes 127+s with s uniform on the integers lo..hi."""
     return (torch.randint(lo, hi + 1, shape, generator=gen, dtype=torch.int32)
@@ -101,9 +112,13 @@ def make(w: Workload | str) -> dict:
     g = generator(w.seed)
     lead = (w.batch,) if w.batch > 1 else ()
     shp_a, shp_b = lead + (w.M, w.K), lead + (w.N, w.K)
-    if w.dtype == "e4m3":
-        a = e4m3_normal(shp_a, g, w.sigma)
-        b = e4m3_normal(shp_b, g, w.sigma)
+    if w.dtype in ("e4m3", "e2m1"):
+        if w.dtype == "e4m3":
+            a = e4m3_normal(shp_a, g, w.sigma)
+            b = e4m3_normal(shp_b, g, w.sigma)
+        else:
+            a = e2m1_codes(w.M, w.K, g)
+            b = e2m1_codes(w.N, w.K, g)
         lo, hi = w.scale_exp
         sa = e8m0_scales((w.M, w.K // 32), g, lo, hi)
         sb = e8m0_scales((w.N, w.K // 32), g, lo, hi)

@@ -13,7 +13,12 @@ applied to the wrong block -- fails at least one of them:
 * quarter-integer operands (the input structure of the 16x8x32 example on the
   "mma.sync" page, Examples): exact integer arithmetic;
 * invariants: transpose symmetry, power-of-two linearity, batch slices, MX
-  with unit scales equals the plain E4M3 product, uniform scale shifts.
+  with unit scales equals the plain E4M3 product, uniform scale shifts;
+* E2M1 (MXFP4): the format's sixteen values as the OCP specification lists
+  them, the nibble order of a hand-packed byte, every value re-encoded by
+  torch's own E4M3 cast decoding the same, and the MXFP4 product equal to the
+  MXFP8 product of the same values (E2M1 is a subset of E4M3), plus brute
+  force.
 """
 from fractions import Fraction
 
@@ -31,6 +36,13 @@ def _same(x, y):
     """Bitwise-equal float64 arrays, NaN matching NaN."""
     x, y = np.asarray(x, np.float64), np.asarray(y, np.float64)
     return x.shape == y.shape and bool(np.all((x == y) | (np.isnan(x) & np.isnan(y))))
+
+
+def _e2m1_to_e4m3(codes_packed: np.ndarray) -> np.ndarray:
+    """E4M3 bytes holding the same values as packed E2M1 pairs, encoded by
+    torch's float8 cast (every E2M1 value is exactly an E4M3 value)."""
+    v = orc.decode(orc.E2M1, codes_packed)
+    return torch.from_numpy(v).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 # ---------------------------------------------------------------- decoders
@@ -52,6 +64,22 @@ def test_decode_e4m3_all_patterns():
     got = orc.decode(orc.E4M3, bits)
     assert _same(got, want)
     assert np.nanmax(got) == 448.0 and np.isnan(got).sum() == 2  # 0x7F, 0xFF
+
+
+def test_decode_e2m1_all_codes_and_nibble_order():
+    # OCP MX E2M1: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7 (sign
+    # in bit 3), listed here as the specification's table, not recomputed
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    codes = np.arange(16, dtype=np.uint8)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    got = orc.decode(orc.E2M1, packed)
+    assert list(got[:8]) == table and list(-got[8:]) == table
+    assert np.signbit(got[8])  # code 8 is -0
+    # byte 0x21 holds element 0 = code 1 (0.5) in its low nibble, element 1 =
+    # code 2 (1.0) in its high nibble; 0xF7: 6.0, then code 15 = -6.0
+    assert list(orc.decode(orc.E2M1, np.array([0x21, 0xF7], np.uint8))) == [0.5, 1.0, 6.0, -6.0]
+    # each value, re-encoded by torch's E4M3 cast, decodes identically
+    assert _same(orc.decode(orc.E4M3, _e2m1_to_e4m3(packed)), got)
 
 
 def test_decode_e8m0_all_patterns():
@@ -111,6 +139,53 @@ def test_brute_force_mx(shape):
                       * Fraction(float(bv[j, k])) * Fraction(2) ** int(eb[j, k // 32])
                       for k in range(K)), Fraction(0))
             assert abs(Fraction(ref[i, j]) - ex) <= Fraction(K * 2.0 ** -52) * Fraction(s[i, j])
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (3, 4, 64), (2, 3, 96)])
+def test_brute_force_mxfp4(shape):
+    M, N, K = shape
+    g = inp.generator(40 + K)
+    a = inp.e2m1_codes(M, K, g)
+    b = inp.e2m1_codes(N, K, g)
+    sa = inp.e8m0_scales((M, K // 32), g, -6, 6)
+    sb = inp.e8m0_scales((N, K // 32), g, -6, 6)
+    ref, s = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), dtype=orc.E2M1)
+    # element values straight from the specification's table and the
+    # low-nibble-first packing, independent of the oracle's decoder
+    mag = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+           Fraction(4), Fraction(6)]
+
+    def val(packed, r, k):
+        byte = int(packed[r, k // 2])
+        c = (byte >> 4) if k % 2 else (byte & 15)
+        return -mag[c & 7] if c & 8 else mag[c & 7]
+
+    an, bn = a.numpy(), b.numpy()
+    ea = sa.numpy().astype(np.int64) - 127
+    eb = sb.numpy().astype(np.int64) - 127
+    for i in range(M):
+        for j in range(N):
+            ex = sum((val(an, i, k) * Fraction(2) ** int(ea[i, k // 32])
+                      * val(bn, j, k) * Fraction(2) ** int(eb[j, k // 32])
+                      for k in range(K)), Fraction(0))
+            assert Fraction(ref[i, j]) == ex  # every term and partial sum is exact in fp64
+
+
+def test_mxfp4_equals_mxfp8_of_the_same_values():
+    M, N, K = 9, 7, 128
+    g = inp.generator(44)
+    a = inp.e2m1_codes(M, K, g)
+    b = inp.e2m1_codes(N, K, g)
+    sa = inp.e8m0_scales((M, K // 32), g)
+    sb = inp.e8m0_scales((N, K // 32), g)
+    r4, s4 = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), dtype=orc.E2M1)
+    r8, s8 = orc.gemm_mx(_e2m1_to_e4m3(inp.raw(a)), _e2m1_to_e4m3(inp.raw(b)), inp.raw(sa),
+                         inp.raw(sb))
+    assert _same(r4, r8) and _same(s4, s8)
+    ii, jj = np.array([0, 8, 4]), np.array([6, 0, 3])
+    re, se = orc.entries(orc.E2M1, inp.raw(a), inp.raw(b), ii, jj, sa=inp.raw(sa),
+                         sb=inp.raw(sb))
+    assert _same(re, r4[ii, jj]) and _same(se, s4[ii, jj])
 
 
 # ------------------------------------------------- identity / permutation
