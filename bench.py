@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s and % of MFMA dense peak (bf16 8192³; MXFP8 8192³)"
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}   # dense MFMA, MI355X
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.3}  # dense MFMA, MI355X
 HBM_GBS = 8000.0
 KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pingpong.h", "tcm_device.h", "tcm_internal.h", "gemm_tn.hip",
                   "gemm_mx.hip", "tcm_api.cpp"]
@@ -84,9 +84,10 @@ def prepare(name, torch, inp, tcm):
     w = inp.WORKLOADS[name]
     x = {k: v.to("cuda") for k, v in inp.make(w).items()}
     odt = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
-    if w.dtype == "e4m3":
+    if w.dtype in ("e4m3", "e2m1"):
         out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
-        fn = lambda: tcm.gemm_mx_fp8(x["A"], x["B"], x["SA"], x["SB"], out)
+        mx = tcm.gemm_mx_fp8 if w.dtype == "e4m3" else tcm.gemm_mx_fp4
+        fn = lambda: mx(x["A"], x["B"], x["SA"], x["SB"], out)
     elif w.batch > 1:
         out = torch.empty(w.batch, w.M, w.N, dtype=odt, device="cuda")
         fn = lambda: tcm.batched_gemm_tn(x["A"], x["B"], out)
@@ -165,7 +166,7 @@ def main() -> int:
     from tensor_core_matrix_amd import inputs as inp
 
     tcm.lib()
-    order = ["bf16_8192", "mxfp8_8192", "bf16_4096", "batched", "tile_f16"]
+    order = ["bf16_8192", "mxfp8_8192", "mxfp4_8192", "bf16_4096", "batched", "tile_f16"]
     if args.only:
         order = [args.only]
     results = {}
@@ -184,7 +185,8 @@ def main() -> int:
             "ms": ms, "tflops": tflops, "steps": steps,
             "frac_of_peak": tflops / PEAK_TFLOPS[w.dtype],
             "gbs": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes,
-            "plan": tcm.plan(w.M, w.N, w.K, batch=w.batch, mx=w.dtype == "e4m3",
+            "plan": tcm.plan(w.M, w.N, w.K, batch=w.batch,
+                             mx={"e4m3": 1, "e2m1": 2}.get(w.dtype, 0),
                              dtype=tcm.F16 if w.dtype == "f16" else tcm.BF16,
                              out_dtype=tcm.BF16 if w.out_dtype == "bf16" else tcm.F32,
                              num_cus=0),
@@ -215,7 +217,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if hw.dtype != "e4m3" else "e4m3",
+        "dtype": hw.dtype if hw.dtype in ("e4m3", "e2m1") else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{head}: M=N=K={hw.M} TN, {hw.dtype} in, fp32 accumulate, "
                                f"{hw.out_dtype} out, seed {hw.seed}",

@@ -73,7 +73,9 @@ typedef enum tcm_dtype {
     TCM_BF16 = 1, /* bfloat16 */
     TCM_F32 = 2,  /* IEEE binary32 */
     TCM_E4M3 = 3, /* OCP FP8 E4M3 ("FN": no infinities, max 448) */
-    TCM_E8M0 = 4  /* OCP E8M0 scale: 2^(e-127), 0xFF = NaN */
+    TCM_E8M0 = 4, /* OCP E8M0 scale: 2^(e-127), 0xFF = NaN */
+    TCM_E2M1 = 5  /* OCP FP4 E2M1, two per byte, element 2t in the low four bits of
+                     byte t (no infinities, no NaN, max 6) */
 } tcm_dtype;
 
 /*
@@ -111,6 +113,18 @@ tcm_status tcm_gemm_mx_fp8(const void* A, const void* B, const void* scale_A, co
                            void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
                            void* stream);
 
+/*
+ * MXFP4 block-scaled Out = (A * SA) . (B * SB)^T ("Hopper and Blackwell GEMM",
+ * Concept, "FP8 and FP4, with block scaling": the MXFP4 row of its format
+ * table, E2M1 elements with one E8M0 scale per 32).
+ *   A        M x K E2M1 elements stored M x (K/2) bytes (TCM_E2M1 packing)
+ *   B        N x K E2M1 elements stored N x (K/2) bytes
+ *   scale_A, scale_B, Out, K, errors: as tcm_gemm_mx_fp8.
+ */
+tcm_status tcm_gemm_mx_fp4(const void* A, const void* B, const void* scale_A, const void* scale_B,
+                           void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
+                           void* stream);
+
 /* What a call with these arguments would launch (host only: no HIP call when
  * num_cus > 0; num_cus == 0 asks the current device for its CU count). */
 typedef struct tcm_plan {
@@ -126,7 +140,7 @@ typedef struct tcm_plan {
     int32_t kernel;                 /* internal kernel variant id */
 } tcm_plan;
 
-/* mx != 0 plans tcm_gemm_mx_fp8 (dtype is then ignored). */
+/* mx == 1 plans tcm_gemm_mx_fp8, mx == 2 tcm_gemm_mx_fp4 (dtype is then ignored). */
 tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
                          tcm_dtype out_dtype, int mx, int num_cus, tcm_plan* plan);
 

@@ -8,6 +8,8 @@ kernels; there is no fallback.  If the library is missing, every call raises.
     gemm_tn(a, b, out=None, out_dtype=None)            a: M x K, b: N x K
     batched_gemm_tn(a, b, out=None, out_dtype=None)    a: B x M x K, b: B x N x K
     gemm_mx_fp8(a, b, scale_a, scale_b, out=None, out_dtype=torch.bfloat16)
+    gemm_mx_fp4(a, b, scale_a, scale_b, out=None, out_dtype=torch.bfloat16)
+                                                       a: M x K/2, b: N x K/2 E2M1 pairs
 """
 from __future__ import annotations
 
@@ -15,13 +17,13 @@ import ctypes
 import os
 import threading
 
-__all__ = ["gemm_tn", "batched_gemm_tn", "gemm_mx_fp8", "plan", "lib", "TcmError", "LIB_PATH",
-           "F16", "BF16", "F32", "E4M3", "E8M0"]
+__all__ = ["gemm_tn", "batched_gemm_tn", "gemm_mx_fp8", "gemm_mx_fp4", "plan", "lib", "TcmError",
+           "LIB_PATH", "F16", "BF16", "F32", "E4M3", "E8M0", "E2M1"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtcm.so")
 
 # tcm_dtype codes
-F16, BF16, F32, E4M3, E8M0 = 0, 1, 2, 3, 4
+F16, BF16, F32, E4M3, E8M0, E2M1 = 0, 1, 2, 3, 4, 5
 
 
 class TcmError(RuntimeError):
@@ -43,8 +45,8 @@ class Plan(ctypes.Structure):
 
 _lock = threading.Lock()
 _lib = None
-EXPORTS = ("tcm_gemm_tn", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8", "tcm_plan_gemm",
-           "tcm_status_string")
+EXPORTS = ("tcm_gemm_tn", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8", "tcm_gemm_mx_fp4",
+           "tcm_plan_gemm", "tcm_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -60,10 +62,12 @@ def lib() -> ctypes.CDLL:
             L.tcm_gemm_tn.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
             L.tcm_batched_gemm_tn.argtypes = [vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
             L.tcm_gemm_mx_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
+            L.tcm_gemm_mx_fp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_plan_gemm.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(Plan)]
             L.tcm_status_string.argtypes = [ci]
             L.tcm_status_string.restype = ctypes.c_char_p
-            for f in ("tcm_gemm_tn", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8", "tcm_plan_gemm"):
+            for f in ("tcm_gemm_tn", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8", "tcm_gemm_mx_fp4",
+                      "tcm_plan_gemm"):
                 getattr(L, f).restype = ci
             _lib = L
     return _lib
@@ -167,8 +171,37 @@ def gemm_mx_fp8(a, b, scale_a, scale_b, out=None, out_dtype=None):
     return out
 
 
+def gemm_mx_fp4(a, b, scale_a, scale_b, out=None, out_dtype=None):
+    """MXFP4 Out = (a * scale_a) . (b * scale_b)^T.  a (M, K/2), b (N, K/2) uint8
+    holding two E2M1 elements each (element 2t in the low four bits of byte t);
+    scale_a (M, K/32), scale_b (N, K/32) E8M0 bytes."""
+    torch = _torch()
+    M, KH = a.shape
+    N = b.shape[0]
+    K = 2 * KH
+    if b.shape[1] != KH:
+        raise ValueError("K mismatch")
+    if K % 32 or tuple(scale_a.shape) != (M, K // 32) or tuple(scale_b.shape) != (N, K // 32):
+        raise ValueError("scale tensors must be (rows, K/32) with K a multiple of 32")
+    for t in (a, b):
+        if t.dtype != torch.uint8:
+            raise TypeError("MXFP4 elements must be uint8 pairs")
+    for t in (scale_a, scale_b):
+        if t.dtype not in (torch.uint8, torch.float8_e8m0fnu):
+            raise TypeError("MX scales must be uint8 or float8_e8m0fnu")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be {(M, N)}")
+    with torch.cuda.device(a.device):
+        _check(lib().tcm_gemm_mx_fp4(_ptr(a), _ptr(b), _ptr(scale_a), _ptr(scale_b), _ptr(out),
+                                     M, N, K, _code(out.dtype), _stream(a)))
+    return out
+
+
 def plan(M, N, K, dtype=BF16, out_dtype=BF16, batch=1, mx=False, num_cus=256) -> dict:
-    """The launch a call would make (tile, ring depth, LDS bytes, grid)."""
+    """The launch a call would make (tile, ring depth, LDS bytes, grid).  mx:
+    False (or 0) plain, True (or 1) MXFP8, 2 MXFP4."""
     p = Plan()
     _check(lib().tcm_plan_gemm(batch, M, N, K, dtype, out_dtype, int(mx), num_cus,
                                ctypes.byref(p)))

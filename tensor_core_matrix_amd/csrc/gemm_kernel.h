@@ -44,6 +44,7 @@ namespace tcm {
 // ---------------------------------------------------------------------------
 struct OpBF16 {
     static constexpr int kElemBytes = 2;
+    static constexpr int kElemBits = 16;
     static constexpr int kK = 16;  // K per MFMA
     static constexpr bool kScaled = false;
     typedef bf16x8_t frag_t;
@@ -54,6 +55,7 @@ struct OpBF16 {
 
 struct OpF16 {
     static constexpr int kElemBytes = 2;
+    static constexpr int kElemBits = 16;
     static constexpr int kK = 16;
     static constexpr bool kScaled = false;
     typedef f16x8_t frag_t;
@@ -69,6 +71,7 @@ struct OpF16 {
 // 32-bit scale register.
 struct OpMXFP8 {
     static constexpr int kElemBytes = 1;
+    static constexpr int kElemBits = 8;
     static constexpr int kK = 64;
     static constexpr bool kScaled = true;
     typedef i32x8_t frag_t;
@@ -76,6 +79,28 @@ struct OpMXFP8 {
     __device__ static __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c, int sa, int sb) {
         // format codes 0 / 0: both operands FP8 E4M3
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
+    }
+};
+
+// MXFP4: E2M1 x E2M1, two elements per byte (element 2t in the low four
+// bits of byte t), one E8M0 scale per 32 K values.  The scaled MFMA reads the
+// first four registers of each operand, and (unlike FP8) lane l + 32 b holds
+// the whole block b of row l % 32: 32 K values in 16 bytes, together with
+// that block's scale.  Established on the device by feeding one nonzero
+// element per lane with block scales 1 and 2: every nibble of lanes 0..31
+// took scale 1, every nibble of lanes 32..63 scale 2.
+struct OpMXFP4 {
+    static constexpr int kElemBytes = 0;  // two elements per byte
+    static constexpr int kElemBits = 4;
+    static constexpr int kK = 64;
+    static constexpr bool kScaled = true;
+    typedef i32x4_t frag_t;
+    template <int SEL>
+    __device__ static __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c, int sa, int sb) {
+        const i32x8_t a8 = __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
+        const i32x8_t b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, -1, -1, -1, -1);
+        // format codes 4 / 4: both operands FP4 E2M1
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, SEL, sa, SEL, sb);
     }
 };
 
@@ -107,8 +132,11 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert(KSTEPS % 2 == 0, "fragment double buffer alternates per K step");
     static_assert(((4 * ROWS_PER_WAVE_COPY) >> SWZ) % CPR == 0, "copy chunk independent of i");
     static_assert((S - 1) * LOADS < 64, "vmcnt range");
-    static_assert(NSPLIT >= 1 && NSPLIT <= KSTEPS && LOADS % NSPLIT == 0, "copy split");
-    constexpr int PART = LOADS / NSPLIT;  // copies per part
+    static_assert(NSPLIT >= 1 && NSPLIT <= KSTEPS && NSPLIT <= LOADS, "copy split");
+    // Part p of a slice's copies: copies part_base(p) .. part_base(p + 1) - 1.
+    auto part_base = [](int p) { return p * LOADS / NSPLIT; };
+    constexpr int PART = LOADS / NSPLIT;                 // copies in part 0
+    constexpr int PMAX = (LOADS + NSPLIT - 1) / NSPLIT;  // largest part
     static_assert(CPR == 4 || CPR == 8, "row slice must be 64 or 128 bytes");
     static_assert(A_BYTES % (kThreads * 16) == 0 && B_BYTES % (kThreads * 16) == 0, "copy split");
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
@@ -116,6 +144,7 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert((32 >> SWZ) % CPR == 0, "swizzle must depend on the row within 32 only");
     static_assert(!Op::kScaled || (BK == 128 && S == 2), "MX path: 128-deep slices, 2 stages");
     static_assert(!VG || (!Op::kScaled && S == 2), "register-staged copies: plain types, 2 stages");
+    static_assert(Op::kElemBits >= 8, "whole-byte elements");
 
     // Epilogue staging: one 32-row block of a wave's output at a time, in a
     // wave-private LDS area after the ring.
@@ -415,20 +444,21 @@ void tiled_gemm_kernel(GemmArgs p) {
     // MFMA is ready when the matrix core frees up.
     constexpr int N_MFMA = FM * FN;
     constexpr int N_FRAG = FM + FN;
+    // `nc` copies ride in the step (at most PMAX; a constant once the K-step
+    // loop is unrolled).
     auto kstep = [&](int buf, int s, const char* rd_st, int rd_s, int copy_st, int copy_base,
-                     auto NCOPY, auto ZERO) {
-        constexpr int NC = decltype(NCOPY)::value;
-        constexpr int NX = N_MFMA > N_FRAG ? (N_MFMA > NC ? N_MFMA : NC)
-                                           : (N_FRAG > NC ? N_FRAG : NC);
+                     int nc, auto ZERO) {
+        constexpr int NM = N_MFMA > N_FRAG ? N_MFMA : N_FRAG;
+        constexpr int NX = NM > PMAX ? NM : PMAX;
         // Copies go out after every second MFMA where the step has room for
         // that (fewer back-to-back copies in the address FIFOs; measured
         // better than back-to-back and than every fourth), the reads of the
         // next step's fragments after the first MFMAs.
-        constexpr int CS = NC > 0 && 2 * NC <= N_MFMA ? 2 : 1;
+        constexpr int CS = 2 * PMAX <= N_MFMA ? 2 : 1;
 #pragma unroll
         for (int x = 0; x < NX; ++x) {
             if (x < N_MFMA) mma_one(buf, s, x, ZERO);
-            if (x % CS == 0 && x / CS < NC) copy_one(copy_st, copy_base + x / CS);
+            if (x % CS == 0 && x / CS < nc) copy_one(copy_st, copy_base + x / CS);
             if (x < N_FRAG) read_one(buf ^ 1, rd_st, rd_s, x);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -506,8 +536,7 @@ void tiled_gemm_kernel(GemmArgs p) {
             if (g + 1 < total) load_scales(nc, nx_a, nx_b);
         }
         __builtin_amdgcn_sched_barrier(0);
-        constexpr auto NONE = std::integral_constant<int, 0>{};
-        constexpr auto ONE_PART = std::integral_constant<int, PART>{};
+        constexpr int NONE = 0;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             const int cur = s & 1;
@@ -517,9 +546,11 @@ void tiled_gemm_kernel(GemmArgs p) {
                     // a later part of slice g - 1 + S, into stage (g - 1) % S
                     const int cst = (g + S - 1) % S;
                     if (zero)
-                        kstep(cur, s, st, s + 1, cst, (s + 1) * PART, ONE_PART, std::true_type{});
+                        kstep(cur, s, st, s + 1, cst, part_base(s + 1),
+                              part_base(s + 2) - part_base(s + 1), std::true_type{});
                     else
-                        kstep(cur, s, st, s + 1, cst, (s + 1) * PART, ONE_PART, std::false_type{});
+                        kstep(cur, s, st, s + 1, cst, part_base(s + 1),
+                              part_base(s + 2) - part_base(s + 1), std::false_type{});
                     if (s + 2 == NSPLIT) feed_next();
                 } else {
                     if (zero)
@@ -540,9 +571,9 @@ void tiled_gemm_kernel(GemmArgs p) {
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
                 if (zero)
-                    kstep(cur, s, st_next, 0, g % S, 0, ONE_PART, std::true_type{});
+                    kstep(cur, s, st_next, 0, g % S, 0, PART, std::true_type{});
                 else
-                    kstep(cur, s, st_next, 0, g % S, 0, ONE_PART, std::false_type{});
+                    kstep(cur, s, st_next, 0, g % S, 0, PART, std::false_type{});
             }
         }
         if constexpr (NSPLIT == 1) feed_next();

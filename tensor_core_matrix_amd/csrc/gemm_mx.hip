@@ -17,10 +17,10 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename TOut, int MODE, int UNIT_K, int S, bool CM = false>
+template <typename TOut, int MODE, int UNIT_K, int S, bool CM = false, class Op = OpMXFP8>
 static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, UNIT_K, S, MODE, CM && MODE != 1>), dim3(grid),
-                       dim3(kPPThreads), 0, st, a);
+    hipLaunchKernelGGL((pingpong_gemm_kernel<Op, TOut, UNIT_K, S, MODE, CM && MODE != 1>),
+                       dim3(grid), dim3(kPPThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -36,6 +36,7 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_MXPP256: return launch_pp<TOut, MODE, 128, 2>(a, grid, st);
     case V_MXPP256_K64S4: return launch_pp<TOut, MODE, 64, 4>(a, grid, st);
     case V_MXPP256_K64S4_CM: return launch_pp<TOut, MODE, 64, 4, true>(a, grid, st);
+    case V_MX4PP256: return launch_pp<TOut, MODE, 128, 4, false, OpMXFP4>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

@@ -50,9 +50,9 @@ template <class Op, typename TOut, int UNIT_K, int S, int SCALE_MODE = 0, bool C
 __global__ __launch_bounds__(kPPThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256;
-    constexpr int ESZ = Op::kElemBytes;
+    constexpr int EBITS = Op::kElemBits;
     constexpr int BK = UNIT_K;
-    constexpr int RB = BK * ESZ;        // bytes of one operand row's K unit
+    constexpr int RB = BK * EBITS / 8;  // bytes of one operand row's K unit
     constexpr int CPR = RB / 16;        // 16-byte chunks per row
     // chunk ^= row bits chosen so that the 16 rows read together by 16 lanes
     // fall on 16 different 16-byte bank groups (64 banks of 4 bytes)
@@ -75,7 +75,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int SC_CHUNK_TOTAL = SC_CHUNK ? 2 * CHUNK_BYTES : 0;
     constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32;
     constexpr int KSTEPS = BK / Op::kK;
-    constexpr int CPL = Op::kK * ESZ / 32;
+    constexpr int CPL = Op::kK * EBITS / 8 / 32;  // 16-byte chunks per lane per MFMA (>= 8 bits)
     // copies: 1 KiB per wave instruction; shared by both groups when S >= 3
     // With two stages group 1's share would have to land within the half it
     // is issued in (measured: far slower), so group 0 copies alone.
@@ -103,7 +103,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
                   "copies in MFMA halves: shared copies, no per-stage scale words");
     static_assert(!(SC_LDS || SC_CHUNK) || NCW == 8,
                   "one scale DMA per wave: 4 x 64 A rows, 4 x 64 B rows");
-    static_assert(!SC_CHUNK || UPC == 8, "a chunk lands two halves after its DMA; 64-deep units");
+    static_assert(!SC_CHUNK || UPC * KSTEPS == 8, "8 packed scale bytes per lane per chunk");
+    static_assert(!SC_CHUNK || UPC >= 2, "a chunk lands two halves after its DMA");
     static_assert((32 >> SWZ) % CPR == 0, "swizzle depends on the row within 32 only");
 
     __shared__ __attribute__((aligned(1024))) char lds[RING + 8 * STG_BYTES];
@@ -120,6 +121,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
     const int my_tiles = (p.total_tiles - 1 - lid) / G + 1;
     const int T = my_tiles * p.ksteps;  // K units of this workgroup
     const int K = p.K;
+    const uint32_t ROWB = (uint32_t)K * EBITS / 8;  // bytes of a whole operand row
 
     auto locate = [&](TileCursor& c) { tile_coords(p, c.tl * G + lid, c.batch, c.tm, c.tn); };
     auto advance = [&](TileCursor& c) {
@@ -143,12 +145,12 @@ void pingpong_gemm_kernel(GemmArgs p) {
     const int cp_row = lane / CPR;
     const int sw_row = cw * RPC + cp_row;  // congruent to every copied row of the lane
     const int cp_chunk = (lane % CPR) ^ ((sw_row >> SWZ) & (CPR - 1));
-    const uint32_t cp_lane_off = (uint32_t)cp_row * (uint32_t)K * ESZ + cp_chunk * 16;
-    const int cp_k = cp_chunk * (16 / ESZ);  // first K element of the lane's chunk
+    const uint32_t cp_lane_off = (uint32_t)cp_row * ROWB + cp_chunk * 16;
+    const int cp_k = cp_chunk * (128 / EBITS);  // first K element of the lane's chunk
     auto copy_row_off = [&](int t) -> uint32_t {
         const int q = cw + t * NCW;
         const int qq = q < A_COPIES ? q : q - A_COPIES;
-        return (uint32_t)(qq * RPC) * (uint32_t)K * ESZ;
+        return (uint32_t)(qq * RPC) * ROWB;
     };
     TileCursor fc = {0, 0, 0, 0, 0};
     __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
@@ -157,10 +159,10 @@ void pingpong_gemm_kernel(GemmArgs p) {
     auto feed_resources = [&]() {
         const int rows_a = min(BM, p.M - fc.tm * BM);
         const int rows_b = min(BN, p.N - fc.tn * BN);
-        const char* abase = (const char*)p.A + fc.batch * p.stride_a + (int64_t)fc.tm * BM * K * ESZ;
-        const char* bbase = (const char*)p.B + fc.batch * p.stride_b + (int64_t)fc.tn * BN * K * ESZ;
-        ra = make_rsrc(abase, (uint32_t)rows_a * (uint32_t)K * ESZ);
-        rb = make_rsrc(bbase, (uint32_t)rows_b * (uint32_t)K * ESZ);
+        const char* abase = (const char*)p.A + fc.batch * p.stride_a + (int64_t)fc.tm * BM * ROWB;
+        const char* bbase = (const char*)p.B + fc.batch * p.stride_b + (int64_t)fc.tn * BN * ROWB;
+        ra = make_rsrc(abase, (uint32_t)rows_a * ROWB);
+        rb = make_rsrc(bbase, (uint32_t)rows_b * ROWB);
         if constexpr (SC_LDS) {
             const uint8_t* sab = (const uint8_t*)p.SA + (int64_t)fc.tm * BM * kblocks;
             const uint8_t* sbb = (const uint8_t*)p.SB + (int64_t)fc.tn * BN * kblocks;
@@ -206,7 +208,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // for pieces past K.
     auto copy_base = [&]() -> uint32_t {
         const int k0 = fc.kk * BK;
-        return (fu < T && k0 + cp_k < K) ? cp_lane_off + (uint32_t)k0 * ESZ : kOutOfRange;
+        return (fu < T && k0 + cp_k < K) ? cp_lane_off + (uint32_t)k0 * EBITS / 8 : kOutOfRange;
     };
     auto issue_one = [&](int t, uint32_t base) {
         const int q = cw + t * NCW;
@@ -246,7 +248,11 @@ void pingpong_gemm_kernel(GemmArgs p) {
     frag_t fa[KSTEPS][FM], fb[KSTEPS][FN];
     auto read_frag = [&](const char* base, int s) -> frag_t {
         frag_t f;
-        if constexpr (CPL == 1) {
+        if constexpr (EBITS == 4) {
+            // MXFP4: half-wave hi holds block hi of the MFMA's 64 K values,
+            // the 16-byte chunk 2s + hi of the row
+            f = *(const frag_t*)(base + (((2 * s + hi) ^ xr) * 16));
+        } else if constexpr (CPL == 1) {
             f = *(const frag_t*)(base + (((2 * s + hi) ^ xr) * 16));
         } else {
             // scaled MFMA: block 0 of the 64 K values in bytes 0..15 of both
@@ -275,7 +281,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
     uint64_t pk[SC_CHUNK ? FM + FN : 1];
     auto load_scales = [&](const TileCursor& c, int u) {
         if constexpr (SC_CHUNK) {
-            const int k = u % UPC;
+            const int k = u % UPC;  // unit within the chunk
             if (k == 0) {
                 // first unit of a chunk: one 16-byte read per fragment row
                 // (16 consecutive rows per 16 lanes: no bank conflicts), bytes
@@ -295,7 +301,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
             }
 #pragma unroll
             for (int f = 0; f < FM + FN; ++f) {
-                const int v = (int)(uint32_t)(pk[f] >> (8 * k));
+                // byte s of v serves K step s
+                const int v = (int)(uint32_t)(pk[f] >> (8 * KSTEPS * k));
                 if (f < FM) sc_a[f] = v; else sc_b[f - FM] = v;
             }
         } else if constexpr (SC_LDS) {
@@ -360,10 +367,13 @@ void pingpong_gemm_kernel(GemmArgs p) {
                         c = acc[i][j];
                     }
                     if constexpr (Op::kScaled) {
+                        // the second K step's scale: byte 1 of a packed chunk
+                        // value, byte 2 of the other forms
+                        constexpr int SEL1 = SC_CHUNK ? 1 : 2;
                         if (s == 0)
                             acc[i][j] = Op::template mma<0>(fb[s][j], fa[s][i], c, sc_b[j], sc_a[i]);
                         else
-                            acc[i][j] = Op::template mma<2>(fb[s][j], fa[s][i], c, sc_b[j], sc_a[i]);
+                            acc[i][j] = Op::template mma<SEL1>(fb[s][j], fa[s][i], c, sc_b[j], sc_a[i]);
                     } else {
                         acc[i][j] = Op::mma(fb[s][j], fa[s][i], c);
                     }

@@ -49,6 +49,7 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_T256x256_K32S5: return launch_one<Op, TOut, 256, 256, 32, 5, 1, 2>(a, grid, st);
     case V_T256x256_SPLIT2: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 2>(a, grid, st);
     case V_T256x256_SPLIT4: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 4>(a, grid, st);
+    case V_T256x256_SPLIT3: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 3>(a, grid, st);
     case V_T256x256_VG2: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 2, true, true>(a, grid, st);
     case V_T256x256_VG4: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 4, true, true>(a, grid, st);
     case V_PP256: return launch_pp<Op, TOut, 64, 2>(a, grid, st);

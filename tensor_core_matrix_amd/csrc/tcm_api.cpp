@@ -17,25 +17,27 @@ namespace tcm {
 
 VariantInfo variant_info(int32_t v) {
     switch (v) {
-    case V_T256x256: return {256, 256, 64, 2, 1, 2, kThreads};
-    case V_T128x256: return {128, 256, 64, 2, 1, 2, kThreads};
-    case V_T128x128: return {128, 128, 64, 2, 2, 2, kThreads};
-    case V_T128x64: return {128, 64, 64, 2, 3, 2, kThreads};
-    case V_T256x256_K32S4: return {256, 256, 32, 4, 1, 2, kThreads};
-    case V_T256x256_K32S5: return {256, 256, 32, 5, 1, 2, kThreads};
-    case V_T256x256_SPLIT2: return {256, 256, 64, 2, 1, 2, kThreads};
-    case V_T256x256_SPLIT4: return {256, 256, 64, 2, 1, 2, kThreads};
-    case V_MX256x256: return {256, 256, 128, 2, 1, 1, kThreads};
-    case V_MX128x128: return {128, 128, 128, 2, 1, 1, kThreads};
-    case V_MX256x256_SPLIT2: return {256, 256, 128, 2, 1, 1, kThreads};
-    case V_PP256: return {256, 256, 64, 2, 1, 2, 512};
-    case V_PP256_K32S4: return {256, 256, 32, 4, 1, 2, 512};
-    case V_PP256_K32S4_CM: return {256, 256, 32, 4, 1, 2, 512};
-    case V_T256x256_VG2: return {256, 256, 64, 2, 1, 2, kThreads};
-    case V_T256x256_VG4: return {256, 256, 64, 2, 1, 2, kThreads};
-    case V_MXPP256: return {256, 256, 128, 2, 1, 1, 512};
-    case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 1, 512};
-    case V_MXPP256_K64S4_CM: return {256, 256, 64, 4, 1, 1, 512};
+    case V_T256x256: return {256, 256, 64, 2, 1, 16, kThreads};
+    case V_T128x256: return {128, 256, 64, 2, 1, 16, kThreads};
+    case V_T128x128: return {128, 128, 64, 2, 2, 16, kThreads};
+    case V_T128x64: return {128, 64, 64, 2, 3, 16, kThreads};
+    case V_T256x256_K32S4: return {256, 256, 32, 4, 1, 16, kThreads};
+    case V_T256x256_K32S5: return {256, 256, 32, 5, 1, 16, kThreads};
+    case V_T256x256_SPLIT2: return {256, 256, 64, 2, 1, 16, kThreads};
+    case V_T256x256_SPLIT4: return {256, 256, 64, 2, 1, 16, kThreads};
+    case V_MX256x256: return {256, 256, 128, 2, 1, 8, kThreads};
+    case V_MX128x128: return {128, 128, 128, 2, 1, 8, kThreads};
+    case V_MX256x256_SPLIT2: return {256, 256, 128, 2, 1, 8, kThreads};
+    case V_PP256: return {256, 256, 64, 2, 1, 16, 512};
+    case V_PP256_K32S4: return {256, 256, 32, 4, 1, 16, 512};
+    case V_PP256_K32S4_CM: return {256, 256, 32, 4, 1, 16, 512};
+    case V_T256x256_VG2: return {256, 256, 64, 2, 1, 16, kThreads};
+    case V_T256x256_SPLIT3: return {256, 256, 64, 2, 1, 16, kThreads};
+    case V_T256x256_VG4: return {256, 256, 64, 2, 1, 16, kThreads};
+    case V_MXPP256: return {256, 256, 128, 2, 1, 8, 512};
+    case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 8, 512};
+    case V_MXPP256_K64S4_CM: return {256, 256, 64, 4, 1, 8, 512};
+    case V_MX4PP256: return {256, 256, 128, 4, 1, 4, 512};
     }
     return {0, 0, 0, 0, 0, 0, kThreads};
 }
@@ -134,13 +136,15 @@ int64_t max_grid() {
 
 // Tile choice: the largest tile whose tile count still gives every CU at
 // least one tile with little padding; small problems take the smallest tile.
-int32_t choose_variant(int64_t batch, int64_t M, int64_t N, bool mx, int cus) {
+// Families by element bits: 16 (f16/bf16), 8 (MXFP8), 4 (MXFP4).
+int32_t choose_variant(int64_t batch, int64_t M, int64_t N, int32_t bits, int cus) {
     const int32_t f = forced_variant();
-    if (f >= 0 && variant_info(f).tile_m > 0 && (variant_info(f).elem_bytes == 1) == mx) return f;
-    static const int32_t plain[] = {V_T256x256_SPLIT2, V_T128x256, V_T128x128, V_T128x64};
+    if (f >= 0 && variant_info(f).tile_m > 0 && variant_info(f).elem_bits == bits) return f;
+    static const int32_t plain[] = {V_T256x256_SPLIT3, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MXPP256_K64S4, V_MX128x128};
-    const int32_t* cand = mx ? mxv : plain;
-    const int n = mx ? 2 : 4;
+    static const int32_t mx4[] = {V_MX4PP256};
+    const int32_t* cand = bits == 8 ? mxv : bits == 4 ? mx4 : plain;
+    const int n = bits == 8 ? 2 : bits == 4 ? 1 : 4;
     for (int i = 0; i < n; ++i) {
         VariantInfo vi = variant_info(cand[i]);
         int64_t tiles = batch * cdiv(M, vi.tile_m) * cdiv(N, vi.tile_n);
@@ -150,9 +154,9 @@ int32_t choose_variant(int64_t batch, int64_t M, int64_t N, bool mx, int cus) {
     return cand[n - 1];
 }
 
-tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool mx, int cus,
+tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t bits, int cus,
                      tcm_plan* plan, GemmArgs* args) {
-    int32_t v = choose_variant(batch, M, N, mx, cus);
+    int32_t v = choose_variant(batch, M, N, bits, cus);
     VariantInfo vi = variant_info(v);
     int64_t tm = cdiv(M, vi.tile_m), tn = cdiv(N, vi.tile_n);
     int64_t tiles = batch * tm * tn;
@@ -160,7 +164,7 @@ tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, bool mx, in
     int64_t grid = tiles < slots ? tiles : slots;
     const int64_t cap = max_grid();
     if (grid > cap) grid = cap;
-    int32_t stage = (vi.tile_m + vi.tile_n) * vi.tile_k * vi.elem_bytes;
+    int32_t stage = (vi.tile_m + vi.tile_n) * vi.tile_k * vi.elem_bits / 8;
     if (plan) {
         plan->tile_m = vi.tile_m;
         plan->tile_n = vi.tile_n;
@@ -208,7 +212,7 @@ tcm_status run_plain(const void* A, const void* B, void* Out, int64_t batch, int
     if ((s = device_info(&dev)) != TCM_OK) return s;
     tcm_plan plan;
     GemmArgs a;
-    make_plan(batch, M, N, K, false, dev.cus, &plan, &a);
+    make_plan(batch, M, N, K, 16, dev.cus, &plan, &a);
     a.A = A;
     a.B = B;
     a.C = Out;
@@ -235,9 +239,14 @@ tcm_status tcm_batched_gemm_tn(const void* A, const void* B, void* Out, int64_t 
     return run_plain(A, B, Out, batch, M, N, K, dtype, out_dtype, stream);
 }
 
-tcm_status tcm_gemm_mx_fp8(const void* A, const void* B, const void* scale_A, const void* scale_B,
-                           void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The MX entry points: elements of `bits` bits (8 = E4M3, 4 = E2M1 pairs).
+tcm_status run_mx(int32_t bits, const void* A, const void* B, const void* scale_A,
+                  const void* scale_B, void* Out, int64_t M, int64_t N, int64_t K,
+                  tcm_dtype out_dtype, void* stream) {
     if (!(out_dtype == TCM_F32 || out_dtype == TCM_BF16)) return TCM_ERR_UNSUPPORTED_DTYPE;
     bool empty = false;
     tcm_status s = check_sizes(1, M, N, K, &empty);
@@ -245,20 +254,21 @@ tcm_status tcm_gemm_mx_fp8(const void* A, const void* B, const void* scale_A, co
     if (!Out || (K > 0 && (!A || !B || !scale_A || !scale_B))) return TCM_ERR_NULL_POINTER;
     if ((s = check_range(1, M, N, K)) != TCM_OK) return s;
     if (K % 32 != 0) return TCM_ERR_UNSUPPORTED_SHAPE;
-    if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) || K % 16 != 0)
+    // rows of K * bits / 8 bytes (K % 32 == 0 makes them whole 16-byte pieces)
+    if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) || (K * bits / 8) % 16 != 0)
         return TCM_ERR_MISALIGNED;
     DeviceInfo dev;
     if ((s = device_info(&dev)) != TCM_OK) return s;
     tcm_plan plan;
     GemmArgs a;
-    make_plan(1, M, N, K, true, dev.cus, &plan, &a);
+    make_plan(1, M, N, K, bits, dev.cus, &plan, &a);
     a.A = A;
     a.B = B;
     a.SA = scale_A;
     a.SB = scale_B;
     a.C = Out;
-    a.stride_a = M * K;
-    a.stride_b = N * K;
+    a.stride_a = M * K * bits / 8;
+    a.stride_b = N * K * bits / 8;
     a.stride_c = M * N * elem_bytes(out_dtype);
     // Wide scale reads need every row's K/32 bytes to be whole words (16-byte
     // pieces) and the arrays aligned to match.
@@ -271,6 +281,22 @@ tcm_status tcm_gemm_mx_fp8(const void* A, const void* B, const void* scale_A, co
     hipError_t e = launch_gemm_mx(plan.kernel, (int32_t)out_dtype, scale_mode, a, plan.grid,
                                   (hipStream_t)stream);
     return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+tcm_status tcm_gemm_mx_fp8(const void* A, const void* B, const void* scale_A, const void* scale_B,
+                           void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
+                           void* stream) {
+    return run_mx(8, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream);
+}
+
+tcm_status tcm_gemm_mx_fp4(const void* A, const void* B, const void* scale_A, const void* scale_B,
+                           void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
+                           void* stream) {
+    return run_mx(4, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream);
 }
 
 tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
@@ -288,8 +314,8 @@ tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dty
         if ((s = device_info(&dev)) != TCM_OK) return s;
         num_cus = dev.cus;
     }
-    make_plan(batch < 1 ? 1 : batch, M < 1 ? 1 : M, N < 1 ? 1 : N, K, mx != 0, num_cus, plan,
-              nullptr);
+    make_plan(batch < 1 ? 1 : batch, M < 1 ? 1 : M, N < 1 ? 1 : N, K,
+              mx == 2 ? 4 : mx ? 8 : 16, num_cus, plan, nullptr);
     if (empty) {
         plan->grid = 0;
         plan->tiles = 0;

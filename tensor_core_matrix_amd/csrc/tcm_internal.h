@@ -42,6 +42,8 @@ enum Variant : int32_t {
     V_PP256_K32S4_CM = 16, // variant 9 with the copies issued between the MFMAs
     V_T256x256_VG2 = 17,   // variant 6 with register-staged copies (loads + ds_write)
     V_T256x256_VG4 = 18,   // variant 7 with register-staged copies
+    V_T256x256_SPLIT3 = 19, // 256x256x64, 2-stage ring, copies split over 3 K steps (5/5/6)
+    V_MX4PP256 = 20,        // MXFP4 256x256x128 ping-pong, 4-stage ring
     V_MX256x256 = 10, // MXFP8 256x256x128, 2-stage ring
     V_MX128x128 = 11, // MXFP8 128x128x128, 2-stage ring
     V_MX256x256_SPLIT2 = 12, // MXFP8 256x256x128, copies split over 2 K steps
@@ -52,7 +54,7 @@ enum Variant : int32_t {
 
 struct VariantInfo {
     int32_t tile_m, tile_n, tile_k, stages, occupancy;
-    int32_t elem_bytes;
+    int32_t elem_bits;  // 16 f16/bf16, 8 MXFP8, 4 MXFP4
     int32_t threads;
 };
 

@@ -43,6 +43,7 @@ def test_dtype_pairs_rejected():
                     (tcm.BF16, tcm.E4M3), (7, tcm.F32)]:
         assert call_plain(dt=dt, odt=odt) == UNSUP_DTYPE
     assert tcm.lib().tcm_gemm_mx_fp8(A, B, SA, SB, C, 64, 64, 64, tcm.F16, None) == UNSUP_DTYPE
+    assert tcm.lib().tcm_gemm_mx_fp4(A, B, SA, SB, C, 64, 64, 64, tcm.E4M3, None) == UNSUP_DTYPE
 
 
 def test_shapes_rejected():
@@ -54,6 +55,8 @@ def test_shapes_rejected():
     L = tcm.lib()
     assert L.tcm_batched_gemm_tn(A, B, C, -2, 8, 8, 8, tcm.BF16, tcm.F32, None) == BADSHAPE
     assert L.tcm_gemm_mx_fp8(A, B, SA, SB, C, 64, 64, 48, tcm.BF16, None) == UNSUP_SHAPE
+    assert L.tcm_gemm_mx_fp4(A, B, SA, SB, C, 64, 64, 48, tcm.BF16, None) == UNSUP_SHAPE
+    assert L.tcm_gemm_mx_fp4(A, B, SA, SB, C, -64, 64, 64, tcm.BF16, None) == BADSHAPE
 
 
 def test_empty_calls_are_no_ops():
@@ -71,6 +74,8 @@ def test_null_pointers_rejected():
     L = tcm.lib()
     assert L.tcm_gemm_mx_fp8(A, B, None, SB, C, 64, 64, 64, tcm.BF16, None) == NULLP
     assert L.tcm_gemm_mx_fp8(A, B, SA, None, C, 64, 64, 64, tcm.BF16, None) == NULLP
+    assert L.tcm_gemm_mx_fp4(None, B, SA, SB, C, 64, 64, 64, tcm.BF16, None) == NULLP
+    assert L.tcm_gemm_mx_fp4(A, B, SA, SB, None, 64, 64, 64, tcm.BF16, None) == NULLP
 
 
 def test_alignment_rejected():
@@ -82,6 +87,8 @@ def test_alignment_rejected():
     assert L.tcm_gemm_mx_fp8(A + 1, B, SA, SB, C, 64, 64, 64, tcm.BF16, None) == MISALIGNED
     # scale tensors need no alignment: a valid call gets past validation
     assert L.tcm_gemm_mx_fp8(A, B, SA + 1, SB + 3, C, 64, 64, 64, tcm.BF16, None) in (OK, NO_DEVICE)
+    assert L.tcm_gemm_mx_fp4(A, B + 8, SA, SB, C, 64, 64, 64, tcm.BF16, None) == MISALIGNED
+    assert L.tcm_gemm_mx_fp4(A, B, SA, SB, C + 2, 64, 64, 64, tcm.F32, None) == MISALIGNED
 
 
 def test_valid_call_without_gpu_reports_no_device():
@@ -93,6 +100,7 @@ def test_valid_call_without_gpu_reports_no_device():
     if has_gpu:
         pytest.skip("a GPU is present")
     assert call_plain() == NO_DEVICE
+    assert tcm.lib().tcm_gemm_mx_fp4(A, B, SA, SB, C, 64, 64, 64, tcm.BF16, None) == NO_DEVICE
 
 
 def test_plan_stage_bytes_match_page():
@@ -119,5 +127,9 @@ def test_plans_of_the_workloads():
     p = tcm.plan(8192, 8192, 8192, mx=True)
     assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"]) == \
         (256, 64, 32 * 1024, 4, 512)
+    # MXFP4 8192^3: the same ring of four 32 KiB units, 128 E2M1 deep
+    p = tcm.plan(8192, 8192, 8192, mx=2)
+    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"]) == \
+        (256, 128, 32 * 1024, 4, 512)
     # empty problem plans nothing
     assert tcm.plan(0, 8, 8)["grid"] == 0

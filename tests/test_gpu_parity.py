@@ -297,7 +297,7 @@ def test_repeat_runs_bitwise_identical():
 
 
 # ------------------------------------------------------ every kernel variant
-PLAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 17, 18]
+PLAIN_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 17, 18, 19]
 MX_VARIANTS = [10, 11, 12, 13, 14, 15]
 
 
