@@ -301,6 +301,32 @@ int oracle_gemm_mx(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const 
 }
 
 /*
+ * Epilogue with a C input.  "API Card: Blackwell Pipeline (tcgen05)",
+ * "Device side.", lists an axpby(alpha, beta, out) accessor among the
+ * epilogue's operations, and "mma.sync", "Accumulation, transpose and
+ * alpha/beta", places alpha/beta scaling after the product at the call site.
+ * Read plainly (the BLAS axpby), with C the output's prior contents:
+ *
+ *   out[t] = alpha * ref[t] + beta * c(t)       fp64, exact up to one rounding
+ *
+ * where c(t) is the exact value of stored element t of C (format c_dtype,
+ * OR_F16, OR_BF16 or OR_F32).  C may be NULL when beta == 0.
+ */
+int oracle_axpby(int64_t n, double alpha, const double* ref, double beta, int c_dtype,
+                 const void* C, double* out) {
+    if (n < 0 || (n > 0 && (!ref || !out)) ||
+        (beta != 0.0 && (!C || !(c_dtype == OR_F16 || c_dtype == OR_BF16 || c_dtype == OR_F32))))
+        return -1;
+    for (int64_t t = 0; t < n; ++t) {
+        double v = alpha * ref[t];
+        if (beta != 0.0)
+            v += beta * dec_one(c_dtype, C, t);
+        out[t] = v;
+    }
+    return 0;
+}
+
+/*
  * Selected entries only, for problems too large to compute whole: entry t is
  * (row ii[t], column jj[t]) of problem bb[t] (bb may be NULL for batch 1).
  * SA/SB non-NULL selects the MX definition (dtype must then be OR_E4M3 or

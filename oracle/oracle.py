@@ -66,10 +66,12 @@ def _load():
             lib.oracle_gemm_mx.argtypes = [vp, vp, vp, vp, i64, i64, i64, dp, dp, ctypes.c_int]
             lib.oracle_gemm_mx_typed.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, dp,
                                                  dp, ctypes.c_int]
+            lib.oracle_axpby.argtypes = [i64, ctypes.c_double, dp, ctypes.c_double, ctypes.c_int,
+                                         vp, dp]
             lib.oracle_entries.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, vp, vp,
                                            vp, i64, dp, dp]
             for f in (lib.oracle_decode, lib.oracle_gemm_tn, lib.oracle_gemm_mx,
-                      lib.oracle_gemm_mx_typed, lib.oracle_entries):
+                      lib.oracle_gemm_mx_typed, lib.oracle_entries, lib.oracle_axpby):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -177,6 +179,22 @@ def entries(dtype: int, a: np.ndarray, b: np.ndarray, ii, jj, bb=None, sa=None, 
     return ref, s
 
 
+def axpby(alpha: float, ref: np.ndarray, beta: float = 0.0, c: np.ndarray | None = None,
+          c_dtype: int = F32) -> np.ndarray:
+    """alpha * ref + beta * C in fp64 (C given as raw storage of c_dtype, same
+    shape as ref; may be None when beta == 0)."""
+    ref = np.ascontiguousarray(ref, np.float64)
+    out = np.empty_like(ref)
+    cr = None if c is None else _raw(c, c_dtype)
+    if cr is not None and cr.shape != ref.shape:
+        raise ValueError("C shape must equal the output shape")
+    rc = _load().oracle_axpby(ref.size, float(alpha), _ptr(ref), float(beta), c_dtype,
+                              _ptr(cr), _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_axpby failed ({rc})")
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Comparison rule
 # ----------------------------------------------------------------------------
@@ -192,6 +210,45 @@ def ulp_bf16(x: np.ndarray) -> np.ndarray:
     nz = x > 0
     e[nz] = np.maximum(np.floor(np.log2(x[nz])), -126.0)
     return np.exp2(e - 7.0)
+
+
+def ulp_f16(x: np.ndarray) -> np.ndarray:
+    """Spacing of IEEE binary16 numbers at |x|: 2^(max(floor(log2|x|), -14) - 10)
+    (10 stored mantissa bits, smallest normal exponent -14, subnormal spacing
+    2^-24)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.full(x.shape, -14.0)
+    nz = x > 0
+    e[nz] = np.maximum(np.floor(np.log2(x[nz])), -14.0)
+    return np.exp2(e - 10.0)
+
+
+def bound_epi(exact: np.ndarray, alpha: float, abssum: np.ndarray, beta_c: np.ndarray,
+              out: str) -> np.ndarray:
+    """Acceptance bound of Out = alpha * (A B^T) + beta * C computed with fp32
+    sums and an fp32 combine: |alpha| * 1e-4 * abssum for the sum, 2^-22 of
+    |alpha * sum| + |beta * C| for the two fp32 roundings of the combine, plus
+    one ulp of the output format (bf16 or f16)."""
+    b = abs(alpha) * REL_TOL * np.asarray(abssum, np.float64)
+    b = b + 2.0 ** -22 * (np.abs(exact) + np.abs(np.asarray(beta_c, np.float64)))
+    if out == "bf16":
+        b = b + ulp_bf16(exact)
+    elif out == "f16":
+        b = b + ulp_f16(exact)
+    return b
+
+
+def check_epi(gpu, exact, alpha, abssum, beta_c, out: str):
+    """Elementwise acceptance of the epilogue form; (ok, worst err/bound, n bad)."""
+    gpu = np.asarray(gpu, np.float64)
+    bnd = bound_epi(exact, alpha, abssum, beta_c, out)
+    err = np.abs(gpu - np.asarray(exact, np.float64))
+    finite = np.isfinite(gpu)
+    bad = ~finite | (err > bnd)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bnd > 0, err / bnd, np.where(err > 0, np.inf, 0.0))
+    ratio = np.where(finite, ratio, np.inf)
+    return int(bad.sum()) == 0, float(ratio.max()) if ratio.size else 0.0, int(bad.sum())
 
 
 def bound(ref: np.ndarray, abssum: np.ndarray, out_bf16: bool) -> np.ndarray:

@@ -354,6 +354,61 @@ def test_planted_mistakes_fail_the_pins():
     assert not np.all(dropped == 64)
 
 
+# ----------------------------------------------------- axpby epilogue
+def test_axpby_pins():
+    g = inp.generator(45)
+    M, N, K = 5, 7, 24
+    a = inp.normal((M, K), g, 1.0, torch.bfloat16)
+    b = inp.normal((N, K), g, 1.0, torch.bfloat16)
+    ref, _ = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    # alpha = 1, beta = 0 is the product itself; C may be absent
+    assert _same(orc.axpby(1.0, ref), ref)
+    # power-of-two alpha scales exactly
+    assert _same(orc.axpby(-4.0, ref), -4.0 * ref)
+    for name, dt in (("f32", torch.float32), ("bf16", torch.bfloat16), ("f16", torch.float16)):
+        c = inp.normal((M, N), g, 3.0, dt)
+        cv = c.double().numpy()               # torch's own decode of C
+        got = orc.axpby(0.5, ref, -2.0, inp.raw(c), _dt_code(name))
+        # 0.5 * ref and -2 * c are exact; their fp64 sum rounds once
+        assert np.array_equal(got, 0.5 * ref + (-2.0) * cv)
+    # C = the product's own bf16 rounding: alpha + beta = 0 leaves only the
+    # rounding error, at most half a bf16 ulp of ref
+    cb = torch.from_numpy(ref).to(torch.bfloat16)
+    d = orc.axpby(1.0, ref, -1.0, inp.raw(cb), orc.BF16)
+    assert np.all(np.abs(d) <= 0.5 * orc.ulp_bf16(ref))
+    with pytest.raises(ValueError):
+        orc.axpby(1.0, ref, 1.0, None)
+
+
+def _dt_code(name):
+    return orc.DTYPE_NAMES[name]
+
+
+def test_ulp_f16_matches_bit_spacing():
+    g = inp.generator(46)
+    v = inp.normal((4096,), g, 100.0, torch.float16).abs()
+    v = v[(v > 0) & torch.isfinite(v) & (v < 60000)]
+    # the next representable value up: the bit pattern plus one
+    up = (v.view(torch.int16) + 1).view(torch.float16).double().numpy()
+    assert np.array_equal(up - v.double().numpy(), orc.ulp_f16(v.double().numpy()))
+    # subnormal spacing and the smallest normal
+    assert orc.ulp_f16(np.array([0.0]))[0] == 2.0 ** -24
+    assert orc.ulp_f16(np.array([2.0 ** -14]))[0] == 2.0 ** -24
+
+
+def test_check_epi_rule():
+    exact = np.array([1.0, 1000.0, -3.0])
+    ok, _, _ = orc.check_epi(exact + np.array([0.0, 0.5, 0.0]), exact, 1.0, np.zeros(3),
+                             np.zeros(3), "f16")
+    assert ok                                  # half an f16 ulp at 1000 (ulp 0.5)
+    ok, _, nbad = orc.check_epi(exact + np.array([0.0, 1.5, 0.0]), exact, 1.0, np.zeros(3),
+                                np.zeros(3), "f16")
+    assert not ok and nbad == 1
+    ok, _, _ = orc.check_epi(np.array([np.nan, 1000.0, -3.0]), exact, 1.0, np.ones(3),
+                             np.zeros(3), "f32")
+    assert not ok
+
+
 # ------------------------------------------------------- comparison rule
 def test_ulp_bf16_matches_bit_spacing():
     g = inp.generator(31)
