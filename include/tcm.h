@@ -100,6 +100,25 @@ tcm_status tcm_batched_gemm_tn(const void* A, const void* B, void* Out, int64_t 
                                void* stream);
 
 /*
+ * Out = alpha * (A . B^T) + beta * C for one problem: the epilogue with a C
+ * input ("API Card: Blackwell Pipeline (tcgen05)", "Device side.": the
+ * axpby(alpha, beta, out) accessor; "mma.sync", "Accumulation, transpose and
+ * alpha/beta": the scaling after the product, in a stated rounding order).
+ *   A, B     as tcm_gemm_tn (dtype TCM_F16 or TCM_BF16)
+ *   C        M x N elements of `c_dtype` (TCM_F16, TCM_BF16 or TCM_F32),
+ *            16-byte aligned; read only when beta != 0 (then non-NULL)
+ *   Out      M x N of `out_dtype` (TCM_F16, TCM_BF16 or TCM_F32), overwritten
+ * The product is summed in fp32, combined as alpha * sum + beta * c in fp32,
+ * and rounded once to out_dtype (round to nearest even; fp16 overflows to
+ * infinity).  C may be Out itself (same pointer and dtype): every element is
+ * read before it is written, by the same thread.  Partly overlapping C and
+ * Out are not allowed.
+ */
+tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out, int64_t M,
+                          int64_t N, int64_t K, tcm_dtype dtype, tcm_dtype c_dtype,
+                          tcm_dtype out_dtype, float alpha, float beta, void* stream);
+
+/*
  * MXFP8 block-scaled Out = (A * SA) . (B * SB)^T.
  *   A        M x K E4M3 bytes;  B  N x K E4M3 bytes
  *   scale_A  M x (K/32) E8M0 bytes, row-major: scale_A[i][q] multiplies

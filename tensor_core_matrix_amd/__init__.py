@@ -7,6 +7,8 @@ kernels; there is no fallback.  If the library is missing, every call raises.
 
     gemm_tn(a, b, out=None, out_dtype=None)            a: M x K, b: N x K
     batched_gemm_tn(a, b, out=None, out_dtype=None)    a: B x M x K, b: B x N x K
+    gemm_tn_ex(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None)
+                                                       Out = alpha a . b^T + beta c
     gemm_mx_fp8(a, b, scale_a, scale_b, out=None, out_dtype=torch.bfloat16)
     gemm_mx_fp4(a, b, scale_a, scale_b, out=None, out_dtype=torch.bfloat16)
                                                        a: M x K/2, b: N x K/2 E2M1 pairs
@@ -17,7 +19,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["gemm_tn", "batched_gemm_tn", "gemm_mx_fp8", "gemm_mx_fp4", "plan", "lib", "TcmError",
+__all__ = ["gemm_tn", "gemm_tn_ex", "batched_gemm_tn", "gemm_mx_fp8", "gemm_mx_fp4", "plan", "lib", "TcmError",
            "LIB_PATH", "F16", "BF16", "F32", "E4M3", "E8M0", "E2M1"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtcm.so")
@@ -45,8 +47,8 @@ class Plan(ctypes.Structure):
 
 _lock = threading.Lock()
 _lib = None
-EXPORTS = ("tcm_gemm_tn", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8", "tcm_gemm_mx_fp4",
-           "tcm_plan_gemm", "tcm_status_string")
+EXPORTS = ("tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
+           "tcm_gemm_mx_fp4", "tcm_plan_gemm", "tcm_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -61,13 +63,15 @@ def lib() -> ctypes.CDLL:
             vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
             L.tcm_gemm_tn.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
             L.tcm_batched_gemm_tn.argtypes = [vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
+            cf = ctypes.c_float
+            L.tcm_gemm_tn_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, cf, cf, vp]
             L.tcm_gemm_mx_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_gemm_mx_fp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_plan_gemm.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(Plan)]
             L.tcm_status_string.argtypes = [ci]
             L.tcm_status_string.restype = ctypes.c_char_p
-            for f in ("tcm_gemm_tn", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8", "tcm_gemm_mx_fp4",
-                      "tcm_plan_gemm"):
+            for f in ("tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
+                      "tcm_gemm_mx_fp4", "tcm_plan_gemm"):
                 getattr(L, f).restype = ci
             _lib = L
     return _lib
@@ -168,6 +172,32 @@ def gemm_mx_fp8(a, b, scale_a, scale_b, out=None, out_dtype=None):
     with torch.cuda.device(a.device):
         _check(lib().tcm_gemm_mx_fp8(_ptr(a), _ptr(b), _ptr(scale_a), _ptr(scale_b), _ptr(out),
                                      M, N, K, _code(out.dtype), _stream(a)))
+    return out
+
+
+def gemm_tn_ex(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None):
+    """Out = alpha * a . b^T + beta * c; a (M, K), b (N, K) float16/bfloat16;
+    c (M, N) float16/bfloat16/float32 or None (then beta must be 0); out
+    float16/bfloat16/float32 and may be c itself."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or b.dtype != a.dtype:
+        raise ValueError("a and b must share K and dtype")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    if tuple(out.shape) != (M, N) or (c is not None and tuple(c.shape) != (M, N)):
+        raise ValueError(f"out and c must be {(M, N)}")
+    if c is None and beta != 0.0:
+        raise ValueError("beta != 0 needs c")
+    codes = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+    for t in (out,) + ((c,) if c is not None else ()):
+        if t.dtype not in codes:
+            raise TypeError(f"unsupported dtype {t.dtype}")
+    with torch.cuda.device(a.device):
+        _check(lib().tcm_gemm_tn_ex(_ptr(a), _ptr(b), None if c is None else _ptr(c), _ptr(out),
+                                    M, N, K, _code(a.dtype), codes[c.dtype] if c is not None else F32,
+                                    codes[out.dtype], float(alpha), float(beta), _stream(a)))
     return out
 
 

@@ -111,8 +111,11 @@ struct TileCursor {
 // VG selects the copy path: false, direct-to-LDS DMA (`buffer_load ... lds`);
 // true, 16-byte buffer loads into registers one slice ahead and `ds_write_b128`
 // into the ring when the stage is free (plain bf16/f16, 2-stage ring).
+// AB builds the epilogue with a C input: Out = alpha * (A B^T) + beta * C,
+// combined in fp32 in the accumulator layout and rounded once to TOut.
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int SWZ,
-          bool SCALE_WORDS = false, int NSPLIT = 1, bool EPI_LDS = false, bool VG = false>
+          bool SCALE_WORDS = false, int NSPLIT = 1, bool EPI_LDS = false, bool VG = false,
+          bool AB = false>
 __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void tiled_gemm_kernel(GemmArgs p) {
     constexpr int ESZ = Op::kElemBytes;
@@ -353,6 +356,45 @@ void tiled_gemm_kernel(GemmArgs p) {
         const int m_base = c.tm * BM + wm * WTM + l32;
         const int n_base = c.tn * BN + wn * WTN + 4 * hi;
         const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (p.N & 3) == 0;
+        if constexpr (AB) {
+            // Each lane reads the C values of exactly the outputs it writes,
+            // so C may be the output itself (an in-place update).
+            const bool vec = (p.N & 3) == 0;
+            const bool use_c = p.beta != 0.0f;
+            const int cdt = p.c_dtype;
+            const int ces = cdt == 2 ? 4 : 2;
+            const char* Cinb = (const char*)p.Cin + c.batch * p.stride_cin;
+            const float al = p.alpha, be = p.beta;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int m = m_base + i * 32;
+                if (m >= p.M) continue;
+                TOut* row = (TOut*)Cb + (int64_t)m * p.N;
+                const char* crow = Cinb + (int64_t)m * p.N * ces;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = n_base + j * 32 + 8 * q;
+                        const f32x16_t& a4 = acc[i][j];
+                        if (vec && n + 3 < p.N) {
+                            f32x4_t v = {al * a4[4 * q], al * a4[4 * q + 1], al * a4[4 * q + 2],
+                                         al * a4[4 * q + 3]};
+                            if (use_c) v += be * load4_c(crow, n, cdt);
+                            store4<TOut>(row + n, v[0], v[1], v[2], v[3]);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < p.N) {
+                                    float x = al * a4[4 * q + e];
+                                    if (use_c) x += be * load1_c(crow, n + e, cdt);
+                                    row[n + e] = convert_out<TOut>(x);
+                                }
+                        }
+                    }
+            }
+            return;
+        }
         if constexpr (EPI_LDS) {
             // Interior tiles go through LDS: each 32-row block of the wave's
             // output is written to the wave's staging area in the MFMA layout,

@@ -299,6 +299,42 @@ tcm_status tcm_gemm_mx_fp4(const void* A, const void* B, const void* scale_A, co
     return run_mx(4, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream);
 }
 
+tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out, int64_t M,
+                          int64_t N, int64_t K, tcm_dtype dtype, tcm_dtype c_dtype,
+                          tcm_dtype out_dtype, float alpha, float beta, void* stream) {
+    auto out_ok = [](tcm_dtype d) { return d == TCM_F16 || d == TCM_BF16 || d == TCM_F32; };
+    if (!(dtype == TCM_F16 || dtype == TCM_BF16) || !out_ok(out_dtype) ||
+        (beta != 0.0f && !out_ok(c_dtype)))
+        return TCM_ERR_UNSUPPORTED_DTYPE;
+    bool empty = false;
+    tcm_status s = check_sizes(1, M, N, K, &empty);
+    if (s != TCM_OK || empty) return s;
+    if (!Out || (K > 0 && (!A || !B)) || (beta != 0.0f && !C)) return TCM_ERR_NULL_POINTER;
+    if ((s = check_range(1, M, N, K)) != TCM_OK) return s;
+    if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) ||
+        (beta != 0.0f && !aligned16(C)) || (K * 2) % 16 != 0)
+        return TCM_ERR_MISALIGNED;
+    DeviceInfo dev;
+    if ((s = device_info(&dev)) != TCM_OK) return s;
+    tcm_plan plan;
+    GemmArgs a;
+    make_plan(1, M, N, K, 16, dev.cus, &plan, &a);
+    a.A = A;
+    a.B = B;
+    a.C = Out;
+    a.stride_a = M * K * 2;
+    a.stride_b = N * K * 2;
+    a.stride_c = M * N * elem_bytes(out_dtype);
+    a.Cin = beta != 0.0f ? C : nullptr;
+    a.stride_cin = beta != 0.0f ? M * N * elem_bytes(c_dtype) : 0;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.c_dtype = (int32_t)c_dtype;
+    hipError_t e = launch_gemm_epi(plan.kernel, (int32_t)dtype, (int32_t)out_dtype, a, plan.grid,
+                                   (hipStream_t)stream);
+    return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
+}
+
 tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
                          tcm_dtype out_dtype, int mx, int num_cus, tcm_plan* plan) {
     if (!plan) return TCM_ERR_NULL_POINTER;

@@ -78,6 +78,9 @@ template <>
 __device__ __forceinline__ float convert_out<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ __bf16 convert_out<__bf16>(float x) { return to_bf16(x); }
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32); beyond the range: inf
+template <>
+__device__ __forceinline__ _Float16 convert_out<_Float16>(float x) { return (_Float16)x; }
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -92,6 +95,29 @@ __device__ __forceinline__ void store4<float>(float* dst, float a, float b, floa
 template <>
 __device__ __forceinline__ void store4<__bf16>(__bf16* dst, float a, float b, float c, float d) {
     *(bf16x4_t*)dst = (bf16x4_t){to_bf16(a), to_bf16(b), to_bf16(c), to_bf16(d)};
+}
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+template <>
+__device__ __forceinline__ void store4<_Float16>(_Float16* dst, float a, float b, float c, float d) {
+    *(f16x4_t*)dst = (f16x4_t){(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+}
+
+// Values of a C input as floats; dt is the tcm_dtype code (0 f16, 1 bf16,
+// 2 f32).  load4_c reads elements n .. n+3 of a row in one access (n a
+// multiple of 4, the row start aligned to 4 elements).
+__device__ __forceinline__ f32x4_t load4_c(const char* row, int n, int dt) {
+    if (dt == 2) return *(const f32x4_t*)(row + 4 * (int64_t)n);
+    if (dt == 1) {
+        const bf16x4_t v = *(const bf16x4_t*)(row + 2 * (int64_t)n);
+        return (f32x4_t){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+    const f16x4_t v = *(const f16x4_t*)(row + 2 * (int64_t)n);
+    return (f32x4_t){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ float load1_c(const char* row, int n, int dt) {
+    if (dt == 2) return ((const float*)row)[n];
+    if (dt == 1) return (float)((const __bf16*)row)[n];
+    return (float)((const _Float16*)row)[n];
 }
 
 // XCD-aware workgroup order.  Workgroups are dealt round-robin to the 8 XCDs

@@ -25,6 +25,13 @@ struct GemmArgs {
     int32_t total_tiles;
     int32_t ksteps;   // K slices per tile (at least 1, so K == 0 writes zeros)
     int32_t group_m;  // tile rows per group of the grouped tile order
+    // epilogue with a C input (Out = alpha * A B^T + beta * Cin; the kernels
+    // built for it only): Cin is M x N of c_dtype (tcm_dtype code), read only
+    // when beta != 0
+    const void* Cin;
+    int64_t stride_cin;  // bytes
+    float alpha, beta;
+    int32_t c_dtype;
 };
 
 // Kernel variants.  The id is reported by tcm_plan_gemm.
@@ -65,6 +72,8 @@ hipError_t launch_gemm_tn(int32_t variant, int32_t in_dtype, int32_t out_dtype, 
                           int grid, hipStream_t stream);
 // scale_mode: how E8M0 rows may be read -- 0 bytes, 1 32-bit words (K % 128 == 0,
 // word-aligned arrays), 2 16-byte pieces (K % 512 == 0, 16-byte-aligned arrays).
+hipError_t launch_gemm_epi(int32_t variant, int32_t in_dtype, int32_t out_dtype, const GemmArgs& a,
+                           int grid, hipStream_t stream);
 hipError_t launch_gemm_mx(int32_t variant, int32_t out_dtype, int32_t scale_mode, const GemmArgs& a,
                           int grid, hipStream_t stream);
 

@@ -103,6 +103,26 @@ def test_valid_call_without_gpu_reports_no_device():
     assert tcm.lib().tcm_gemm_mx_fp4(A, B, SA, SB, C, 64, 64, 64, tcm.BF16, None) == NO_DEVICE
 
 
+def call_ex(a=A, b=B, c=SA, o=C, M=64, N=64, K=64, dt=tcm.BF16, cdt=tcm.F32, odt=tcm.F16,
+            alpha=1.0, beta=0.5):
+    return tcm.lib().tcm_gemm_tn_ex(a, b, c, o, M, N, K, dt, cdt, odt, alpha, beta, None)
+
+
+def test_epilogue_entry_validation():
+    assert call_ex(dt=tcm.F32) == UNSUP_DTYPE
+    assert call_ex(odt=tcm.E4M3) == UNSUP_DTYPE
+    assert call_ex(cdt=tcm.E8M0) == UNSUP_DTYPE
+    assert call_ex(cdt=tcm.E8M0, beta=0.0, c=None) in (OK, NO_DEVICE)  # C unused when beta == 0
+    assert call_ex(c=None) == NULLP                                      # beta != 0 needs C
+    assert call_ex(o=None) == NULLP
+    assert call_ex(M=-1) == BADSHAPE
+    assert call_ex(K=(1 << 20) + 8) == UNSUP_SHAPE
+    assert call_ex(c=SA + 4) == MISALIGNED
+    assert call_ex(K=60) == MISALIGNED
+    assert call_ex(a=None, b=None, c=None, o=None, M=0) == OK             # empty: no-op
+    assert call_ex() in (OK, NO_DEVICE)
+
+
 def test_plan_stage_bytes_match_page():
     fig = json.load(open(GOLDEN))["stage_bytes"]
     p = tcm.plan(fig["tile_m"], fig["tile_n"], fig["tile_k"], tcm.BF16, tcm.F32, batch=1024)
