@@ -360,3 +360,92 @@ int oracle_entries(int dtype, const void* A, const void* B, const uint8_t* SA, c
     }
     return 0;
 }
+
+/*
+ * Operands in either arrangement, with leading dimensions.  "API Card:
+ * Blackwell Pipeline (tcgen05)", "Descriptor." and "Host side.": the product
+ * is Out = A . B with A the M x K matrix and B the K x N matrix; each global
+ * operand is declared row-major or column-major and takes a leading dimension
+ * (the elements from one stored row, or column, to the next), and the 16-bit
+ * types run in either arrangement.  Read plainly, as in BLAS:
+ *
+ *   a(i,k) = A[i * lda + k]   row-major A      A[k * lda + i]   column-major A
+ *   b(k,j) = B[k * ldb + j]   row-major B      B[j * ldb + k]   column-major B
+ *
+ *   ref[i][j] = sum_k a(i,k) * b(k,j),   abssum likewise, fp64, k ascending
+ *
+ * The TN arrangement of oracle_gemm_tn is row-major A with lda = K and
+ * column-major B with ldb = K.  A row-major matrix needs ld >= its column
+ * count, a column-major one ld >= its row count.
+ */
+enum { OR_ROW_MAJOR = 0, OR_COL_MAJOR = 1 };
+
+static int64_t a_index(int order, int64_t ld, int64_t i, int64_t k) {
+    return order == OR_ROW_MAJOR ? i * ld + k : k * ld + i;
+}
+
+static int64_t b_index(int order, int64_t ld, int64_t k, int64_t j) {
+    return order == OR_ROW_MAJOR ? k * ld + j : j * ld + k;
+}
+
+static int ld_ok(int dtype, int a_order, int64_t lda, int b_order, int64_t ldb, int64_t M,
+                 int64_t N, int64_t K) {
+    if (!(dtype == OR_F16 || dtype == OR_BF16 || dtype == OR_F32) || !shape_ok(1, M, N, K))
+        return 0;
+    if ((a_order != OR_ROW_MAJOR && a_order != OR_COL_MAJOR) ||
+        (b_order != OR_ROW_MAJOR && b_order != OR_COL_MAJOR))
+        return 0;
+    return lda >= (a_order == OR_ROW_MAJOR ? K : M) && lda >= 1 &&
+           ldb >= (b_order == OR_ROW_MAJOR ? N : K) && ldb >= 1;
+}
+
+int oracle_gemm_ld(int dtype, const void* A, int a_order, int64_t lda, const void* B, int b_order,
+                   int64_t ldb, int64_t M, int64_t N, int64_t K, double* ref, double* abssum,
+                   int nthreads) {
+    if (!A || !B || !ld_ok(dtype, a_order, lda, b_order, ldb, M, N, K))
+        return -1;
+    /* gather the logical matrices: a as M x K, b as N x K (b's row j holds
+     * column j of B), then the same sums as the TN form */
+    double* a = (double*)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
+    double* b = (double*)malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(double));
+    if (!a || !b) {
+        free(a);
+        free(b);
+        return -2;
+    }
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k)
+            a[i * K + k] = dec_one(dtype, A, a_index(a_order, lda, i, k));
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k)
+            b[j * K + k] = dec_one(dtype, B, b_index(b_order, ldb, k, j));
+    int rc = run_rows(a, b, M, N, K, ref, abssum, nthreads);
+    free(a);
+    free(b);
+    return rc;
+}
+
+/* Selected entries (ii[t], jj[t]) of the same product, one by one. */
+int oracle_entries_ld(int dtype, const void* A, int a_order, int64_t lda, const void* B,
+                      int b_order, int64_t ldb, int64_t M, int64_t N, int64_t K, const int64_t* ii,
+                      const int64_t* jj, int64_t n, double* ref, double* abssum) {
+    if (!A || !B || !ii || !jj || !ld_ok(dtype, a_order, lda, b_order, ldb, M, N, K))
+        return -1;
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t i = ii[t], j = jj[t];
+        if (i < 0 || i >= M || j < 0 || j >= N)
+            return -1;
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double prod = dec_one(dtype, A, a_index(a_order, lda, i, k)) *
+                          dec_one(dtype, B, b_index(b_order, ldb, k, j));
+            s += prod;
+            sa += fabs(prod);
+        }
+        if (ref)
+            ref[t] = s;
+        if (abssum)
+            abssum[t] = sa;
+    }
+    return 0;
+}

@@ -17,6 +17,10 @@ element products are exact ("Blackwell Tensor Cores", The Accumulator's
 Lifetime: float16 products accumulated in float32).  Its bf16 ulp term covers
 the single rounding of the fp32 result to a bf16 output.
 
+``gemm_ld`` / ``entries_ld`` take the operands in either arrangement
+(row-major or column-major A and B of Out = A . B) with leading dimensions,
+as the cuBLASDx Blackwell card's host side declares global operands.
+
 Inputs are numpy arrays holding the raw storage of the operands:
 uint16 for float16 / bfloat16 bit patterns, uint8 for E4M3 and E8M0 bytes,
 uint8 for E2M1 pairs (two elements per byte, the even element in the low four
@@ -70,8 +74,14 @@ def _load():
                                          vp, dp]
             lib.oracle_entries.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, vp, vp,
                                            vp, i64, dp, dp]
+            ci = ctypes.c_int
+            lib.oracle_gemm_ld.argtypes = [ci, vp, ci, i64, vp, ci, i64, i64, i64, i64, dp, dp,
+                                           ci]
+            lib.oracle_entries_ld.argtypes = [ci, vp, ci, i64, vp, ci, i64, i64, i64, i64, vp,
+                                              vp, i64, dp, dp]
             for f in (lib.oracle_decode, lib.oracle_gemm_tn, lib.oracle_gemm_mx,
-                      lib.oracle_gemm_mx_typed, lib.oracle_entries, lib.oracle_axpby):
+                      lib.oracle_gemm_mx_typed, lib.oracle_entries, lib.oracle_axpby,
+                      lib.oracle_gemm_ld, lib.oracle_entries_ld):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -176,6 +186,57 @@ def entries(dtype: int, a: np.ndarray, b: np.ndarray, ii, jj, bb=None, sa=None, 
                                 _ptr(bbv), _ptr(ii), _ptr(jj), n, _ptr(ref), _ptr(s))
     if rc:
         raise ValueError(f"oracle_entries failed ({rc})")
+    return ref, s
+
+
+ROW_MAJOR, COL_MAJOR = 0, 1
+
+
+def storage_elems(order: int, ld: int, rows: int, cols: int) -> int:
+    """Elements a rows x cols matrix of the given order and leading dimension
+    spans in storage (0 when it is empty)."""
+    if rows == 0 or cols == 0:
+        return 0
+    return (rows - 1) * ld + cols if order == ROW_MAJOR else (cols - 1) * ld + rows
+
+
+def _ld_args(dtype, a, a_order, lda, b, b_order, ldb, M, N, K):
+    a = _raw(a, dtype).reshape(-1)
+    b = _raw(b, dtype).reshape(-1)
+    if a.size < storage_elems(a_order, lda, M, K) or b.size < storage_elems(b_order, ldb, K, N):
+        raise ValueError("operand storage smaller than its shape and leading dimension need")
+    return a, b
+
+
+def gemm_ld(dtype: int, a: np.ndarray, a_order: int, lda: int, b: np.ndarray, b_order: int,
+            ldb: int, M: int, N: int, K: int, nthreads: int | None = None):
+    """ref, abssum (fp64, M x N) of Out = A . B with A the M x K matrix and B
+    the K x N matrix, each stored row-major or column-major (ROW_MAJOR /
+    COL_MAJOR) with leading dimension lda / ldb in elements (see oracle.c).
+    a and b are raw storage, any shape, read flat."""
+    a, b = _ld_args(dtype, a, a_order, lda, b, b_order, ldb, M, N, K)
+    ref = np.empty((M, N), np.float64)
+    s = np.empty((M, N), np.float64)
+    rc = _load().oracle_gemm_ld(dtype, _ptr(a), a_order, lda, _ptr(b), b_order, ldb, M, N, K,
+                                _ptr(ref), _ptr(s), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_gemm_ld failed ({rc})")
+    return ref, s
+
+
+def entries_ld(dtype: int, a, a_order: int, lda: int, b, b_order: int, ldb: int, M: int, N: int,
+               K: int, ii, jj):
+    """ref, abssum at outputs (ii[t], jj[t]) of the gemm_ld product, each from
+    the definition, for problems too big to do whole."""
+    a, b = _ld_args(dtype, a, a_order, lda, b, b_order, ldb, M, N, K)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    ref = np.empty(ii.size, np.float64)
+    s = np.empty(ii.size, np.float64)
+    rc = _load().oracle_entries_ld(dtype, _ptr(a), a_order, lda, _ptr(b), b_order, ldb, M, N, K,
+                                   _ptr(ii), _ptr(jj), ii.size, _ptr(ref), _ptr(s))
+    if rc:
+        raise ValueError(f"oracle_entries_ld failed ({rc})")
     return ref, s
 
 

@@ -18,7 +18,11 @@ applied to the wrong block -- fails at least one of them:
   them, the nibble order of a hand-packed byte, every value re-encoded by
   torch's own E4M3 cast decoding the same, and the MXFP4 product equal to the
   MXFP8 product of the same values (E2M1 is a subset of E4M3), plus brute
-  force.
+  force;
+* operand arrangements and leading dimensions: every row-/column-major pair,
+  stored through torch's own transposes inside NaN-padded rows, equals the
+  pinned TN product bit for bit (a swapped index or an ignored leading
+  dimension reads a NaN or a wrong element).
 """
 from fractions import Fraction
 
@@ -352,6 +356,87 @@ def test_planted_mistakes_fail_the_pins():
     dropped, _ = orc.gemm_tn(orc.BF16, inp.raw(torch.ones(3, 63, dtype=torch.bfloat16)),
                              inp.raw(torch.ones(4, 63, dtype=torch.bfloat16)))
     assert not np.all(dropped == 64)
+
+
+# --------------------------------- arrangements and leading dimensions
+def _in_nan_rows(x: torch.Tensor, ld: int) -> torch.Tensor:
+    """x (rows x c) in the first c columns of a rows x ld array whose other
+    elements are NaN: row-major storage of x with leading dimension ld."""
+    out = torch.full((x.shape[0], ld), float("nan"), dtype=x.dtype)
+    out[:, : x.shape[1]] = x
+    return out
+
+
+def _stored(a, b, a_order, b_order, pad):
+    """Storage and leading dimensions of logical A = a (M x K) and B = b^T
+    (K x N) in the given orders, made with torch's transposes."""
+    ast = a if a_order == orc.ROW_MAJOR else a.T      # column-major A: rows of A^T
+    bst = b.T if b_order == orc.ROW_MAJOR else b      # column-major B: rows of B^T = b
+    lda, ldb = ast.shape[1] + pad, bst.shape[1] + pad
+    return _in_nan_rows(ast, lda), lda, _in_nan_rows(bst, ldb), ldb
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("a_order", [0, 1])
+@pytest.mark.parametrize("b_order", [0, 1])
+@pytest.mark.parametrize("pad", [0, 5])
+def test_arrangements_equal_tn_product(dt, a_order, b_order, pad):
+    M, N, K = 13, 11, 24
+    g = inp.generator(46 + a_order + 2 * b_order)
+    tdt = inp.TORCH_DTYPES[dt]
+    a = inp.normal((M, K), g, 1.0, tdt)
+    b = inp.normal((N, K), g, 1.0, tdt)
+    want, ws = orc.gemm_tn(orc.DTYPE_NAMES[dt], inp.raw(a), inp.raw(b))
+    ast, lda, bst, ldb = _stored(a, b, a_order, b_order, pad)
+    got, gs = orc.gemm_ld(orc.DTYPE_NAMES[dt], inp.raw(ast), a_order, lda, inp.raw(bst),
+                          b_order, ldb, M, N, K)
+    assert _same(got, want) and _same(gs, ws)
+    ii, jj = np.array([0, 12, 7]), np.array([10, 0, 4])
+    r, s = orc.entries_ld(orc.DTYPE_NAMES[dt], inp.raw(ast), a_order, lda, inp.raw(bst), b_order,
+                          ldb, M, N, K, ii, jj)
+    assert _same(r, want[ii, jj]) and _same(s, ws[ii, jj])
+
+
+def test_arrangement_exact_against_numpy_matmul():
+    """Small-integer operands: the product is exact in fp64, so it must equal
+    numpy's matmul of the logical matrices (column-major A, row-major B)."""
+    M, N, K = 6, 9, 40
+    g = inp.generator(47)
+    a = torch.randint(-8, 9, (K, M), generator=g).to(torch.bfloat16)   # storage of A^T
+    b = torch.randint(-8, 9, (K, N), generator=g).to(torch.bfloat16)   # storage of B
+    got, _ = orc.gemm_ld(orc.BF16, inp.raw(a), orc.COL_MAJOR, M, inp.raw(b), orc.ROW_MAJOR, N,
+                         M, N, K)
+    assert np.array_equal(got, a.double().numpy().T @ b.double().numpy())
+
+
+def test_arrangement_validation():
+    z = np.zeros(64, np.uint16)
+    with pytest.raises(ValueError):   # row-major A needs lda >= K
+        orc.gemm_ld(orc.BF16, z, orc.ROW_MAJOR, 3, z, orc.COL_MAJOR, 4, 2, 2, 4)
+    with pytest.raises(ValueError):   # column-major A needs lda >= M
+        orc.gemm_ld(orc.BF16, z, orc.COL_MAJOR, 1, z, orc.COL_MAJOR, 4, 2, 2, 4)
+    with pytest.raises(ValueError):   # storage too small for the leading dimension
+        orc.gemm_ld(orc.BF16, z, orc.ROW_MAJOR, 70, z, orc.COL_MAJOR, 4, 2, 2, 4)
+    with pytest.raises(ValueError):   # unknown order
+        orc.gemm_ld(orc.BF16, z, 2, 4, z, orc.COL_MAJOR, 4, 2, 2, 4)
+
+
+def test_planted_arrangement_mistakes_fail_the_pin():
+    """Planted on the CPU: reading column-major storage as row-major, or
+    stepping rows by the column count instead of the leading dimension, must
+    break the equality with the TN product."""
+    M = N = K = 16
+    g = inp.generator(48)
+    a = inp.normal((M, K), g, 1.0, torch.bfloat16)
+    b = inp.normal((N, K), g, 1.0, torch.bfloat16)
+    want, _ = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    ast, lda, bst, ldb = _stored(a, b, orc.COL_MAJOR, orc.ROW_MAJOR, 3)
+    wrong_order, _ = orc.gemm_ld(orc.BF16, inp.raw(ast), orc.ROW_MAJOR, lda, inp.raw(bst),
+                                 orc.ROW_MAJOR, ldb, M, N, K)
+    assert not _same(wrong_order, want)
+    wrong_ld, _ = orc.gemm_ld(orc.BF16, inp.raw(ast), orc.COL_MAJOR, M, inp.raw(bst),
+                              orc.ROW_MAJOR, ldb, M, N, K)
+    assert not _same(wrong_ld, want)
 
 
 # ----------------------------------------------------- axpby epilogue
