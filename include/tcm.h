@@ -21,7 +21,8 @@
  *   Layout     A: M x K row-major (leading dimension K).  B: N x K row-major
  *              (leading dimension K).  Out: M x N row-major (leading dimension
  *              N).  Batched operands are contiguous: problem p starts at
- *              p*M*K, p*N*K and p*M*N elements.
+ *              p*M*K, p*N*K and p*M*N elements.  tcm_gemm alone takes other
+ *              arrangements and leading dimensions.
  *   Pointers   device pointers (hipMalloc'ed or torch CUDA tensors) on the
  *              current HIP device.  The caller owns all buffers; the library
  *              never allocates, frees or retains them and keeps no per-call
@@ -78,6 +79,14 @@ typedef enum tcm_dtype {
                      byte t (no infinities, no NaN, max 6) */
 } tcm_dtype;
 
+/* Arrangement of a matrix in memory: row-major (the elements of one row
+ * contiguous, rows `ld` elements apart) or column-major (columns contiguous,
+ * `ld` elements apart). */
+typedef enum tcm_order {
+    TCM_ROW_MAJOR = 0,
+    TCM_COL_MAJOR = 1
+} tcm_order;
+
 /*
  * Out = A . B^T for one problem.
  *   A        M x K elements of `dtype` (TCM_F16 or TCM_BF16)
@@ -117,6 +126,38 @@ tcm_status tcm_batched_gemm_tn(const void* A, const void* B, void* Out, int64_t 
 tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out, int64_t M,
                           int64_t N, int64_t K, tcm_dtype dtype, tcm_dtype c_dtype,
                           tcm_dtype out_dtype, float alpha, float beta, void* stream);
+
+/*
+ * General form: Out = alpha * (A . B) + beta * C with A the M x K matrix and B
+ * the K x N matrix, each in either arrangement with a leading dimension
+ * ("API Card: Blackwell Pipeline (tcgen05)", "Descriptor.": half and bfloat16
+ * run in either majorness; "Host side.": global operands are declared
+ * row-major or column-major with a leading dimension).
+ *   A        element (i, k) at A[i*lda + k] (a_order TCM_ROW_MAJOR, lda >= K)
+ *            or A[k*lda + i] (TCM_COL_MAJOR, lda >= M)
+ *   B        element (k, j) at B[k*ldb + j] (b_order TCM_ROW_MAJOR, ldb >= N)
+ *            or B[j*ldb + k] (TCM_COL_MAJOR, ldb >= K)
+ *   C        M x N row-major of `c_dtype`, element (i, j) at C[i*ldc + j],
+ *            ldc >= N; read only when beta != 0 (then non-NULL)
+ *   Out      M x N row-major of `out_dtype`, element (i, j) at Out[i*ldo + j],
+ *            ldo >= N; only these M x N elements are written
+ * dtype TCM_F16 or TCM_BF16; c_dtype and out_dtype TCM_F16, TCM_BF16 or
+ * TCM_F32.  Sums, combine and rounding as tcm_gemm_tn_ex; C may be Out itself
+ * (same pointer, dtype and leading dimension).  Row-major A with
+ * column-major B (lda = ldb = K, ldo = N) is tcm_gemm_tn's operation.
+ * Every leading dimension must be at least 1 and at least the size named
+ * above (TCM_ERR_INVALID_SHAPE), lda and ldb at most 2^21
+ * (TCM_ERR_UNSUPPORTED_SHAPE); an order other than the two gives
+ * TCM_ERR_INVALID_SHAPE.  Alignment: A, B, Out (and C when read) 16-byte
+ * aligned, lda and ldb multiples of 8 elements, and K a multiple of 8 unless
+ * A is column-major and B row-major (TCM_ERR_MISALIGNED); ldo and ldc are
+ * free.
+ */
+tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B,
+                    tcm_order b_order, int64_t ldb, const void* C, int64_t ldc, void* Out,
+                    int64_t ldo, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
+                    tcm_dtype c_dtype, tcm_dtype out_dtype, float alpha, float beta,
+                    void* stream);
 
 /*
  * MXFP8 block-scaled Out = (A * SA) . (B * SB)^T.

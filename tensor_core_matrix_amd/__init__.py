@@ -12,6 +12,9 @@ kernels; there is no fallback.  If the library is missing, every call raises.
     gemm_mx_fp8(a, b, scale_a, scale_b, out=None, out_dtype=torch.bfloat16)
     gemm_mx_fp4(a, b, scale_a, scale_b, out=None, out_dtype=torch.bfloat16)
                                                        a: M x K/2, b: N x K/2 E2M1 pairs
+    gemm(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None)
+                                                       Out = alpha a . b + beta c, a: M x K
+                                                       and b: K x N strided views
 """
 from __future__ import annotations
 
@@ -19,13 +22,15 @@ import ctypes
 import os
 import threading
 
-__all__ = ["gemm_tn", "gemm_tn_ex", "batched_gemm_tn", "gemm_mx_fp8", "gemm_mx_fp4", "plan", "lib", "TcmError",
+__all__ = ["gemm", "gemm_tn", "gemm_tn_ex", "batched_gemm_tn", "gemm_mx_fp8", "gemm_mx_fp4", "plan", "lib", "TcmError",
            "LIB_PATH", "F16", "BF16", "F32", "E4M3", "E8M0", "E2M1"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtcm.so")
 
 # tcm_dtype codes
 F16, BF16, F32, E4M3, E8M0, E2M1 = 0, 1, 2, 3, 4, 5
+# tcm_order codes
+ROW_MAJOR, COL_MAJOR = 0, 1
 
 
 class TcmError(RuntimeError):
@@ -47,7 +52,7 @@ class Plan(ctypes.Structure):
 
 _lock = threading.Lock()
 _lib = None
-EXPORTS = ("tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
+EXPORTS = ("tcm_gemm", "tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
            "tcm_gemm_mx_fp4", "tcm_plan_gemm", "tcm_status_string")
 
 
@@ -65,12 +70,14 @@ def lib() -> ctypes.CDLL:
             L.tcm_batched_gemm_tn.argtypes = [vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
             cf = ctypes.c_float
             L.tcm_gemm_tn_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, cf, cf, vp]
+            L.tcm_gemm.argtypes = [vp, ci, i64, vp, ci, i64, vp, i64, vp, i64, i64, i64, i64,
+                                   ci, ci, ci, cf, cf, vp]
             L.tcm_gemm_mx_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_gemm_mx_fp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_plan_gemm.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(Plan)]
             L.tcm_status_string.argtypes = [ci]
             L.tcm_status_string.restype = ctypes.c_char_p
-            for f in ("tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
+            for f in ("tcm_gemm", "tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
                       "tcm_gemm_mx_fp4", "tcm_plan_gemm"):
                 getattr(L, f).restype = ci
             _lib = L
@@ -226,6 +233,52 @@ def gemm_mx_fp4(a, b, scale_a, scale_b, out=None, out_dtype=None):
     with torch.cuda.device(a.device):
         _check(lib().tcm_gemm_mx_fp4(_ptr(a), _ptr(b), _ptr(scale_a), _ptr(scale_b), _ptr(out),
                                      M, N, K, _code(out.dtype), _stream(a)))
+    return out
+
+
+def order_ld(t) -> tuple[int, int]:
+    """(tcm_order, leading dimension) of a 2-D tensor view whose rows or
+    columns are contiguous (unit stride along dimension 1 or 0)."""
+    r, c = t.shape
+    s0, s1 = t.stride()
+    if s1 == 1 and (s0 >= c or r <= 1):
+        return ROW_MAJOR, s0 if r > 1 else max(s0, c)
+    if s0 == 1 and (s1 >= r or c <= 1):
+        return COL_MAJOR, s1 if c > 1 else max(s1, r)
+    raise ValueError(f"no unit stride: shape {tuple(t.shape)}, strides {t.stride()}")
+
+
+def gemm(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None):
+    """Out = alpha * a . b + beta * c for 2-D views: a (M, K) and b (K, N)
+    float16/bfloat16 with rows or columns contiguous (transposed views and
+    slices of larger tensors are taken as they are, by their strides); c and
+    out (M, N) float16/bfloat16/float32 with contiguous rows; out may be c."""
+    torch = _torch()
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K or b.dtype != a.dtype:
+        raise ValueError("a (M, K) and b (K, N) must share K and dtype")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.float32, device=a.device)
+    if tuple(out.shape) != (M, N) or (c is not None and tuple(c.shape) != (M, N)):
+        raise ValueError(f"out and c must be {(M, N)}")
+    if c is None and beta != 0.0:
+        raise ValueError("beta != 0 needs c")
+    codes = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+    for t in (out,) + ((c,) if c is not None else ()):
+        if t.dtype not in codes:
+            raise TypeError(f"unsupported dtype {t.dtype}")
+    ao, lda = order_ld(a)
+    bo, ldb = order_ld(b)
+    oo, ldo = order_ld(out)
+    co, ldc = order_ld(c) if c is not None else (ROW_MAJOR, N)
+    if oo != ROW_MAJOR or co != ROW_MAJOR:
+        raise ValueError("out and c need contiguous rows")
+    with torch.cuda.device(a.device):
+        _check(lib().tcm_gemm(a.data_ptr(), ao, lda, b.data_ptr(), bo, ldb,
+                              None if c is None else c.data_ptr(), ldc, out.data_ptr(), ldo,
+                              M, N, K, _code(a.dtype), codes[c.dtype] if c is not None else F32,
+                              codes[out.dtype], float(alpha), float(beta), _stream(a)))
     return out
 
 

@@ -1,5 +1,9 @@
 // The tiled product kernel for gfx950: Out = A . B^T, A M x K and B N x K
-// both K-contiguous ("TN"), fp32 accumulation in the matrix cores.
+// both K-contiguous ("TN"), fp32 accumulation in the matrix cores.  For
+// 16-bit inputs either operand may instead be stored with its M (N) index
+// contiguous, K rows of M (N) values ("API Card: Blackwell Pipeline
+// (tcgen05)", Descriptor: half and bfloat16 run in either majorness), and
+// every operand, the C input and the output take a leading dimension.
 //
 // Structure (the pipelined tile loop of "Hopper and Blackwell GEMM", Concept
 // and Maths sections, and of "API Card: Blackwell Pipeline (tcgen05)",
@@ -113,9 +117,11 @@ struct TileCursor {
 // into the ring when the stage is free (plain bf16/f16, 2-stage ring).
 // AB builds the epilogue with a C input: Out = alpha * (A B^T) + beta * C,
 // combined in fp32 in the accumulator layout and rounded once to TOut.
+// A_MN (B_MN): A (B) is stored M-major (N-major): K rows of lda (ldb)
+// elements, the tile's BM (BN) values of one k contiguous.
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int SWZ,
           bool SCALE_WORDS = false, int NSPLIT = 1, bool EPI_LDS = false, bool VG = false,
-          bool AB = false>
+          bool AB = false, bool A_MN = false, bool B_MN = false>
 __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void tiled_gemm_kernel(GemmArgs p) {
     constexpr int ESZ = Op::kElemBytes;
@@ -148,6 +154,10 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert(!Op::kScaled || (BK == 128 && S == 2), "MX path: 128-deep slices, 2 stages");
     static_assert(!VG || (!Op::kScaled && S == 2), "register-staged copies: plain types, 2 stages");
     static_assert(Op::kElemBits >= 8, "whole-byte elements");
+    constexpr bool ANY_MN = A_MN || B_MN;
+    static_assert(!ANY_MN || (ESZ == 2 && !Op::kScaled && !VG), "M/N-major: 16-bit, DMA copies");
+    static_assert((!A_MN || BM * ESZ >= 256) && (!B_MN || BN * ESZ >= 256),
+                  "M/N-major rows of at least 16 chunks (bank spread of the transposing reads)");
 
     // Epilogue staging: one 32-row block of a wave's output at a time, in a
     // wave-private LDS area after the ring.
@@ -170,15 +180,33 @@ void tiled_gemm_kernel(GemmArgs p) {
     const int K = p.K;
 
     // ---- per-lane copy geometry -------------------------------------------
-    // Copy i of wave w fills LDS chunk q = (4 i + w) * 64 + lane of the A (B)
-    // region: row q / CPR, physical chunk q % CPR, which holds logical chunk
-    // (q % CPR) ^ swz(row) of that row's K slice.  The chunk is the same for
-    // every i, and copy i sits 4 * ROWS_PER_WAVE_COPY rows below copy i - 1.
+    // K-major operand: copy i of wave w fills LDS chunk q = (4 i + w) * 64 +
+    // lane of the A (B) region: row q / CPR, physical chunk q % CPR, which
+    // holds logical chunk (q % CPR) ^ swz(row) of that row's K slice.  The
+    // chunk is the same for every i, and copy i sits 4 * ROWS_PER_WAVE_COPY
+    // rows below copy i - 1.
     const int cp_row = wave * ROWS_PER_WAVE_COPY + lane / CPR;
     const int cp_chunk = (lane % CPR) ^ ((cp_row >> SWZ) & (CPR - 1));
-    const uint32_t cp_off = (uint32_t)cp_row * (uint32_t)K * ESZ + cp_chunk * 16;
     const int cp_k = cp_chunk * (16 / ESZ);  // first K element of the chunk
-    const uint32_t cp_step = 4u * ROWS_PER_WAVE_COPY * (uint32_t)K * ESZ;
+    // M-major (N-major) operand: the region holds BK rows, one per k of the
+    // slice, of the tile's BM (BN) values; chunk q is row q / cpr, physical
+    // chunk q % cpr, holding logical chunk (q % cpr) ^ 4 (row % 4), so that
+    // the four rows a transposing read touches sit in different bank groups.
+    struct CopyGeo {
+        uint32_t off, step;  // buffer offset of copy 0, and from copy i to i + 1
+    };
+    auto kmajor_geo = [&](int ld) -> CopyGeo {
+        return {(uint32_t)cp_row * (uint32_t)ld * ESZ + cp_chunk * 16,
+                4u * ROWS_PER_WAVE_COPY * (uint32_t)ld * ESZ};
+    };
+    auto mn_geo = [&](int rows, int ld) -> CopyGeo {
+        const int cpr = rows * ESZ / 16, rpw = kWaveSize / cpr;
+        const int row = wave * rpw + lane / cpr;
+        const int ch = (lane % cpr) ^ (4 * (row & 3));
+        return {(uint32_t)row * (uint32_t)ld * ESZ + ch * 16, 4u * rpw * (uint32_t)ld * ESZ};
+    };
+    const CopyGeo geo_a = A_MN ? mn_geo(BM, p.lda) : kmajor_geo(p.lda);
+    const CopyGeo geo_b = B_MN ? mn_geo(BN, p.ldb) : kmajor_geo(p.ldb);
 
     auto locate = [&](TileCursor& c) {
         tile_coords(p, c.tl * G + lid, c.batch, c.tm, c.tn);
@@ -191,16 +219,37 @@ void tiled_gemm_kernel(GemmArgs p) {
     };
 
     // The copy stream ("producer"): the next slice to copy and the buffer
-    // resources of its tile, rebuilt only when the stream enters a new tile.
+    // resources of its tile, rebuilt when the stream enters a new tile (and,
+    // with an M/N-major operand, at every slice).
     TileCursor fc = {0, 0, 0, 0, 0};
     __amdgpu_buffer_rsrc_t ra, rb;
+    // K-major: the tile's rows r0 .. r0 + rows - 1; rows past the tile's last
+    // (r >= rows) start at or beyond the bound.
+    auto kmajor_rsrc = [&](const char* base, int r0, int R, int BR, int ld) {
+        const int rows = min(BR, R - r0);
+        return make_rsrc(base + (int64_t)r0 * ld * ESZ, (uint32_t)((rows - 1) * ld + K) * ESZ);
+    };
+    // M/N-major: k rows k0 .. k0 + kv - 1 of the slice, columns r0 .. r0 + BR - 1;
+    // the bound ends with the last row's last 16-byte piece that holds a
+    // valid column (ld is a multiple of 8), so rows past K read as zeros
+    // and no read leaves the operand's storage.
+    auto mn_rsrc = [&](const char* base, int r0, int R, int BR, int ld, int k0) {
+        const int kv = min(BK, K - k0);
+        const int cols = min(BR, ((R + 7) & ~7) - r0);
+        const uint32_t bytes = kv > 0 ? (uint32_t)((kv - 1) * ld + cols) * ESZ : 0u;
+        return make_rsrc(base + ((int64_t)k0 * ld + r0) * ESZ, bytes);
+    };
     auto feed_resources = [&]() {
-        const int rows_a = min(BM, p.M - fc.tm * BM);
-        const int rows_b = min(BN, p.N - fc.tn * BN);
-        const char* abase = (const char*)p.A + fc.batch * p.stride_a + (int64_t)fc.tm * BM * K * ESZ;
-        const char* bbase = (const char*)p.B + fc.batch * p.stride_b + (int64_t)fc.tn * BN * K * ESZ;
-        ra = make_rsrc(abase, (uint32_t)rows_a * (uint32_t)K * ESZ);
-        rb = make_rsrc(bbase, (uint32_t)rows_b * (uint32_t)K * ESZ);
+        const char* abase = (const char*)p.A + fc.batch * p.stride_a;
+        const char* bbase = (const char*)p.B + fc.batch * p.stride_b;
+        if constexpr (A_MN)
+            ra = mn_rsrc(abase, fc.tm * BM, p.M, BM, p.lda, fc.kk * BK);
+        else
+            ra = kmajor_rsrc(abase, fc.tm * BM, p.M, BM, p.lda);
+        if constexpr (B_MN)
+            rb = mn_rsrc(bbase, fc.tn * BN, p.N, BN, p.ldb, fc.kk * BK);
+        else
+            rb = kmajor_rsrc(bbase, fc.tn * BN, p.N, BN, p.ldb);
     };
     auto feed_advance = [&]() {
         if (++fc.kk == p.ksteps) {
@@ -209,28 +258,36 @@ void tiled_gemm_kernel(GemmArgs p) {
                 locate(fc);
                 feed_resources();
             }
+        } else if constexpr (ANY_MN) {
+            feed_resources();
         }
     };
-    // Buffer offset of copy 0 of the stream's current slice, computed outside
-    // the hot region; copy i adds i * cp_step.  A slice past the last one
-    // (`live` false) and 16-byte chunks past K get out-of-range offsets
-    // (>= 2^31, beyond any tile's records even after adding i * cp_step):
-    // those copies touch no memory and write zeros into a stage that is
-    // never read again.
-    uint32_t foff0;
+    // Buffer offsets of copy 0 of the stream's current slice, computed
+    // outside the hot region; copy i adds i * step.  A slice past the last
+    // one (`live` false) and K-major 16-byte chunks past K get out-of-range
+    // offsets (>= 2^31, beyond any tile's records even after adding
+    // i * step): those copies touch no memory and write zeros into a stage
+    // that is never read again.  (An M/N-major slice's resource starts at
+    // its own first k row, so its offsets do not move with k.)
+    uint32_t foff_a0, foff_b0;
     auto feed_offsets = [&](bool live) {
-        const int k0 = fc.kk * BK;
-        foff0 = (live && k0 + cp_k < K) ? cp_off + (uint32_t)k0 * ESZ : kOutOfRange;
+        const uint32_t k0b = (uint32_t)(fc.kk * BK) * ESZ;
+        const bool kin = fc.kk * BK + cp_k < K;
+        foff_a0 = A_MN ? (live ? geo_a.off : kOutOfRange)
+                       : (live && kin ? geo_a.off + k0b : kOutOfRange);
+        foff_b0 = B_MN ? (live ? geo_b.off : kOutOfRange)
+                       : (live && kin ? geo_b.off + k0b : kOutOfRange);
     };
-    auto foff = [&](int i) -> uint32_t { return foff0 + (uint32_t)i * cp_step; };
+    auto foff_a = [&](int i) -> uint32_t { return foff_a0 + (uint32_t)i * geo_a.step; };
+    auto foff_b = [&](int i) -> uint32_t { return foff_b0 + (uint32_t)i * geo_b.step; };
     // Copies of the stream's current slice into ring stage `st`.
     auto issue = [&](int st) {
         char* sa = lds + st * STAGE;
         char* sb = sa + A_BYTES;
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) copy16_to_lds(ra, sa + (4 * i + wave) * 1024, foff(i));
+        for (int i = 0; i < A_LOADS; ++i) copy16_to_lds(ra, sa + (4 * i + wave) * 1024, foff_a(i));
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) copy16_to_lds(rb, sb + (4 * i + wave) * 1024, foff(i));
+        for (int i = 0; i < B_LOADS; ++i) copy16_to_lds(rb, sb + (4 * i + wave) * 1024, foff_b(i));
     };
 
     // ---- per-lane fragment geometry ---------------------------------------
@@ -256,12 +313,59 @@ void tiled_gemm_kernel(GemmArgs p) {
         }
         return f;
     };
+    // M-major (N-major) regions: transposing reads.  For fragment block f
+    // and K step s, lane 16 g + t reads the 8 bytes at k row
+    // 16 s + 8 (g / 2) + t / 4 (and 4 rows further for the second half),
+    // columns c + 16 (g % 2) + 4 (t % 4) .. + 3, c the block's first column;
+    // it receives k 16 s + 8 (g / 2) + 0..3 (4..7) of column
+    // c + 16 (g % 2) + t, which is the MFMA operand layout (row l % 32,
+    // K values 8 (l / 32) .. + 7).  k % 4 = t / 4 for every such read, so the
+    // row's chunk swizzle is a per-lane constant folded into the offset.
+    const int g16 = lane >> 4, t16 = lane & 15;
+    auto mn_frag_off = [&](int rowb, int col_byte) -> uint32_t {
+        return (uint32_t)((8 * (g16 >> 1) + (t16 >> 2)) * rowb + (col_byte ^ (64 * (t16 >> 2))) +
+                          32 * (g16 & 1) + 8 * (t16 & 3));
+    };
+    constexpr int RBA = BM * ESZ, RBB = BN * ESZ;  // bytes of one k row, M/N-major regions
+    uint32_t a_mn[A_MN ? FM : 1], b_mn[B_MN ? FN : 1];
+    if constexpr (A_MN) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a_mn[i] = mn_frag_off(RBA, (wm * WTM + 32 * i) * ESZ);
+    }
+    if constexpr (B_MN) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            b_mn[j] = (uint32_t)A_BYTES + mn_frag_off(RBB, (wn * WTN + 32 * j) * ESZ);
+    }
+    auto read_frag_tr = [&](const char* at, int rowb) -> frag_t {
+        if constexpr (ANY_MN) {
+            const s16x4_t lo = lds_read_tr16(at);
+            const s16x4_t up = lds_read_tr16(at + 4 * rowb);
+            return __builtin_bit_cast(frag_t,
+                                      __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            return frag_t{};
+        }
+    };
+    auto frag_a = [&](const char* st, int i, int s) -> frag_t {
+        if constexpr (A_MN)
+            return read_frag_tr(st + a_mn[i] + 16 * s * RBA, RBA);
+        else
+            return read_frag(st + a_frag + i * 32 * RB, s);
+    };
+    auto frag_b = [&](const char* st, int j, int s) -> frag_t {
+        if constexpr (B_MN)
+            return read_frag_tr(st + b_mn[j] + 16 * s * RBB, RBB);
+        else
+            return read_frag(st + b_frag + j * 32 * RB, s);
+    };
+
     frag_t fa[2][FM], fb[2][FN];
     auto read_frags = [&](int buf, const char* st, int s) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[buf][i] = read_frag(st + a_frag + i * 32 * RB, s);
+        for (int i = 0; i < FM; ++i) fa[buf][i] = frag_a(st, i, s);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[buf][j] = read_frag(st + b_frag + j * 32 * RB, s);
+        for (int j = 0; j < FN; ++j) fb[buf][j] = frag_b(st, j, s);
     };
 
     // ---- MX scales: one 32-bit register per fragment row per slice; byte 0
@@ -321,9 +425,9 @@ void tiled_gemm_kernel(GemmArgs p) {
     };
     auto read_one = [&](int buf, const char* st, int s, int x) {
         if (x < FM)
-            fa[buf][x] = read_frag(st + a_frag + x * 32 * RB, s);
+            fa[buf][x] = frag_a(st, x, s);
         else
-            fb[buf][x - FM] = read_frag(st + b_frag + (x - FM) * 32 * RB, s);
+            fb[buf][x - FM] = frag_b(st, x - FM, s);
     };
     // Register-staged copies: stg[x] holds copy x of the slice being written
     // (the copy stream's slice fg); `fc`/`foff` run one slice ahead, on the
@@ -333,7 +437,7 @@ void tiled_gemm_kernel(GemmArgs p) {
     auto load_one = [&](int x) {
         if constexpr (VG) {
             const __amdgpu_buffer_rsrc_t r = x < A_LOADS ? ra : rb;
-            const uint32_t off = x < A_LOADS ? foff(x) : foff(x - A_LOADS);
+            const uint32_t off = x < A_LOADS ? foff_a(x) : foff_b(x - A_LOADS);
             stg[x] = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
         }
     };
@@ -345,9 +449,9 @@ void tiled_gemm_kernel(GemmArgs p) {
             *(i32x4_t*)(dst + lane * 16) = stg[x];
             load_one(x);
         } else if (x < A_LOADS) {
-            copy16_to_lds(ra, sa + (4 * x + wave) * 1024, foff(x));
+            copy16_to_lds(ra, sa + (4 * x + wave) * 1024, foff_a(x));
         } else {
-            copy16_to_lds(rb, sa + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024, foff(x - A_LOADS));
+            copy16_to_lds(rb, sa + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024, foff_b(x - A_LOADS));
         }
     };
 
@@ -355,11 +459,12 @@ void tiled_gemm_kernel(GemmArgs p) {
         char* Cb = (char*)p.C + c.batch * p.stride_c;
         const int m_base = c.tm * BM + wm * WTM + l32;
         const int n_base = c.tn * BN + wn * WTN + 4 * hi;
-        const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (p.N & 3) == 0;
+        const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (p.ldc & 3) == 0;
         if constexpr (AB) {
             // Each lane reads the C values of exactly the outputs it writes,
             // so C may be the output itself (an in-place update).
-            const bool vec = (p.N & 3) == 0;
+            const bool vec = (p.ldc & 3) == 0;
+            const bool vec_c = (p.ldcin & 3) == 0;
             const bool use_c = p.beta != 0.0f;
             const int cdt = p.c_dtype;
             const int ces = cdt == 2 ? 4 : 2;
@@ -369,8 +474,8 @@ void tiled_gemm_kernel(GemmArgs p) {
             for (int i = 0; i < FM; ++i) {
                 const int m = m_base + i * 32;
                 if (m >= p.M) continue;
-                TOut* row = (TOut*)Cb + (int64_t)m * p.N;
-                const char* crow = Cinb + (int64_t)m * p.N * ces;
+                TOut* row = (TOut*)Cb + (int64_t)m * p.ldc;
+                const char* crow = Cinb + (int64_t)m * p.ldcin * ces;
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -380,7 +485,12 @@ void tiled_gemm_kernel(GemmArgs p) {
                         if (vec && n + 3 < p.N) {
                             f32x4_t v = {al * a4[4 * q], al * a4[4 * q + 1], al * a4[4 * q + 2],
                                          al * a4[4 * q + 3]};
-                            if (use_c) v += be * load4_c(crow, n, cdt);
+                            if (use_c)
+                                v += be * (vec_c ? load4_c(crow, n, cdt)
+                                                 : (f32x4_t){load1_c(crow, n, cdt),
+                                                             load1_c(crow, n + 1, cdt),
+                                                             load1_c(crow, n + 2, cdt),
+                                                             load1_c(crow, n + 3, cdt)});
                             store4<TOut>(row + n, v[0], v[1], v[2], v[3]);
                         } else {
 #pragma unroll
@@ -401,7 +511,7 @@ void tiled_gemm_kernel(GemmArgs p) {
             // read back as 16-byte row pieces, and stored so that every store
             // instruction writes whole 256-byte row segments (4 rows for
             // bf16, 2 for fp32) instead of 16-byte pieces of 32 rows.
-            if (full && (p.N * (int)sizeof(TOut)) % 16 == 0) {
+            if (full && (p.ldc * (int)sizeof(TOut)) % 16 == 0) {
                 constexpr int CHK = STG_ROWB / 16;          // 16-byte chunks per staged row
                 constexpr int RPI = kWaveSize * 16 / STG_ROWB;  // rows per store instruction
                 char* stg = lds + S * STAGE + wave * STG_BYTES;
@@ -428,7 +538,7 @@ void tiled_gemm_kernel(GemmArgs p) {
                         const int ck = lane % CHK;
                         const i32x4_t d = *(const i32x4_t*)(stg + r * STG_ROWB +
                                                             ((ck ^ (r & (CHK - 1))) * 16));
-                        char* g = Cb + ((int64_t)(c.tm * BM + wm * WTM + i * 32 + r) * p.N +
+                        char* g = Cb + ((int64_t)(c.tm * BM + wm * WTM + i * 32 + r) * p.ldc +
                                         c.tn * BN + wn * WTN) * (int64_t)sizeof(TOut) + ck * 16;
                         *(i32x4_t*)g = d;
                     }
@@ -441,7 +551,7 @@ void tiled_gemm_kernel(GemmArgs p) {
             // interior tile: one 4-wide store per (block, r / 4), no masks
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                TOut* row = (TOut*)Cb + (int64_t)(m_base + i * 32) * p.N + n_base;
+                TOut* row = (TOut*)Cb + (int64_t)(m_base + i * 32) * p.ldc + n_base;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -453,12 +563,12 @@ void tiled_gemm_kernel(GemmArgs p) {
             }
         } else {
             // edge tile: rows past M and columns past N are not written
-            const bool vec = (p.N & 3) == 0;
+            const bool vec = (p.ldc & 3) == 0;
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int m = m_base + i * 32;
                 if (m >= p.M) continue;
-                TOut* row = (TOut*)Cb + (int64_t)m * p.N;
+                TOut* row = (TOut*)Cb + (int64_t)m * p.ldc;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
 #pragma unroll

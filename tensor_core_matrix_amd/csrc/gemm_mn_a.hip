@@ -1,0 +1,7 @@
+// Kernel instances: M-major A, K-major B.
+#include "gemm_mn.h"
+
+namespace tcm {
+template hipError_t launch_gemm_mn<true, false>(int32_t, int32_t, int32_t, const GemmArgs&, int,
+                                              hipStream_t);
+}  // namespace tcm

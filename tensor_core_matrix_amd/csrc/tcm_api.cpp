@@ -50,6 +50,7 @@ using namespace tcm;
 
 constexpr int64_t kMaxK = int64_t(1) << 20;     // keeps buffer offsets within 32 bits
 constexpr int64_t kMaxMN = int64_t(1) << 30;    // row indices stay in int32
+constexpr int64_t kMaxLd = int64_t(1) << 21;    // operand leading dimensions (32-bit offsets)
 constexpr int kMaxDevices = 64;
 
 struct DeviceInfo {
@@ -93,6 +94,7 @@ int elem_bytes(tcm_dtype d) {
     case TCM_F32: return 4;
     case TCM_E4M3:
     case TCM_E8M0: return 1;
+    case TCM_E2M1: return 0;  // two per byte
     }
     return 0;
 }
@@ -154,9 +156,27 @@ int32_t choose_variant(int64_t batch, int64_t M, int64_t N, int32_t bits, int cu
     return cand[n - 1];
 }
 
-tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t bits, int cus,
-                     tcm_plan* plan, GemmArgs* args) {
-    int32_t v = choose_variant(batch, M, N, bits, cus);
+// Variants the C-input epilogue kernels run (gemm_epi.hip): the 128-row
+// tiles as chosen, every other 16-bit choice as the 256 x 256 split-3 form.
+int32_t epi_variant(int32_t v) {
+    return (v == V_T128x256 || v == V_T128x128 || v == V_T128x64) ? v : V_T256x256_SPLIT3;
+}
+
+// Variants with an M-major A or N-major B (gemm_mn.h): 256 x 256 split-3 for
+// 256-row choices, 128 x 128 otherwise (its 256-byte M/N rows are the
+// narrowest the transposing reads' bank spread allows).
+int32_t mn_variant(int32_t v) {
+    return variant_info(v).tile_m == 256 ? V_T256x256_SPLIT3 : V_T128x128;
+}
+
+// Variants of the plain family that take leading dimensions: the 4-wave
+// kernels (the ping-pong kernel steps operand rows by K).
+int32_t ld_variant(int32_t v) {
+    return variant_info(v).threads == kThreads ? v : V_T256x256_SPLIT3;
+}
+
+tcm_status plan_variant(int32_t v, int64_t batch, int64_t M, int64_t N, int64_t K, int cus,
+                        tcm_plan* plan, GemmArgs* args) {
     VariantInfo vi = variant_info(v);
     int64_t tm = cdiv(M, vi.tile_m), tn = cdiv(N, vi.tile_n);
     int64_t tiles = batch * tm * tn;
@@ -189,8 +209,16 @@ tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t bit
         args->total_tiles = (int32_t)tiles;
         args->ksteps = K > 0 ? (int32_t)cdiv(K, vi.tile_k) : 1;
         args->group_m = 4;
+        // dense storage unless the caller says otherwise
+        args->lda = args->ldb = (int32_t)K;
+        args->ldc = args->ldcin = N;
     }
     return TCM_OK;
+}
+
+tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t bits, int cus,
+                     tcm_plan* plan, GemmArgs* args) {
+    return plan_variant(choose_variant(batch, M, N, bits, cus), batch, M, N, K, cus, plan, args);
 }
 
 bool plain_pair(tcm_dtype in, tcm_dtype out) {
@@ -318,7 +346,8 @@ tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out
     if ((s = device_info(&dev)) != TCM_OK) return s;
     tcm_plan plan;
     GemmArgs a;
-    make_plan(1, M, N, K, 16, dev.cus, &plan, &a);
+    plan_variant(epi_variant(choose_variant(1, M, N, 16, dev.cus)), 1, M, N, K, dev.cus, &plan,
+                 &a);
     a.A = A;
     a.B = B;
     a.C = Out;
@@ -332,6 +361,75 @@ tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out
     a.c_dtype = (int32_t)c_dtype;
     hipError_t e = launch_gemm_epi(plan.kernel, (int32_t)dtype, (int32_t)out_dtype, a, plan.grid,
                                    (hipStream_t)stream);
+    return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
+}
+
+tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B,
+                    tcm_order b_order, int64_t ldb, const void* C, int64_t ldc, void* Out,
+                    int64_t ldo, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
+                    tcm_dtype c_dtype, tcm_dtype out_dtype, float alpha, float beta,
+                    void* stream) {
+    auto out_ok = [](tcm_dtype d) { return d == TCM_F16 || d == TCM_BF16 || d == TCM_F32; };
+    if (!(dtype == TCM_F16 || dtype == TCM_BF16) || !out_ok(out_dtype) ||
+        (beta != 0.0f && !out_ok(c_dtype)))
+        return TCM_ERR_UNSUPPORTED_DTYPE;
+    bool empty = false;
+    tcm_status s = check_sizes(1, M, N, K, &empty);
+    if (s != TCM_OK) return s;
+    auto order_ok = [](tcm_order o) { return o == TCM_ROW_MAJOR || o == TCM_COL_MAJOR; };
+    if (!order_ok(a_order) || !order_ok(b_order)) return TCM_ERR_INVALID_SHAPE;
+    // a stored row holds the matrix's columns (row-major) or its rows
+    // (column-major); every leading dimension covers at least that, and 1
+    const bool a_mn = a_order == TCM_COL_MAJOR;  // A's M index contiguous
+    const bool b_mn = b_order == TCM_ROW_MAJOR;  // B's N index contiguous
+    auto at_least = [](int64_t ld, int64_t n) { return ld >= (n > 1 ? n : 1); };
+    if (!at_least(lda, a_mn ? M : K) || !at_least(ldb, b_mn ? N : K) || !at_least(ldo, N) ||
+        (beta != 0.0f && !at_least(ldc, N)))
+        return TCM_ERR_INVALID_SHAPE;
+    if (!mul_ok(M, ldo, 1) || (beta != 0.0f && !mul_ok(M, ldc, 1))) return TCM_ERR_INVALID_SHAPE;
+    if (empty) return TCM_OK;
+    if (!Out || (K > 0 && (!A || !B)) || (beta != 0.0f && !C)) return TCM_ERR_NULL_POINTER;
+    if ((s = check_range(1, M, N, K)) != TCM_OK) return s;
+    if (lda > kMaxLd || ldb > kMaxLd) return TCM_ERR_UNSUPPORTED_SHAPE;
+    // 16-byte operand rows; a K-major operand's rows end on a whole 16-byte
+    // piece (K % 8), an M/N-major one's K is free
+    if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) ||
+        (beta != 0.0f && !aligned16(C)) || lda % 8 != 0 || ldb % 8 != 0 ||
+        ((!a_mn || !b_mn) && K % 8 != 0))
+        return TCM_ERR_MISALIGNED;
+    DeviceInfo dev;
+    if ((s = device_info(&dev)) != TCM_OK) return s;
+    const int32_t chosen = choose_variant(1, M, N, 16, dev.cus);
+    const bool plain_epi = alpha == 1.0f && beta == 0.0f && out_dtype != TCM_F16;
+    int32_t v = (a_mn || b_mn) ? mn_variant(chosen)
+                : plain_epi    ? ld_variant(chosen)
+                               : epi_variant(chosen);
+    tcm_plan plan;
+    GemmArgs a;
+    plan_variant(v, 1, M, N, K, dev.cus, &plan, &a);
+    a.A = A;
+    a.B = B;
+    a.C = Out;
+    a.lda = (int32_t)lda;
+    a.ldb = (int32_t)ldb;
+    a.ldc = ldo;
+    a.Cin = beta != 0.0f ? C : nullptr;
+    a.ldcin = beta != 0.0f ? ldc : 0;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.c_dtype = (int32_t)c_dtype;
+    hipError_t e;
+    const hipStream_t st = (hipStream_t)stream;
+    if (a_mn && b_mn)
+        e = launch_gemm_mn<true, true>(v, (int32_t)dtype, (int32_t)out_dtype, a, plan.grid, st);
+    else if (a_mn)
+        e = launch_gemm_mn<true, false>(v, (int32_t)dtype, (int32_t)out_dtype, a, plan.grid, st);
+    else if (b_mn)
+        e = launch_gemm_mn<false, true>(v, (int32_t)dtype, (int32_t)out_dtype, a, plan.grid, st);
+    else if (plain_epi)
+        e = launch_gemm_tn(v, (int32_t)dtype, (int32_t)out_dtype, a, plan.grid, st);
+    else
+        e = launch_gemm_epi(v, (int32_t)dtype, (int32_t)out_dtype, a, plan.grid, st);
     return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
 }
 

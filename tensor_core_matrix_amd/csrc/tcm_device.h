@@ -47,6 +47,18 @@ __device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCM_LDS_PTR(lds_wave_base), 4, voffset, 0, 0, 0);
 }
 
+// Transposing 8-byte LDS read of 16-bit elements (ds_read_b64_tr_b16).  The
+// lanes act in groups of 16; within a group, lane t addresses 8 bytes (4
+// elements), the group's 16 addresses forming a 4 x 16 block whose row r is
+// what lanes 4 r .. 4 r + 3 address, in lane order.  Lane t receives column t
+// of that block: element t of each of the 4 rows.  (Established on the device
+// by reading an LDS array that holds each element's own index.)
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4_t lds_read_tr16(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(p));
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -32,6 +32,13 @@ struct GemmArgs {
     int64_t stride_cin;  // bytes
     float alpha, beta;
     int32_t c_dtype;
+    // Leading dimensions in elements.  lda / ldb: from one stored row of A / B
+    // to the next (the 4-wave kernel; the ping-pong kernel takes K).  For an
+    // operand stored K-major (the TN form) a row holds K values; stored
+    // M-major (N-major for B), a row holds one k of every output row (column).
+    // ldc / ldcin: from one row of Out / of the C input to the next.
+    int32_t lda, ldb;
+    int64_t ldc, ldcin;
 };
 
 // Kernel variants.  The id is reported by tcm_plan_gemm.
@@ -74,6 +81,12 @@ hipError_t launch_gemm_tn(int32_t variant, int32_t in_dtype, int32_t out_dtype, 
 // word-aligned arrays), 2 16-byte pieces (K % 512 == 0, 16-byte-aligned arrays).
 hipError_t launch_gemm_epi(int32_t variant, int32_t in_dtype, int32_t out_dtype, const GemmArgs& a,
                            int grid, hipStream_t stream);
+// A stored M-major (A_MN) and/or B stored N-major (B_MN), C-input epilogue;
+// variants V_T256x256_SPLIT3 and V_T128x128 only.  One translation unit per
+// arrangement.
+template <bool A_MN, bool B_MN>
+hipError_t launch_gemm_mn(int32_t variant, int32_t in_dtype, int32_t out_dtype, const GemmArgs& a,
+                          int grid, hipStream_t stream);
 hipError_t launch_gemm_mx(int32_t variant, int32_t out_dtype, int32_t scale_mode, const GemmArgs& a,
                           int grid, hipStream_t stream);
 

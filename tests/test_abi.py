@@ -153,3 +153,75 @@ def test_plans_of_the_workloads():
         (256, 128, 32 * 1024, 4, 512)
     # empty problem plans nothing
     assert tcm.plan(0, 8, 8)["grid"] == 0
+
+
+ROW, COL = tcm.ROW_MAJOR, tcm.COL_MAJOR
+
+
+def call_gen(a=A, ao=ROW, lda=64, b=B, bo=COL, ldb=64, c=SA, ldc=64, o=C, ldo=64, M=64, N=64,
+             K=64, dt=tcm.BF16, cdt=tcm.F32, odt=tcm.F32, alpha=1.0, beta=0.5):
+    return tcm.lib().tcm_gemm(a, ao, lda, b, bo, ldb, c, ldc, o, ldo, M, N, K, dt, cdt, odt,
+                              alpha, beta, None)
+
+
+def test_general_entry_validation():
+    ok = (OK, NO_DEVICE)
+    assert call_gen() in ok
+    for ao in (ROW, COL):
+        for bo in (ROW, COL):
+            assert call_gen(ao=ao, bo=bo) in ok
+    # dtypes
+    assert call_gen(dt=tcm.F32) == UNSUP_DTYPE
+    assert call_gen(odt=tcm.E4M3) == UNSUP_DTYPE
+    assert call_gen(cdt=tcm.E8M0) == UNSUP_DTYPE
+    assert call_gen(cdt=tcm.E8M0, beta=0.0, c=None, ldc=0) in ok   # C unused when beta == 0
+    # orders and leading dimensions
+    assert call_gen(ao=2) == BADSHAPE
+    assert call_gen(bo=-1) == BADSHAPE
+    assert call_gen(lda=56, K=64) == BADSHAPE                      # row-major A: lda >= K
+    assert call_gen(ao=COL, lda=56, M=64, K=32) == BADSHAPE        # column-major A: lda >= M
+    assert call_gen(ao=COL, lda=64, M=64, K=200, ldb=200) in ok    # ... and K is free of lda
+    assert call_gen(bo=ROW, ldb=56, N=64) == BADSHAPE              # row-major B: ldb >= N
+    assert call_gen(bo=COL, ldb=56, K=64) == BADSHAPE              # column-major B: ldb >= K
+    assert call_gen(ldo=63) == BADSHAPE
+    assert call_gen(ldc=63) == BADSHAPE
+    assert call_gen(ldc=0, beta=0.0, c=None) in ok                 # ldc unused when beta == 0
+    assert call_gen(M=-1) == BADSHAPE
+    assert call_gen(M=0, a=None, b=None, c=None, o=None) == OK    # empty: no-op
+    assert call_gen(M=0, lda=0) == BADSHAPE                        # even then lda >= 1
+    # pointers
+    assert call_gen(o=None) == NULLP
+    assert call_gen(a=None) == NULLP
+    assert call_gen(c=None) == NULLP
+    # range
+    assert call_gen(lda=1 << 22) == UNSUP_SHAPE
+    assert call_gen(bo=ROW, ldb=(1 << 21) + 8) == UNSUP_SHAPE
+    assert call_gen(lda=1 << 21) in ok
+    # alignment: 16-byte rows and pointers; K % 8 unless both operands are M/N-major
+    assert call_gen(lda=68) == MISALIGNED
+    assert call_gen(bo=ROW, ldb=100) == MISALIGNED
+    assert call_gen(a=A + 8) == MISALIGNED
+    assert call_gen(c=SA + 4) == MISALIGNED
+    assert call_gen(K=60) == MISALIGNED
+    assert call_gen(ao=COL, bo=COL, K=60) == MISALIGNED
+    assert call_gen(ao=ROW, bo=ROW, K=60, ldb=64) == MISALIGNED
+    assert call_gen(ao=COL, bo=ROW, K=61) in ok
+    assert call_gen(ldo=67, ldc=65) in ok                         # Out / C rows are free
+
+
+def test_order_ld_of_views():
+    import torch
+    x = torch.empty(40, 24)
+    assert tcm.order_ld(x) == (ROW, 24)
+    assert tcm.order_ld(x.T) == (COL, 24)
+    assert tcm.order_ld(x[:, :16]) == (ROW, 24)
+    assert tcm.order_ld(x[:16, :].T) == (COL, 24)
+    with pytest.raises(ValueError):
+        tcm.order_ld(x[::2, ::2])
+
+
+def test_order_ld_of_single_column_and_row_views():
+    import torch
+    st = torch.empty(1, 304)                 # one stored row of 304
+    assert tcm.order_ld(st[:, :300].T) == (COL, 304)   # a 300 x 1 column-major view
+    assert tcm.order_ld(st[:, :300]) == (ROW, 304)     # a 1 x 300 row-major view
