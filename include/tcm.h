@@ -146,8 +146,8 @@ tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out
  * (same pointer, dtype and leading dimension).  Row-major A with
  * column-major B (lda = ldb = K, ldo = N) is tcm_gemm_tn's operation.
  * Every leading dimension must be at least 1 and at least the size named
- * above (TCM_ERR_INVALID_SHAPE), lda and ldb at most 2^21
- * (TCM_ERR_UNSUPPORTED_SHAPE); an order other than the two gives
+ * above (TCM_ERR_INVALID_SHAPE), lda and ldb at most 2^21 and ldo and ldc
+ * below 2^31 (TCM_ERR_UNSUPPORTED_SHAPE); an order other than the two gives
  * TCM_ERR_INVALID_SHAPE.  Alignment: A, B, Out (and C when read) 16-byte
  * aligned, lda and ldb multiples of 8 elements, and K a multiple of 8 unless
  * A is column-major and B row-major (TCM_ERR_MISALIGNED); ldo and ldc are

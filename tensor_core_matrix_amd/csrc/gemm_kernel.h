@@ -118,10 +118,14 @@ struct TileCursor {
 // AB builds the epilogue with a C input: Out = alpha * (A B^T) + beta * C,
 // combined in fp32 in the accumulator layout and rounded once to TOut.
 // A_MN (B_MN): A (B) is stored M-major (N-major): K rows of lda (ldb)
-// elements, the tile's BM (BN) values of one k contiguous.
+// elements, the tile's BM (BN) values of one k contiguous.  DENSE: both
+// operands K-major with rows K apart and Out's rows N apart; the kernel then
+// ignores the leading dimensions, so one register holds the copy offsets of
+// both operands and no argument register is added (the 256 x 256 kernels
+// with the LDS-staged epilogue have none to spare: one more spills).
 template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int SWZ,
           bool SCALE_WORDS = false, int NSPLIT = 1, bool EPI_LDS = false, bool VG = false,
-          bool AB = false, bool A_MN = false, bool B_MN = false>
+          bool AB = false, bool A_MN = false, bool B_MN = false, bool DENSE = true>
 __global__ __launch_bounds__(kThreads, OCC) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void tiled_gemm_kernel(GemmArgs p) {
     constexpr int ESZ = Op::kElemBytes;
@@ -156,6 +160,7 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert(Op::kElemBits >= 8, "whole-byte elements");
     constexpr bool ANY_MN = A_MN || B_MN;
     static_assert(!ANY_MN || (ESZ == 2 && !Op::kScaled && !VG), "M/N-major: 16-bit, DMA copies");
+    static_assert(!(DENSE && ANY_MN), "dense storage: both operands K-major");
     static_assert((!A_MN || BM * ESZ >= 256) && (!B_MN || BN * ESZ >= 256),
                   "M/N-major rows of at least 16 chunks (bank spread of the transposing reads)");
 
@@ -205,8 +210,10 @@ void tiled_gemm_kernel(GemmArgs p) {
         const int ch = (lane % cpr) ^ (4 * (row & 3));
         return {(uint32_t)row * (uint32_t)ld * ESZ + ch * 16, 4u * rpw * (uint32_t)ld * ESZ};
     };
-    const CopyGeo geo_a = A_MN ? mn_geo(BM, p.lda) : kmajor_geo(p.lda);
-    const CopyGeo geo_b = B_MN ? mn_geo(BN, p.ldb) : kmajor_geo(p.ldb);
+    const int lda = DENSE ? K : p.lda;
+    const int ldb = DENSE ? K : p.ldb;
+    const CopyGeo geo_a = A_MN ? mn_geo(BM, lda) : kmajor_geo(lda);
+    const CopyGeo geo_b = B_MN ? mn_geo(BN, ldb) : kmajor_geo(ldb);
 
     auto locate = [&](TileCursor& c) {
         tile_coords(p, c.tl * G + lid, c.batch, c.tm, c.tn);
@@ -243,13 +250,13 @@ void tiled_gemm_kernel(GemmArgs p) {
         const char* abase = (const char*)p.A + fc.batch * p.stride_a;
         const char* bbase = (const char*)p.B + fc.batch * p.stride_b;
         if constexpr (A_MN)
-            ra = mn_rsrc(abase, fc.tm * BM, p.M, BM, p.lda, fc.kk * BK);
+            ra = mn_rsrc(abase, fc.tm * BM, p.M, BM, lda, fc.kk * BK);
         else
-            ra = kmajor_rsrc(abase, fc.tm * BM, p.M, BM, p.lda);
+            ra = kmajor_rsrc(abase, fc.tm * BM, p.M, BM, lda);
         if constexpr (B_MN)
-            rb = mn_rsrc(bbase, fc.tn * BN, p.N, BN, p.ldb, fc.kk * BK);
+            rb = mn_rsrc(bbase, fc.tn * BN, p.N, BN, ldb, fc.kk * BK);
         else
-            rb = kmajor_rsrc(bbase, fc.tn * BN, p.N, BN, p.ldb);
+            rb = kmajor_rsrc(bbase, fc.tn * BN, p.N, BN, ldb);
     };
     auto feed_advance = [&]() {
         if (++fc.kk == p.ksteps) {
@@ -275,19 +282,33 @@ void tiled_gemm_kernel(GemmArgs p) {
         const bool kin = fc.kk * BK + cp_k < K;
         foff_a0 = A_MN ? (live ? geo_a.off : kOutOfRange)
                        : (live && kin ? geo_a.off + k0b : kOutOfRange);
-        foff_b0 = B_MN ? (live ? geo_b.off : kOutOfRange)
-                       : (live && kin ? geo_b.off + k0b : kOutOfRange);
+        if constexpr (!DENSE)
+            foff_b0 = B_MN ? (live ? geo_b.off : kOutOfRange)
+                           : (live && kin ? geo_b.off + k0b : kOutOfRange);
     };
     auto foff_a = [&](int i) -> uint32_t { return foff_a0 + (uint32_t)i * geo_a.step; };
-    auto foff_b = [&](int i) -> uint32_t { return foff_b0 + (uint32_t)i * geo_b.step; };
+    auto foff_b = [&](int i) -> uint32_t {
+        if constexpr (DENSE)
+            return foff_a(i);
+        else
+            return foff_b0 + (uint32_t)i * geo_b.step;
+    };
+    // One 16-byte copy per lane; kernels with transposing reads issue it in
+    // the assembly form (see copy16_to_lds_asm).
+    auto dma = [&](__amdgpu_buffer_rsrc_t r, char* dst, uint32_t off) {
+        if constexpr (ANY_MN)
+            copy16_to_lds_asm(r, dst, off);
+        else
+            copy16_to_lds(r, dst, off);
+    };
     // Copies of the stream's current slice into ring stage `st`.
     auto issue = [&](int st) {
         char* sa = lds + st * STAGE;
         char* sb = sa + A_BYTES;
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) copy16_to_lds(ra, sa + (4 * i + wave) * 1024, foff_a(i));
+        for (int i = 0; i < A_LOADS; ++i) dma(ra, sa + (4 * i + wave) * 1024, foff_a(i));
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) copy16_to_lds(rb, sb + (4 * i + wave) * 1024, foff_b(i));
+        for (int i = 0; i < B_LOADS; ++i) dma(rb, sb + (4 * i + wave) * 1024, foff_b(i));
     };
 
     // ---- per-lane fragment geometry ---------------------------------------
@@ -449,21 +470,24 @@ void tiled_gemm_kernel(GemmArgs p) {
             *(i32x4_t*)(dst + lane * 16) = stg[x];
             load_one(x);
         } else if (x < A_LOADS) {
-            copy16_to_lds(ra, sa + (4 * x + wave) * 1024, foff_a(x));
+            dma(ra, sa + (4 * x + wave) * 1024, foff_a(x));
         } else {
-            copy16_to_lds(rb, sa + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024, foff_b(x - A_LOADS));
+            dma(rb, sa + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024, foff_b(x - A_LOADS));
         }
     };
 
     auto epilogue = [&](const TileCursor& c) {
+        // Out's row stride, read from the arguments here (a value held from
+        // the kernel's start costs the main loop a register)
+        const int ldc = DENSE ? p.N : p.ldc;
         char* Cb = (char*)p.C + c.batch * p.stride_c;
         const int m_base = c.tm * BM + wm * WTM + l32;
         const int n_base = c.tn * BN + wn * WTN + 4 * hi;
-        const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (p.ldc & 3) == 0;
+        const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (ldc & 3) == 0;
         if constexpr (AB) {
             // Each lane reads the C values of exactly the outputs it writes,
             // so C may be the output itself (an in-place update).
-            const bool vec = (p.ldc & 3) == 0;
+            const bool vec = (ldc & 3) == 0;
             const bool vec_c = (p.ldcin & 3) == 0;
             const bool use_c = p.beta != 0.0f;
             const int cdt = p.c_dtype;
@@ -474,7 +498,7 @@ void tiled_gemm_kernel(GemmArgs p) {
             for (int i = 0; i < FM; ++i) {
                 const int m = m_base + i * 32;
                 if (m >= p.M) continue;
-                TOut* row = (TOut*)Cb + (int64_t)m * p.ldc;
+                TOut* row = (TOut*)Cb + (int64_t)m * ldc;
                 const char* crow = Cinb + (int64_t)m * p.ldcin * ces;
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
@@ -511,7 +535,7 @@ void tiled_gemm_kernel(GemmArgs p) {
             // read back as 16-byte row pieces, and stored so that every store
             // instruction writes whole 256-byte row segments (4 rows for
             // bf16, 2 for fp32) instead of 16-byte pieces of 32 rows.
-            if (full && (p.ldc * (int)sizeof(TOut)) % 16 == 0) {
+            if (full && (ldc * (int)sizeof(TOut)) % 16 == 0) {
                 constexpr int CHK = STG_ROWB / 16;          // 16-byte chunks per staged row
                 constexpr int RPI = kWaveSize * 16 / STG_ROWB;  // rows per store instruction
                 char* stg = lds + S * STAGE + wave * STG_BYTES;
@@ -538,7 +562,7 @@ void tiled_gemm_kernel(GemmArgs p) {
                         const int ck = lane % CHK;
                         const i32x4_t d = *(const i32x4_t*)(stg + r * STG_ROWB +
                                                             ((ck ^ (r & (CHK - 1))) * 16));
-                        char* g = Cb + ((int64_t)(c.tm * BM + wm * WTM + i * 32 + r) * p.ldc +
+                        char* g = Cb + ((int64_t)(c.tm * BM + wm * WTM + i * 32 + r) * ldc +
                                         c.tn * BN + wn * WTN) * (int64_t)sizeof(TOut) + ck * 16;
                         *(i32x4_t*)g = d;
                     }
@@ -551,7 +575,7 @@ void tiled_gemm_kernel(GemmArgs p) {
             // interior tile: one 4-wide store per (block, r / 4), no masks
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                TOut* row = (TOut*)Cb + (int64_t)(m_base + i * 32) * p.ldc + n_base;
+                TOut* row = (TOut*)Cb + (int64_t)(m_base + i * 32) * ldc + n_base;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -563,12 +587,12 @@ void tiled_gemm_kernel(GemmArgs p) {
             }
         } else {
             // edge tile: rows past M and columns past N are not written
-            const bool vec = (p.ldc & 3) == 0;
+            const bool vec = (ldc & 3) == 0;
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int m = m_base + i * 32;
                 if (m >= p.M) continue;
-                TOut* row = (TOut*)Cb + (int64_t)m * p.ldc;
+                TOut* row = (TOut*)Cb + (int64_t)m * ldc;
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
 #pragma unroll

@@ -388,7 +388,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
         const int col0 = c.tn * BN + sub * WTN;
         const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N;
         if constexpr (EPI_LDS) {
-            if (full && (p.ldc * (int)sizeof(TOut)) % 16 == 0) {
+            if (full && (p.N * (int)sizeof(TOut)) % 16 == 0) {
                 // each block of STG_ROWS rows: MFMA layout -> staging ->
                 // whole row pieces (lane l holds row l % 32 of a 32-row block)
                 constexpr int CHK = STG_ROWB / 16;
@@ -420,7 +420,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
                             const i32x4_t d = *(const i32x4_t*)(stg + r * STG_ROWB +
                                                                 ((ck ^ (r & (CHK - 1))) * 16));
                             char* g = Cb +
-                                      ((int64_t)(row0 + i * 32 + h * STG_ROWS + r) * p.ldc + col0) *
+                                      ((int64_t)(row0 + i * 32 + h * STG_ROWS + r) * p.N + col0) *
                                           (int64_t)sizeof(TOut) +
                                       ck * 16;
                             *(i32x4_t*)g = d;
@@ -431,12 +431,12 @@ void pingpong_gemm_kernel(GemmArgs p) {
                 return;
             }
         }
-        const bool vec = (p.ldc & 3) == 0;
+        const bool vec = (p.N & 3) == 0;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int m = row0 + i * 32 + l32;
             if (m >= p.M) continue;
-            TOut* row = (TOut*)Cb + (int64_t)m * p.ldc;
+            TOut* row = (TOut*)Cb + (int64_t)m * p.N;
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll

@@ -169,12 +169,6 @@ int32_t mn_variant(int32_t v) {
     return variant_info(v).tile_m == 256 ? V_T256x256_SPLIT3 : V_T128x128;
 }
 
-// Variants of the plain family that take leading dimensions: the 4-wave
-// kernels (the ping-pong kernel steps operand rows by K).
-int32_t ld_variant(int32_t v) {
-    return variant_info(v).threads == kThreads ? v : V_T256x256_SPLIT3;
-}
-
 tcm_status plan_variant(int32_t v, int64_t batch, int64_t M, int64_t N, int64_t K, int cus,
                         tcm_plan* plan, GemmArgs* args) {
     VariantInfo vi = variant_info(v);
@@ -211,7 +205,7 @@ tcm_status plan_variant(int32_t v, int64_t batch, int64_t M, int64_t N, int64_t 
         args->group_m = 4;
         // dense storage unless the caller says otherwise
         args->lda = args->ldb = (int32_t)K;
-        args->ldc = args->ldcin = N;
+        args->ldc = args->ldcin = (int32_t)N;
     }
     return TCM_OK;
 }
@@ -390,7 +384,8 @@ tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B
     if (empty) return TCM_OK;
     if (!Out || (K > 0 && (!A || !B)) || (beta != 0.0f && !C)) return TCM_ERR_NULL_POINTER;
     if ((s = check_range(1, M, N, K)) != TCM_OK) return s;
-    if (lda > kMaxLd || ldb > kMaxLd) return TCM_ERR_UNSUPPORTED_SHAPE;
+    if (lda > kMaxLd || ldb > kMaxLd || ldo > INT32_MAX || (beta != 0.0f && ldc > INT32_MAX))
+        return TCM_ERR_UNSUPPORTED_SHAPE;
     // 16-byte operand rows; a K-major operand's rows end on a whole 16-byte
     // piece (K % 8), an M/N-major one's K is free
     if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) ||
@@ -400,9 +395,11 @@ tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B
     DeviceInfo dev;
     if ((s = device_info(&dev)) != TCM_OK) return s;
     const int32_t chosen = choose_variant(1, M, N, 16, dev.cus);
-    const bool plain_epi = alpha == 1.0f && beta == 0.0f && out_dtype != TCM_F16;
+    // the plain kernels read dense storage only (rows K and N apart)
+    const bool plain_epi = alpha == 1.0f && beta == 0.0f && out_dtype != TCM_F16 && lda == K &&
+                           ldb == K && ldo == N;
     int32_t v = (a_mn || b_mn) ? mn_variant(chosen)
-                : plain_epi    ? ld_variant(chosen)
+                : plain_epi    ? chosen
                                : epi_variant(chosen);
     tcm_plan plan;
     GemmArgs a;
@@ -412,9 +409,9 @@ tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B
     a.C = Out;
     a.lda = (int32_t)lda;
     a.ldb = (int32_t)ldb;
-    a.ldc = ldo;
+    a.ldc = (int32_t)ldo;
     a.Cin = beta != 0.0f ? C : nullptr;
-    a.ldcin = beta != 0.0f ? ldc : 0;
+    a.ldcin = beta != 0.0f ? (int32_t)ldc : 0;
     a.alpha = alpha;
     a.beta = beta;
     a.c_dtype = (int32_t)c_dtype;

@@ -40,6 +40,24 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCM_LDS_PTR(lds_wave_base), 16, voffset, 0, 0, 0);
 }
 
+// The same 16-byte copy written as inline assembly, for kernels that read LDS
+// with transposing reads.  After a copy issued through the builtin, the
+// compiler waits for every copy in flight (vmcnt(0)) before each transposing
+// read, which it cannot tell apart from the copy's destination; that wait
+// would drain the copy pipeline at every fragment read.  Kernels order their
+// copies and reads with explicit vmcnt waits and a barrier before a stage is
+// read, so the assembly form changes no ordering they rely on.  M0 (the LDS
+// destination) is an input, so the compiler sets it; one wait state after
+// the M0 write precedes the copy, which reads M0.
+__device__ __forceinline__ void copy16_to_lds_asm(__amdgpu_buffer_rsrc_t r, void* lds_wave_base,
+                                                  uint32_t voffset) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(r), "{m0}"(m0)
+                 : "memory");
+}
+
 // 4 bytes per lane from the buffer into LDS: the wave fills 256 bytes
 // contiguously from `lds_wave_base` (lane l writes bytes [4 l, 4 l + 4)).
 __device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_wave_base,

@@ -33,12 +33,13 @@ struct GemmArgs {
     float alpha, beta;
     int32_t c_dtype;
     // Leading dimensions in elements.  lda / ldb: from one stored row of A / B
-    // to the next (the 4-wave kernel; the ping-pong kernel takes K).  For an
+    // to the next (the 4-wave kernels built for them; the dense instances
+    // and the ping-pong kernel take K, and N for ldc).  For an
     // operand stored K-major (the TN form) a row holds K values; stored
     // M-major (N-major for B), a row holds one k of every output row (column).
     // ldc / ldcin: from one row of Out / of the C input to the next.
     int32_t lda, ldb;
-    int64_t ldc, ldcin;
+    int32_t ldc, ldcin;
 };
 
 // Kernel variants.  The id is reported by tcm_plan_gemm.

@@ -197,6 +197,7 @@ def test_general_entry_validation():
     assert call_gen(lda=1 << 22) == UNSUP_SHAPE
     assert call_gen(bo=ROW, ldb=(1 << 21) + 8) == UNSUP_SHAPE
     assert call_gen(lda=1 << 21) in ok
+    assert call_gen(ldo=1 << 31) == UNSUP_SHAPE
     # alignment: 16-byte rows and pointers; K % 8 unless both operands are M/N-major
     assert call_gen(lda=68) == MISALIGNED
     assert call_gen(bo=ROW, ldb=100) == MISALIGNED
