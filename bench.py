@@ -7,7 +7,8 @@ A step is one call of the product on the headline workload: bfloat16
 8192 x 8192 x 8192, fp32 accumulation, bf16 output (persistent 256 x 256 x 64
 tiles), inputs N(0,1)*0.05 from seed 3, already resident in HBM.  The other
 measured workloads (MXFP8 8192^3, bf16 4096^3, 1024 batched 128x256x64 and
-the 128x64x64 single tile) are timed after it and reported in the same line.
+the 128x64x64 single tile, and bf16 8192^3 with both operands row-major) are
+timed after it and reported in the same line.
 
 Prints ONE JSON line.  `roofline` describes the dominant kernel: achieved =
 algorithmic flops per launch / mean launch time (HIP events on the launch
@@ -33,7 +34,8 @@ METRIC = "GEMM TFLOP/s and % of MFMA dense peak (bf16 8192³; MXFP8 8192³)"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.3}  # dense MFMA, MI355X
 HBM_GBS = 8000.0
 KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pingpong.h", "tcm_device.h", "tcm_internal.h", "gemm_tn.hip",
-                  "gemm_mx.hip", "tcm_api.cpp"]
+                  "gemm_mx.hip", "gemm_epi.hip", "gemm_mn.h", "gemm_mn_a.hip", "gemm_mn_b.hip",
+                  "gemm_mn_ab.hip", "tcm_api.cpp"]
 
 
 def kernel_hash() -> str:
@@ -91,6 +93,10 @@ def prepare(name, torch, inp, tcm):
     elif w.batch > 1:
         out = torch.empty(w.batch, w.M, w.N, dtype=odt, device="cuda")
         fn = lambda: tcm.batched_gemm_tn(x["A"], x["B"], out)
+    elif w.b_order == "row":
+        # A . B with B stored K x N: the general entry, N-major B
+        out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
+        fn = lambda: tcm.gemm(x["A"], x["B"], out=out)
     else:
         out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
         fn = lambda: tcm.gemm_tn(x["A"], x["B"], out)
@@ -166,7 +172,8 @@ def main() -> int:
     from tensor_core_matrix_amd import inputs as inp
 
     tcm.lib()
-    order = ["bf16_8192", "mxfp8_8192", "mxfp4_8192", "bf16_4096", "batched", "tile_f16"]
+    order = ["bf16_8192", "mxfp8_8192", "mxfp4_8192", "bf16_8192_nn", "bf16_4096", "batched",
+             "tile_f16"]
     if args.only:
         order = [args.only]
     results = {}

@@ -21,6 +21,11 @@ problems):
   seed 4, bf16 output ("Hopper and Blackwell GEMM", block-scaling table).
 * ``mxfp4_8192`` -- the same with E2M1 elements (MXFP4, the table's 4-bit
   row): every 4-bit code equally likely, seed 5, bf16 output.
+* ``bf16_8192_nn`` -- A 8192x8192 and B 8192x8192 bfloat16, both row-major
+  (B stored K x N, its N index contiguous: the product A . B of two
+  row-major matrices), N(0,1)*0.05, seed 6, bf16 output ("API Card:
+  Blackwell Pipeline (tcgen05)", Descriptor.: 16-bit types in either
+  majorness).
 """
 from __future__ import annotations
 
@@ -44,6 +49,7 @@ class Workload:
     dist: str           # "uniform", "normal" or "codes" (every code equally likely)
     sigma: float = 1.0
     scale_exp: tuple = field(default=(-4, 4))
+    b_order: str = "col"  # "col": B stored N x K (the TN form); "row": stored K x N
 
     @property
     def flops(self) -> int:
@@ -57,6 +63,8 @@ WORKLOADS = {
     "bf16_8192": Workload("bf16_8192", 1, 8192, 8192, 8192, "bf16", "bf16", 3, "normal", 0.05),
     "mxfp8_8192": Workload("mxfp8_8192", 1, 8192, 8192, 8192, "e4m3", "bf16", 4, "normal", 1.0),
     "mxfp4_8192": Workload("mxfp4_8192", 1, 8192, 8192, 8192, "e2m1", "bf16", 5, "codes"),
+    "bf16_8192_nn": Workload("bf16_8192_nn", 1, 8192, 8192, 8192, "bf16", "bf16", 6, "normal", 0.05,
+                             b_order="row"),
 }
 
 TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
@@ -111,7 +119,8 @@ def make(w: Workload | str) -> dict:
         w = WORKLOADS[w]
     g = generator(w.seed)
     lead = (w.batch,) if w.batch > 1 else ()
-    shp_a, shp_b = lead + (w.M, w.K), lead + (w.N, w.K)
+    shp_a = lead + (w.M, w.K)
+    shp_b = lead + ((w.K, w.N) if w.b_order == "row" else (w.N, w.K))
     if w.dtype in ("e4m3", "e2m1"):
         if w.dtype == "e4m3":
             a = e4m3_normal(shp_a, g, w.sigma)
