@@ -449,3 +449,42 @@ int oracle_entries_ld(int dtype, const void* A, int a_order, int64_t lda, const 
     }
     return 0;
 }
+
+/*
+ * Per-element operation of the epilogue.  "API Card: Blackwell Pipeline
+ * (tcgen05)", "Device side.", lists process_and_store(out, op) among the
+ * epilogue accessors: an operation applied to every result element as it is
+ * stored.  The pages name no particular operation; this oracle defines the
+ * usual activation functions from their mathematical definitions, applied to
+ * the finished value alpha * sum + beta * c:
+ *
+ *   0 identity   x
+ *   1 relu       x if x > 0, else 0
+ *   2 gelu_tanh  x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))
+ *                (the tanh form of the Gaussian error linear unit,
+ *                Hendrycks and Gimpel)
+ *   3 gelu_erf   x * Phi(x) = x/2 * erfc(-x / sqrt(2))   (Phi the standard
+ *                normal distribution function; erfc avoids cancelling
+ *                1 + erf for negative x)
+ *   4 silu       x / (1 + exp(-x))
+ *
+ * fp64 with the C library's tanh, erfc and exp.
+ */
+int oracle_apply_op(int64_t n, int op, const double* x, double* out) {
+    if (n < 0 || (n > 0 && (!x || !out)) || op < 0 || op > 4)
+        return -1;
+    const double k_tanh = sqrt(2.0 / (4.0 * atan(1.0)));  /* sqrt(2 / pi) */
+    for (int64_t t = 0; t < n; ++t) {
+        const double v = x[t];
+        double y;
+        switch (op) {
+        case 1: y = v > 0.0 ? v : 0.0; break;
+        case 2: y = 0.5 * v * (1.0 + tanh(k_tanh * (v + 0.044715 * v * v * v))); break;
+        case 3: y = 0.5 * v * erfc(-v / sqrt(2.0)); break;
+        case 4: y = v / (1.0 + exp(-v)); break;
+        default: y = v;
+        }
+        out[t] = y;
+    }
+    return 0;
+}

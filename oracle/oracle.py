@@ -79,9 +79,10 @@ def _load():
                                            ci]
             lib.oracle_entries_ld.argtypes = [ci, vp, ci, i64, vp, ci, i64, i64, i64, i64, vp,
                                               vp, i64, dp, dp]
+            lib.oracle_apply_op.argtypes = [i64, ci, dp, dp]
             for f in (lib.oracle_decode, lib.oracle_gemm_tn, lib.oracle_gemm_mx,
                       lib.oracle_gemm_mx_typed, lib.oracle_entries, lib.oracle_axpby,
-                      lib.oracle_gemm_ld, lib.oracle_entries_ld):
+                      lib.oracle_gemm_ld, lib.oracle_entries_ld, lib.oracle_apply_op):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -256,6 +257,22 @@ def axpby(alpha: float, ref: np.ndarray, beta: float = 0.0, c: np.ndarray | None
     return out
 
 
+OPS = {"identity": 0, "relu": 1, "gelu_tanh": 2, "gelu_erf": 3, "silu": 4}
+# Largest |op'(x)| over all x: 1 for identity and relu; silu's maximum is
+# 1.0998 (at x = 2.3994), both gelu forms' 1.1289 (near x = 1.41).
+OP_LIPSCHITZ = {0: 1.0, 1: 1.0, 2: 1.13, 3: 1.13, 4: 1.1}
+
+
+def apply_op(op: int, x: np.ndarray) -> np.ndarray:
+    """The epilogue's per-element operation in fp64 (see oracle.c)."""
+    x = np.ascontiguousarray(x, np.float64)
+    out = np.empty_like(x)
+    rc = _load().oracle_apply_op(x.size, int(op), _ptr(x), _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_apply_op failed ({rc})")
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Comparison rule
 # ----------------------------------------------------------------------------
@@ -304,6 +321,42 @@ def check_epi(gpu, exact, alpha, abssum, beta_c, out: str):
     gpu = np.asarray(gpu, np.float64)
     bnd = bound_epi(exact, alpha, abssum, beta_c, out)
     err = np.abs(gpu - np.asarray(exact, np.float64))
+    finite = np.isfinite(gpu)
+    bad = ~finite | (err > bnd)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bnd > 0, err / bnd, np.where(err > 0, np.inf, 0.0))
+    ratio = np.where(finite, ratio, np.inf)
+    return int(bad.sum()) == 0, float(ratio.max()) if ratio.size else 0.0, int(bad.sum())
+
+
+def bound_op(exact: np.ndarray, op: int, alpha: float, abssum: np.ndarray, beta_c: np.ndarray,
+             out: str) -> np.ndarray:
+    """Acceptance bound of Out = op(alpha * (A B) + beta * C): the fp32 sum and
+    combine errors of bound_epi (without its output rounding) carried through
+    op with op's largest slope, plus 2^-20 (|x| + |op(x)|) for op evaluated in
+    fp32 with the hardware exp / reciprocal and a polynomial erf, plus one
+    ulp of a bf16 or fp16 output at op(x).  `exact` is alpha * sum + beta * c."""
+    x = np.asarray(exact, np.float64)
+    y = apply_op(op, x)
+    b = abs(alpha) * REL_TOL * np.asarray(abssum, np.float64)
+    b = b + 2.0 ** -22 * (np.abs(x) + np.abs(np.asarray(beta_c, np.float64)))
+    b = OP_LIPSCHITZ[int(op)] * b
+    if op:
+        b = b + 2.0 ** -20 * (np.abs(x) + np.abs(y))
+    if out == "bf16":
+        b = b + ulp_bf16(y)
+    elif out == "f16":
+        b = b + ulp_f16(y)
+    return b
+
+
+def check_op(gpu, exact, op, alpha, abssum, beta_c, out: str):
+    """Elementwise acceptance of the epilogue with a per-element op;
+    (ok, worst err/bound, n bad).  `exact` is the value before op."""
+    gpu = np.asarray(gpu, np.float64)
+    want = apply_op(op, exact)
+    bnd = bound_op(exact, op, alpha, abssum, beta_c, out)
+    err = np.abs(gpu - want)
     finite = np.isfinite(gpu)
     bad = ~finite | (err > bnd)
     with np.errstate(divide="ignore", invalid="ignore"):

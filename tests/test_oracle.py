@@ -22,7 +22,12 @@ applied to the wrong block -- fails at least one of them:
 * operand arrangements and leading dimensions: every row-/column-major pair,
   stored through torch's own transposes inside NaN-padded rows, equals the
   pinned TN product bit for bit (a swapped index or an ignored leading
-  dimension reads a NaN or a wrong element).
+  dimension reads a NaN or a wrong element);
+* the epilogue's per-element operations: relu's closed form; x * Phi(x)
+  against printed standard normal table values; op(x) - op(-x) = x for the
+  odd-part forms (gelu, silu); silu at +-ln 3, where the logistic function is
+  3/4 and 1/4; the tanh form of gelu within its known 5e-4 of the erf form,
+  and both approaching x and 0 in the tails.
 """
 from fractions import Fraction
 
@@ -437,6 +442,75 @@ def test_planted_arrangement_mistakes_fail_the_pin():
     wrong_ld, _ = orc.gemm_ld(orc.BF16, inp.raw(ast), orc.COL_MAJOR, M, inp.raw(bst),
                               orc.ROW_MAJOR, ldb, M, N, K)
     assert not _same(wrong_ld, want)
+
+
+# --------------------------------------------- per-element epilogue ops
+def test_op_relu_and_identity_closed_form():
+    x = np.array([-3.5, -1e-30, 0.0, 1e-30, 2.25, 7.0])
+    assert np.array_equal(orc.apply_op(orc.OPS["identity"], x), x)
+    assert np.array_equal(orc.apply_op(orc.OPS["relu"], x), [0, 0, 0, 1e-30, 2.25, 7.0])
+
+
+def test_op_gelu_erf_is_x_times_normal_cdf():
+    # standard normal distribution function Phi at 1, 2, -1 and 0.5, as
+    # printed in statistical tables
+    phi = {1.0: 0.8413447460685429, 2.0: 0.9772498680518208, -1.0: 0.15865525393145707,
+           0.5: 0.6914624612740131}
+    x = np.array(list(phi))
+    got = orc.apply_op(orc.OPS["gelu_erf"], x)
+    assert np.allclose(got, x * np.array(list(phi.values())), rtol=1e-14, atol=0)
+    # deep in the negative tail erfc keeps full relative accuracy:
+    # Phi(-10) = 7.619853024160527e-24
+    assert abs(orc.apply_op(3, np.array([-10.0]))[0] / (-10 * 7.619853024160527e-24) - 1) < 1e-12
+
+
+@pytest.mark.parametrize("name", ["gelu_tanh", "gelu_erf", "silu"])
+def test_op_odd_part_identity(name):
+    """x/2 (1 + f(x)) with f odd gives op(x) - op(-x) = x."""
+    x = np.linspace(-9, 9, 181)
+    d = orc.apply_op(orc.OPS[name], x) - orc.apply_op(orc.OPS[name], -x)
+    assert np.allclose(d, x, rtol=0, atol=1e-13)
+
+
+def test_op_silu_at_log3():
+    # logistic(ln 3) = 3/4, logistic(-ln 3) = 1/4
+    l3 = np.log(3.0)
+    got = orc.apply_op(orc.OPS["silu"], np.array([l3, -l3, 0.0]))
+    assert np.allclose(got, [0.75 * l3, -0.25 * l3, 0.0], rtol=1e-15, atol=0)
+
+
+def test_op_gelu_tanh_approximates_gelu_erf():
+    x = np.linspace(-8, 8, 3201)
+    t = orc.apply_op(orc.OPS["gelu_tanh"], x)
+    e = orc.apply_op(orc.OPS["gelu_erf"], x)
+    err = np.abs(t - e)
+    assert err.max() < 5e-4 and err.max() > 1e-5    # the known quality of the tanh form
+    assert np.allclose(t[-1], 8.0, atol=1e-12) and abs(t[0]) < 1e-12
+    assert orc.apply_op(2, np.array([0.0]))[0] == 0.0
+
+
+def test_planted_op_mistakes_fail_the_pins():
+    """Planted on the CPU: gelu with erf(x) in place of erf(x/sqrt 2), and the
+    tanh form without its cubic term, miss the table value and the 5e-4
+    agreement."""
+    from math import erf, tanh, sqrt, pi
+    wrong = 0.5 * 1.0 * (1 + erf(1.0))
+    assert abs(wrong - 0.8413447460685429) > 1e-3
+    x = np.linspace(-8, 8, 3201)
+    no_cube = 0.5 * x * (1 + np.tanh(sqrt(2 / pi) * x))
+    assert np.abs(no_cube - orc.apply_op(3, x)).max() > 5e-4
+
+
+def test_check_op_rule():
+    x = np.array([-2.0, -0.5, 0.0, 0.5, 3.0])
+    y = orc.apply_op(orc.OPS["gelu_erf"], x)
+    ok, worst, nbad = orc.check_op(y, x, 3, 1.0, np.ones(5), np.zeros(5), "f32")
+    assert ok and worst == 0.0
+    ok, _, nbad = orc.check_op(y + 1e-3, x, 3, 1.0, np.ones(5), np.zeros(5), "f32")
+    assert not ok and nbad == 5
+    ok, _, _ = orc.check_op(np.array([np.nan]), np.array([1.0]), 1, 1.0, np.ones(1), np.zeros(1),
+                            "f32")
+    assert not ok
 
 
 # ----------------------------------------------------- axpby epilogue
