@@ -66,7 +66,8 @@ typedef enum tcm_status {
     TCM_ERR_MISALIGNED = 4,        /* pointer or row length not 16-byte aligned */
     TCM_ERR_UNSUPPORTED_DTYPE = 5, /* dtype / out_dtype pair not supported */
     TCM_ERR_NO_DEVICE = 6,         /* no HIP device, or it is not gfx950 */
-    TCM_ERR_HIP = 7                /* a HIP runtime call or kernel launch failed */
+    TCM_ERR_HIP = 7,               /* a HIP runtime call or kernel launch failed */
+    TCM_ERR_INVALID_ARGUMENT = 8   /* an enumeration argument outside its values */
 } tcm_status;
 
 typedef enum tcm_dtype {
@@ -86,6 +87,18 @@ typedef enum tcm_order {
     TCM_ROW_MAJOR = 0,
     TCM_COL_MAJOR = 1
 } tcm_order;
+
+/* Per-element operation of the epilogue ("API Card: Blackwell Pipeline
+ * (tcgen05)", "Device side.": process_and_store(out, op)), applied in fp32 to
+ * the finished value x = alpha * sum + beta * c before the rounding to the
+ * output type. */
+typedef enum tcm_op {
+    TCM_OP_IDENTITY = 0,   /* x */
+    TCM_OP_RELU = 1,       /* x if x > 0, else 0 */
+    TCM_OP_GELU_TANH = 2,  /* x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+    TCM_OP_GELU_ERF = 3,   /* x Phi(x), Phi the standard normal distribution function */
+    TCM_OP_SILU = 4        /* x / (1 + e^-x) */
+} tcm_op;
 
 /*
  * Out = A . B^T for one problem.
@@ -128,7 +141,7 @@ tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out
                           tcm_dtype out_dtype, float alpha, float beta, void* stream);
 
 /*
- * General form: Out = alpha * (A . B) + beta * C with A the M x K matrix and B
+ * General form: Out = op(alpha * (A . B) + beta * C) with A the M x K matrix and B
  * the K x N matrix, each in either arrangement with a leading dimension
  * ("API Card: Blackwell Pipeline (tcgen05)", "Descriptor.": half and bfloat16
  * run in either majorness; "Host side.": global operands are declared
@@ -142,13 +155,17 @@ tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out
  *   Out      M x N row-major of `out_dtype`, element (i, j) at Out[i*ldo + j],
  *            ldo >= N; only these M x N elements are written
  * dtype TCM_F16 or TCM_BF16; c_dtype and out_dtype TCM_F16, TCM_BF16 or
- * TCM_F32.  Sums, combine and rounding as tcm_gemm_tn_ex; C may be Out itself
+ * TCM_F32.  Sums, combine and rounding as tcm_gemm_tn_ex, with `op` (a tcm_op)
+ * applied in fp32 between the combine and the rounding: ReLU exactly, the
+ * others from the hardware exponential and reciprocal (and, for
+ * TCM_OP_GELU_ERF, the erfc approximation of Abramowitz and Stegun 7.1.26,
+ * absolute error <= 1.5e-7), within 2^-20 (|x| + |op(x)|).  C may be Out itself
  * (same pointer, dtype and leading dimension).  Row-major A with
  * column-major B (lda = ldb = K, ldo = N) is tcm_gemm_tn's operation.
  * Every leading dimension must be at least 1 and at least the size named
  * above (TCM_ERR_INVALID_SHAPE), lda and ldb at most 2^21 and ldo and ldc
- * below 2^31 (TCM_ERR_UNSUPPORTED_SHAPE); an order other than the two gives
- * TCM_ERR_INVALID_SHAPE.  Alignment: A, B, Out (and C when read) 16-byte
+ * below 2^31 (TCM_ERR_UNSUPPORTED_SHAPE); an order or op outside its values
+ * gives TCM_ERR_INVALID_ARGUMENT.  Alignment: A, B, Out (and C when read) 16-byte
  * aligned, lda and ldb multiples of 8 elements, and K a multiple of 8 unless
  * A is column-major and B row-major (TCM_ERR_MISALIGNED); ldo and ldc are
  * free.
@@ -156,7 +173,7 @@ tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out
 tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B,
                     tcm_order b_order, int64_t ldb, const void* C, int64_t ldc, void* Out,
                     int64_t ldo, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
-                    tcm_dtype c_dtype, tcm_dtype out_dtype, float alpha, float beta,
+                    tcm_dtype c_dtype, tcm_dtype out_dtype, float alpha, float beta, tcm_op op,
                     void* stream);
 
 /*

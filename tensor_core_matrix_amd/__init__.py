@@ -31,6 +31,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtcm.so")
 F16, BF16, F32, E4M3, E8M0, E2M1 = 0, 1, 2, 3, 4, 5
 # tcm_order codes
 ROW_MAJOR, COL_MAJOR = 0, 1
+# tcm_op codes
+OPS = {"identity": 0, "relu": 1, "gelu_tanh": 2, "gelu_erf": 3, "silu": 4}
 
 
 class TcmError(RuntimeError):
@@ -71,7 +73,7 @@ def lib() -> ctypes.CDLL:
             cf = ctypes.c_float
             L.tcm_gemm_tn_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, cf, cf, vp]
             L.tcm_gemm.argtypes = [vp, ci, i64, vp, ci, i64, vp, i64, vp, i64, i64, i64, i64,
-                                   ci, ci, ci, cf, cf, vp]
+                                   ci, ci, ci, cf, cf, ci, vp]
             L.tcm_gemm_mx_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_gemm_mx_fp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_plan_gemm.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(Plan)]
@@ -248,11 +250,12 @@ def order_ld(t) -> tuple[int, int]:
     raise ValueError(f"no unit stride: shape {tuple(t.shape)}, strides {t.stride()}")
 
 
-def gemm(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None):
-    """Out = alpha * a . b + beta * c for 2-D views: a (M, K) and b (K, N)
+def gemm(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None, op="identity"):
+    """Out = op(alpha * a . b + beta * c) for 2-D views: a (M, K) and b (K, N)
     float16/bfloat16 with rows or columns contiguous (transposed views and
     slices of larger tensors are taken as they are, by their strides); c and
-    out (M, N) float16/bfloat16/float32 with contiguous rows; out may be c."""
+    out (M, N) float16/bfloat16/float32 with contiguous rows; out may be c.
+    op: "identity", "relu", "gelu_tanh", "gelu_erf" or "silu"."""
     torch = _torch()
     M, K = a.shape
     K2, N = b.shape
@@ -278,7 +281,7 @@ def gemm(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None):
         _check(lib().tcm_gemm(a.data_ptr(), ao, lda, b.data_ptr(), bo, ldb,
                               None if c is None else c.data_ptr(), ldc, out.data_ptr(), ldo,
                               M, N, K, _code(a.dtype), codes[c.dtype] if c is not None else F32,
-                              codes[out.dtype], float(alpha), float(beta), _stream(a)))
+                              codes[out.dtype], float(alpha), float(beta), OPS[op], _stream(a)))
     return out
 
 

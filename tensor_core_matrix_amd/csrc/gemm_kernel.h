@@ -168,8 +168,19 @@ void tiled_gemm_kernel(GemmArgs p) {
     // wave-private LDS area after the ring.
     constexpr int STG_ROWB = WTN * (int)sizeof(TOut);  // bytes of one staged row
     constexpr int STG_BYTES = EPI_LDS ? 32 * STG_ROWB : 0;
-    static_assert(S * STAGE + 4 * STG_BYTES <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE + 4 * STG_BYTES];
+    // C-input kernels: an fp32 staging area per wave for the epilogue with a
+    // per-element operation, 32 rows of OPJ 32-column accumulator blocks, as
+    // many blocks as the workgroups of one CU leave room for (0: the tile
+    // has no room, and the host never asks it for an operation).
+    constexpr int OPJ = !AB ? 0
+                        : (FN % 4 == 0 && OCC * (S * STAGE + 4 * 32 * 128 * 4) <= 160 * 1024) ? 4
+                        : (FN % 2 == 0 && OCC * (S * STAGE + 4 * 32 * 64 * 4) <= 160 * 1024)  ? 2
+                        : (OCC * (S * STAGE + 4 * 32 * 32 * 4) <= 160 * 1024)                 ? 1
+                                                                                              : 0;
+    constexpr int OP_BYTES = 32 * OPJ * 32 * 4;  // per wave
+    constexpr int EPI_BYTES = 4 * (STG_BYTES > OP_BYTES ? STG_BYTES : OP_BYTES);
+    static_assert(S * STAGE + EPI_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE + EPI_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -476,6 +487,124 @@ void tiled_gemm_kernel(GemmArgs p) {
         }
     };
 
+    // Epilogue of the C-input kernels, with a per-element operation: the wave's
+    // fp32 accumulators go, OPJ 32-column blocks at a time (all 32 rows, so
+    // every lane writes), to a wave-private LDS area in the MFMA layout, and
+    // are read back as 16-byte row pieces (4 consecutive columns per lane,
+    // whole rows per group of lanes).  Each lane then combines
+    // alpha * sum + beta * c, applies the operation and stores, so C is read
+    // and Out written row by row.  The loop over passes is not unrolled and
+    // the read-back body exists once per operation: an operation unrolled
+    // over all 256 accumulators of a lane does not fit the registers.  Every
+    // element is read before it is written, by one lane, so C may be Out.
+    auto op_epilogue = [&](const TileCursor& c) {
+        if constexpr (AB && OPJ > 0) {
+            constexpr int ROWB = OPJ * 32 * 4;           // bytes of one staged row
+            constexpr int CHK = ROWB / 16;               // 16-byte chunks per row
+            constexpr int RPI = kWaveSize / CHK;         // rows per read-back instruction
+            constexpr int ITER = 32 / RPI;               // read-back instructions per pass
+            constexpr int BATCH = ITER < 8 ? ITER : 8;   // pieces in flight at once
+            constexpr int JP = FN / OPJ;                 // passes per 32-row block
+            // chunk swizzle: 16 consecutive lanes of a write (16 rows, one
+            // chunk) or of a read (whole rows) cover the 64 banks
+            auto swz = [](int r) { return CHK >= 16 ? (r & 15) : ((r >> 1) & (CHK - 1)); };
+            char* stg = lds + S * STAGE + wave * OP_BYTES;
+            char* Cb = (char*)p.C + c.batch * p.stride_c;
+            const char* Cinb = (const char*)p.Cin + c.batch * p.stride_cin;
+            const int ldc = p.ldc;
+            const bool vec = (ldc & 3) == 0;
+            const bool vec_c = (p.ldcin & 3) == 0;
+            const bool use_c = p.beta != 0.0f;
+            const int cdt = p.c_dtype;
+            const int ces = cdt == 2 ? 4 : 2;
+            const float al = p.alpha, be = p.beta;
+            const int row0 = c.tm * BM + wm * WTM;   // the wave's first output row
+            const int col0 = c.tn * BN + wn * WTN;
+            // pass P: rows of block i = P / JP, column blocks (P % JP) OPJ + 0..OPJ-1
+            auto stage = [&](auto P) {
+                constexpr int i = decltype(P)::value / JP, jg = decltype(P)::value % JP;
+#pragma unroll
+                for (int jj = 0; jj < OPJ; ++jj)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x16_t& a = acc[i][jg * OPJ + jj];
+                        const int ch = (8 * jj + 2 * q + hi) ^ swz(l32);
+                        lds_write16_acc(stg + l32 * ROWB + ch * 16,
+                                        (f32x4_t){a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]});
+                    }
+            };
+            auto readback = [&](auto OPC, int m0, int n0) {
+                constexpr int OP = decltype(OPC)::value;
+                const int ck = lane % CHK;
+                const int n = n0 + 4 * ck;
+                const bool vec4 = vec && n + 3 < p.N;
+#pragma unroll
+                for (int t0 = 0; t0 < ITER; t0 += BATCH) {
+                    // the batch's row pieces and their C values in flight first,
+                    // then one scheduling region per piece
+                    f32x4_t a4[BATCH], c4[BATCH];
+#pragma unroll
+                    for (int t = 0; t < BATCH; ++t) {
+                        const int r = (t0 + t) * RPI + lane / CHK;
+                        a4[t] = *(const f32x4_t*)(stg + r * ROWB + ((ck ^ swz(r)) * 16));
+                    }
+#pragma unroll
+                    for (int t = 0; t < BATCH; ++t) {
+                        const int m = m0 + (t0 + t) * RPI + lane / CHK;
+                        c4[t] = (f32x4_t){};
+                        if (use_c && m < p.M) {
+                            const char* crow = Cinb + (int64_t)m * p.ldcin * ces;
+                            if (vec_c && vec4) {
+                                c4[t] = load4_c(crow, n, cdt);
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (n + e < p.N) c4[t][e] = load1_c(crow, n + e, cdt);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < BATCH; ++t) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        const int m = m0 + (t0 + t) * RPI + lane / CHK;
+                        if (m >= p.M) continue;
+                        TOut* orow = (TOut*)Cb + (int64_t)m * ldc;
+                        f32x4_t v = {al * a4[t][0], al * a4[t][1], al * a4[t][2], al * a4[t][3]};
+                        if (use_c) v += be * c4[t];
+                        if (vec4) {
+                            store4<TOut>(orow + n, apply_op<OP>(v[0]), apply_op<OP>(v[1]),
+                                         apply_op<OP>(v[2]), apply_op<OP>(v[3]));
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < p.N)
+                                    orow[n + e] = convert_out<TOut>(apply_op<OP>(v[e]));
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+#pragma unroll 1
+            for (int pass = 0; pass < FM * JP; ++pass) {
+                static_for<FM * JP>([&](auto P) {
+                    if (pass == decltype(P)::value) stage(P);
+                });
+                // the wave's own LDS writes, then reads by other lanes
+                wave_lds_exchange();
+                const int m0 = row0 + (pass / JP) * 32;
+                const int n0 = col0 + (pass % JP) * OPJ * 32;
+                switch (p.op) {
+                case kOpIdentity: readback(std::integral_constant<int, kOpIdentity>{}, m0, n0); break;
+                case kOpRelu: readback(std::integral_constant<int, kOpRelu>{}, m0, n0); break;
+                case kOpGeluTanh: readback(std::integral_constant<int, kOpGeluTanh>{}, m0, n0); break;
+                case kOpGeluErf: readback(std::integral_constant<int, kOpGeluErf>{}, m0, n0); break;
+                default: readback(std::integral_constant<int, kOpSilu>{}, m0, n0);
+                }
+                wave_lds_exchange();
+            }
+        }
+    };
+
     auto epilogue = [&](const TileCursor& c) {
         // Out's row stride, read from the arguments here (a value held from
         // the kernel's start costs the main loop a register)
@@ -484,7 +613,11 @@ void tiled_gemm_kernel(GemmArgs p) {
         const int m_base = c.tm * BM + wm * WTM + l32;
         const int n_base = c.tn * BN + wn * WTN + 4 * hi;
         const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (ldc & 3) == 0;
-        if constexpr (AB) {
+        if constexpr (AB && OPJ > 0) {
+            op_epilogue(c);
+            return;
+        } else if constexpr (AB) {
+            // (tiles without room for the staged form: no operation)
             // Each lane reads the C values of exactly the outputs it writes,
             // so C may be the output itself (an in-place update).
             const bool vec = (ldc & 3) == 0;

@@ -361,7 +361,7 @@ tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out
 tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B,
                     tcm_order b_order, int64_t ldb, const void* C, int64_t ldc, void* Out,
                     int64_t ldo, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
-                    tcm_dtype c_dtype, tcm_dtype out_dtype, float alpha, float beta,
+                    tcm_dtype c_dtype, tcm_dtype out_dtype, float alpha, float beta, tcm_op op,
                     void* stream) {
     auto out_ok = [](tcm_dtype d) { return d == TCM_F16 || d == TCM_BF16 || d == TCM_F32; };
     if (!(dtype == TCM_F16 || dtype == TCM_BF16) || !out_ok(out_dtype) ||
@@ -371,7 +371,9 @@ tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B
     tcm_status s = check_sizes(1, M, N, K, &empty);
     if (s != TCM_OK) return s;
     auto order_ok = [](tcm_order o) { return o == TCM_ROW_MAJOR || o == TCM_COL_MAJOR; };
-    if (!order_ok(a_order) || !order_ok(b_order)) return TCM_ERR_INVALID_SHAPE;
+    if (!order_ok(a_order) || !order_ok(b_order) || (int)op < TCM_OP_IDENTITY ||
+        (int)op > TCM_OP_SILU)
+        return TCM_ERR_INVALID_ARGUMENT;
     // a stored row holds the matrix's columns (row-major) or its rows
     // (column-major); every leading dimension covers at least that, and 1
     const bool a_mn = a_order == TCM_COL_MAJOR;  // A's M index contiguous
@@ -397,10 +399,12 @@ tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B
     const int32_t chosen = choose_variant(1, M, N, 16, dev.cus);
     // the plain kernels read dense storage only (rows K and N apart)
     const bool plain_epi = alpha == 1.0f && beta == 0.0f && out_dtype != TCM_F16 && lda == K &&
-                           ldb == K && ldo == N;
+                           ldb == K && ldo == N && op == TCM_OP_IDENTITY;
     int32_t v = (a_mn || b_mn) ? mn_variant(chosen)
                 : plain_epi    ? chosen
                                : epi_variant(chosen);
+    // the 128 x 64 tile has no LDS room for the per-element epilogue
+    if (op != TCM_OP_IDENTITY && v == V_T128x64) v = V_T128x128;
     tcm_plan plan;
     GemmArgs a;
     plan_variant(v, 1, M, N, K, dev.cus, &plan, &a);
@@ -415,6 +419,7 @@ tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B
     a.alpha = alpha;
     a.beta = beta;
     a.c_dtype = (int32_t)c_dtype;
+    a.op = (int32_t)op;
     hipError_t e;
     const hipStream_t st = (hipStream_t)stream;
     if (a_mn && b_mn)
@@ -467,6 +472,8 @@ const char* tcm_status_string(tcm_status s) {
     case TCM_ERR_UNSUPPORTED_DTYPE: return "TCM_ERR_UNSUPPORTED_DTYPE: dtype pair not supported";
     case TCM_ERR_NO_DEVICE: return "TCM_ERR_NO_DEVICE: no gfx950 HIP device is current";
     case TCM_ERR_HIP: return "TCM_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case TCM_ERR_INVALID_ARGUMENT:
+        return "TCM_ERR_INVALID_ARGUMENT: an order or operation code outside its values";
     }
     return "TCM_ERR_UNKNOWN: unknown status code";
 }

@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include "tcm_internal.h"
@@ -130,6 +132,67 @@ typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 template <>
 __device__ __forceinline__ void store4<_Float16>(_Float16* dst, float a, float b, float c, float d) {
     *(f16x4_t*)dst = (f16x4_t){(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+}
+
+// f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N-1>{})
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// 16 bytes of accumulator values into LDS, written from accumulation
+// registers (ds_write_b128 with an AGPR source) by inline assembly.  The
+// builtin store form first copies the values to VGPRs; in the epilogue with a
+// per-element operation, whose loop keeps all 256 accumulators of a lane
+// live, those copies made the register allocator spill accumulators.  LDS
+// operations of a wave complete in order, so a later read of the same bytes
+// by any lane of the wave sees them; the compiler's own lgkmcnt waits are
+// only made longer by the extra operation.
+__device__ __forceinline__ void lds_write16_acc(void* lds_dst, f32x4_t v) {
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_dst;
+    asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "a"(v) : "memory");
+}
+
+// Per-element epilogue operations, codes of tcm_op: applied in fp32 to the
+// finished value alpha * sum + beta * c, before the rounding to the output
+// type.  The exponential and reciprocal are the hardware's base-2
+// exponential (v_exp_f32) and reciprocal (v_rcp_f32), about 1 ulp each.
+enum : int { kOpIdentity = 0, kOpRelu = 1, kOpGeluTanh = 2, kOpGeluErf = 3, kOpSilu = 4 };
+constexpr int kNumOps = 5;
+
+// 1 / (1 + e^-y); 0 for large negative y (e^-y overflows to inf)
+__device__ __forceinline__ float logistic(float y) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * 1.4426950408889634f));
+}
+
+template <int OP>
+__device__ __forceinline__ float apply_op(float x) {
+    if constexpr (OP == kOpRelu) {
+        return x > 0.0f ? x : 0.0f;
+    } else if constexpr (OP == kOpSilu) {
+        return x * logistic(x);
+    } else if constexpr (OP == kOpGeluTanh) {
+        // x/2 (1 + tanh u) = x logistic(2u), u = sqrt(2/pi) (x + 0.044715 x^3)
+        const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+        return x * logistic(2.0f * u);
+    } else if constexpr (OP == kOpGeluErf) {
+        // x Phi(x) = x/2 erfc(-x/sqrt 2).  erfc(z) for z >= 0 from Abramowitz
+        // and Stegun, Handbook of Mathematical Functions, 7.1.26:
+        // t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e^(-z^2), t = 1 / (1 + p z),
+        // absolute error at most 1.5e-7.  Negative x uses erfc(-z) = 2 - erfc(z).
+        const float z = fabsf(x) * 0.7071067811865476f;
+        const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
+        const float poly =
+            t * (0.254829592f +
+                 t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+        const float q = poly * __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);  // erfc(z)
+        return x >= 0.0f ? x * (1.0f - 0.5f * q) : 0.5f * x * q;
+    } else {
+        return x;
+    }
 }
 
 // Values of a C input as floats; dt is the tcm_dtype code (0 f16, 1 bf16,

@@ -40,6 +40,7 @@ struct GemmArgs {
     // ldc / ldcin: from one row of Out / of the C input to the next.
     int32_t lda, ldb;
     int32_t ldc, ldcin;
+    int32_t op;  // per-element epilogue operation (tcm_op code; C-input kernels only)
 };
 
 // Kernel variants.  The id is reported by tcm_plan_gemm.

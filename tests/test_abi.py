@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tcm.h")
 GOLDEN = os.path.join(ROOT, "tests", "golden", "page_figures.json")
 
-OK, NULLP, BADSHAPE, UNSUP_SHAPE, MISALIGNED, UNSUP_DTYPE, NO_DEVICE, HIP = range(8)
+OK, NULLP, BADSHAPE, UNSUP_SHAPE, MISALIGNED, UNSUP_DTYPE, NO_DEVICE, HIP, BADARG = range(9)
 A, B, C, SA, SB = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000  # 16-byte aligned stand-ins
 
 
@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     L = tcm.lib()
-    for s in range(8):
+    for s in range(9):
         txt = L.tcm_status_string(s).decode()
         assert txt.startswith("TCM_") and ":" in txt
     assert "UNKNOWN" in L.tcm_status_string(99).decode()
@@ -159,9 +159,9 @@ ROW, COL = tcm.ROW_MAJOR, tcm.COL_MAJOR
 
 
 def call_gen(a=A, ao=ROW, lda=64, b=B, bo=COL, ldb=64, c=SA, ldc=64, o=C, ldo=64, M=64, N=64,
-             K=64, dt=tcm.BF16, cdt=tcm.F32, odt=tcm.F32, alpha=1.0, beta=0.5):
+             K=64, dt=tcm.BF16, cdt=tcm.F32, odt=tcm.F32, alpha=1.0, beta=0.5, op=0):
     return tcm.lib().tcm_gemm(a, ao, lda, b, bo, ldb, c, ldc, o, ldo, M, N, K, dt, cdt, odt,
-                              alpha, beta, None)
+                              alpha, beta, op, None)
 
 
 def test_general_entry_validation():
@@ -176,8 +176,12 @@ def test_general_entry_validation():
     assert call_gen(cdt=tcm.E8M0) == UNSUP_DTYPE
     assert call_gen(cdt=tcm.E8M0, beta=0.0, c=None, ldc=0) in ok   # C unused when beta == 0
     # orders and leading dimensions
-    assert call_gen(ao=2) == BADSHAPE
-    assert call_gen(bo=-1) == BADSHAPE
+    assert call_gen(ao=2) == BADARG
+    assert call_gen(bo=-1) == BADARG
+    assert call_gen(op=5) == BADARG
+    assert call_gen(op=-1) == BADARG
+    for op in range(5):
+        assert call_gen(op=op) in ok
     assert call_gen(lda=56, K=64) == BADSHAPE                      # row-major A: lda >= K
     assert call_gen(ao=COL, lda=56, M=64, K=32) == BADSHAPE        # column-major A: lda >= M
     assert call_gen(ao=COL, lda=64, M=64, K=200, ldb=200) in ok    # ... and K is free of lda
