@@ -31,8 +31,8 @@
  *   a(i,k) = e4m3(A[i][k]) * e8m0(SA[i][k/32])
  *   b(j,k) = e4m3(B[j][k]) * e8m0(SB[j][k/32])
  *
- * and the same with E2M1 (MXFP4, the format table's 4-bit row) elements in
- * place of E4M3.
+ * and the same with E2M1 (MXFP4, the format table's 4-bit row) or the FP6
+ * formats E2M3 and E3M2 (MXFP6, the 6-bit rows) in place of E4M3.
  *
  * Element decoders are written from the format definitions (IEEE 754
  * binary16; bfloat16 = the upper half of binary32; OCP MX E4M3 "FN" with bias
@@ -42,7 +42,11 @@
  * cited in that page's "Go deeper" list does.  E2M1 elements are stored two
  * per byte, element 2t in the low four bits of byte t and element 2t + 1 in
  * the high four bits (the pages fix no packing; this is the plainest
- * little-endian reading), so a row of K elements is K/2 bytes.
+ * little-endian reading), so a row of K elements is K/2 bytes.  FP6 codes
+ * (E2M3: bias 1, 3 mantissa bits, max 7.5; E3M2: bias 3, 2 mantissa bits,
+ * max 28; neither has infinities or NaN) are stored as one little-endian bit
+ * stream, element t in bits 6t .. 6t+5, so a row of K elements is 3K/4 bytes
+ * and a 32-element block 24 bytes.
  *
  * Accuracy: sequential fp64 summation errs by at most about K * 2^-53 *
  * abssum, far below any tolerance used against the GPU path.  Every MX
@@ -54,7 +58,8 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F16 = 0, OR_BF16 = 1, OR_F32 = 2, OR_E4M3 = 3, OR_E8M0 = 4, OR_E2M1 = 5 };
+enum { OR_F16 = 0, OR_BF16 = 1, OR_F32 = 2, OR_E4M3 = 3, OR_E8M0 = 4, OR_E2M1 = 5, OR_E2M3 = 6,
+       OR_E3M2 = 7 };
 
 /* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits. */
 static double dec_f16(uint16_t h) {
@@ -105,6 +110,32 @@ static double dec_e2m1(unsigned nib) {
     return s ? -v : v;
 }
 
+/* OCP FP6 E2M3: 1 sign, 2 exponent (bias 1), 3 mantissa bits; exponent
+ * field 0 holds the subnormals m/8; no infinities, no NaN; max 7.5. */
+static double dec_e2m3(unsigned c) {
+    int s = (c >> 5) & 1, e = (c >> 3) & 3, m = c & 7;
+    double v = e == 0 ? m / 8.0 : ldexp(1.0 + m / 8.0, e - 1);
+    return s ? -v : v;
+}
+
+/* OCP FP6 E3M2: 1 sign, 3 exponent (bias 3), 2 mantissa bits; exponent
+ * field 0 holds the subnormals m/4 * 2^-2; no infinities, no NaN; max 28. */
+static double dec_e3m2(unsigned c) {
+    int s = (c >> 5) & 1, e = (c >> 2) & 7, m = c & 3;
+    double v = e == 0 ? ldexp(m / 4.0, -2) : ldexp(1.0 + m / 4.0, e - 3);
+    return s ? -v : v;
+}
+
+/* 6-bit code `idx` of a packed FP6 array: bits 6 idx .. 6 idx + 5 of the
+ * byte string read as one little-endian bit stream (element 4t in the low six
+ * bits of byte 3t; four elements per three bytes). */
+static unsigned fp6_code(const uint8_t* b, int64_t idx) {
+    const int64_t bit = 6 * idx;
+    const unsigned lo = b[bit / 8];
+    const unsigned hi = (bit % 8) > 2 ? b[bit / 8 + 1] : 0;
+    return ((lo | (hi << 8)) >> (bit % 8)) & 0x3f;
+}
+
 static double dec_e8m0(uint8_t b) {
     if (b == 0xff)
         return NAN;
@@ -130,6 +161,9 @@ static int elem_bits(int dtype) {
         return 8;
     case OR_E2M1:
         return 4;
+    case OR_E2M3:
+    case OR_E3M2:
+        return 6;
     }
     return 0;
 }
@@ -150,6 +184,10 @@ static double dec_one(int dtype, const void* src, int64_t idx) {
         uint8_t byte = ((const uint8_t*)src)[idx / 2];
         return dec_e2m1((idx & 1) ? byte >> 4 : byte & 0xF);
     }
+    case OR_E2M3:
+        return dec_e2m3(fp6_code((const uint8_t*)src, idx));
+    case OR_E3M2:
+        return dec_e3m2(fp6_code((const uint8_t*)src, idx));
     }
     return NAN;
 }
@@ -282,13 +320,15 @@ int oracle_gemm_tn(int dtype, const void* A, const void* B, int64_t batch, int64
     return 0;
 }
 
-/* MX block-scaled GEMM with elements of format `dtype` (OR_E4M3 or OR_E2M1),
+/* MX block-scaled GEMM with elements of format `dtype` (OR_E4M3, OR_E2M1,
+ * OR_E2M3 or OR_E3M2),
  * one E8M0 scale per 32 consecutive K elements of every row of A
  * (SA: M x K/32) and of B (SB: N x K/32). */
 int oracle_gemm_mx_typed(int dtype, const uint8_t* A, const uint8_t* B, const uint8_t* SA,
                          const uint8_t* SB, int64_t M, int64_t N, int64_t K, double* ref,
                          double* abssum, int nthreads) {
-    if (!(dtype == OR_E4M3 || dtype == OR_E2M1) || !A || !B || !SA || !SB ||
+    if (!(dtype == OR_E4M3 || dtype == OR_E2M1 || dtype == OR_E2M3 || dtype == OR_E3M2) || !A ||
+        !B || !SA || !SB ||
         !shape_ok(1, M, N, K) || K % 32 != 0)
         return -1;
     return gemm_one(dtype, A, B, SA, SB, M, N, K, ref, abssum, nthreads);
@@ -330,15 +370,17 @@ int oracle_axpby(int64_t n, double alpha, const double* ref, double beta, int c_
  * Selected entries only, for problems too large to compute whole: entry t is
  * (row ii[t], column jj[t]) of problem bb[t] (bb may be NULL for batch 1).
  * SA/SB non-NULL selects the MX definition (dtype must then be OR_E4M3 or
- * OR_E2M1).
+ * OR_E2M1, OR_E2M3, OR_E3M2).
  */
 int oracle_entries(int dtype, const void* A, const void* B, const uint8_t* SA, const uint8_t* SB,
                    int64_t M, int64_t N, int64_t K, const int64_t* bb, const int64_t* ii,
                    const int64_t* jj, int64_t n, double* ref, double* abssum) {
     if (!elem_bits(dtype) || !A || !B || !ii || !jj || !shape_ok(1, M, N, K) ||
         ((SA || SB) &&
-         (!SA || !SB || !(dtype == OR_E4M3 || dtype == OR_E2M1) || K % 32 != 0)) ||
-        (dtype == OR_E2M1 && (!SA || K % 2 != 0)))
+         (!SA || !SB ||
+          !(dtype == OR_E4M3 || dtype == OR_E2M1 || dtype == OR_E2M3 || dtype == OR_E3M2) ||
+          K % 32 != 0)) ||
+        ((dtype == OR_E2M1 || dtype == OR_E2M3 || dtype == OR_E3M2) && (!SA || K % 4 != 0)))
         return -1;
     const int64_t bits = elem_bits(dtype);
     for (int64_t t = 0; t < n; ++t) {

@@ -35,8 +35,11 @@ import threading
 
 import numpy as np
 
-F16, BF16, F32, E4M3, E8M0, E2M1 = 0, 1, 2, 3, 4, 5
-DTYPE_NAMES = {"f16": F16, "bf16": BF16, "f32": F32, "e4m3": E4M3, "e8m0": E8M0, "e2m1": E2M1}
+F16, BF16, F32, E4M3, E8M0, E2M1, E2M3, E3M2 = 0, 1, 2, 3, 4, 5, 6, 7
+DTYPE_NAMES = {"f16": F16, "bf16": BF16, "f32": F32, "e4m3": E4M3, "e8m0": E8M0, "e2m1": E2M1,
+               "e2m3": E2M3, "e3m2": E3M2}
+# elements per storage byte-group: (elements, bytes) of the packed formats
+_PACK = {E2M1: (2, 1), E2M3: (4, 3), E3M2: (4, 3)}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -96,7 +99,7 @@ def default_threads() -> int:
 
 
 _STORAGE = {F16: np.uint16, BF16: np.uint16, F32: np.float32, E4M3: np.uint8, E8M0: np.uint8,
-            E2M1: np.uint8}
+            E2M1: np.uint8, E2M3: np.uint8, E3M2: np.uint8}
 
 
 def _raw(x: np.ndarray, dtype: int) -> np.ndarray:
@@ -113,9 +116,16 @@ def _ptr(x):
 
 def decode(dtype: int, raw: np.ndarray) -> np.ndarray:
     """Exact fp64 values of stored elements (format definitions, see oracle.c).
-    E2M1 storage of shape (..., n) decodes to shape (..., 2 n)."""
+    E2M1 storage of shape (..., n) decodes to shape (..., 2 n), FP6 storage
+    (E2M3, E3M2) of shape (..., 3 n) to shape (..., 4 n)."""
     raw = _raw(raw, dtype)
-    shape = raw.shape[:-1] + (raw.shape[-1] * 2,) if dtype == E2M1 else raw.shape
+    if dtype in _PACK:
+        e, b = _PACK[dtype]
+        if raw.shape[-1] % b:
+            raise ValueError("packed rows must be whole byte groups")
+        shape = raw.shape[:-1] + (raw.shape[-1] // b * e,)
+    else:
+        shape = raw.shape
     out = np.empty(shape, dtype=np.float64)
     rc = _load().oracle_decode(dtype, _ptr(raw), out.size, _ptr(out))
     if rc:
@@ -146,12 +156,13 @@ def gemm_tn(dtype: int, a: np.ndarray, b: np.ndarray, nthreads: int | None = Non
 def gemm_mx(a: np.ndarray, b: np.ndarray, sa: np.ndarray, sb: np.ndarray,
             nthreads: int | None = None, dtype: int = E4M3):
     """ref, abssum for the MX block-scaled product: a M x K, b N x K elements of
-    `dtype` (E4M3 bytes, or E2M1 pairs stored M x K/2 and N x K/2); sa M x K/32,
-    sb N x K/32 E8M0 bytes."""
+    `dtype` (E4M3 bytes; E2M1 pairs stored M x K/2 and N x K/2; FP6 (E2M3,
+    E3M2) stored M x 3K/4 and N x 3K/4); sa M x K/32, sb N x K/32 E8M0 bytes."""
     a, b, sa, sb = _raw(a, dtype), _raw(b, dtype), _raw(sa, E8M0), _raw(sb, E8M0)
     M = a.shape[0]
     N = b.shape[0]
-    K = a.shape[1] * (2 if dtype == E2M1 else 1)
+    e, by = _PACK.get(dtype, (1, 1))
+    K = a.shape[1] // by * e
     if b.shape[1] != a.shape[1] or K % 32 or sa.shape != (M, K // 32) or sb.shape != (N, K // 32):
         raise ValueError("bad MX shapes")
     ref = np.empty((M, N), np.float64)
@@ -172,8 +183,8 @@ def entries(dtype: int, a: np.ndarray, b: np.ndarray, ii, jj, bb=None, sa=None, 
     else:
         a3, b3 = a, b
     _, M, K = a3.shape
-    if dtype == E2M1:
-        K *= 2
+    if dtype in _PACK:
+        K = K // _PACK[dtype][1] * _PACK[dtype][0]
     N = b3.shape[1]
     ii = np.ascontiguousarray(ii, dtype=np.int64)
     jj = np.ascontiguousarray(jj, dtype=np.int64)

@@ -21,6 +21,9 @@ problems):
   seed 4, bf16 output ("Hopper and Blackwell GEMM", block-scaling table).
 * ``mxfp4_8192`` -- the same with E2M1 elements (MXFP4, the table's 4-bit
   row): every 4-bit code equally likely, seed 5, bf16 output.
+* ``mxfp6_8192`` -- the same with FP6 E2M3 elements (MXFP6, the table's 6-bit
+  rows): every 6-bit code equally likely, packed four per three bytes, seed
+  7, bf16 output.
 * ``bf16_8192_nn`` -- A 8192x8192 and B 8192x8192 bfloat16, both row-major
   (B stored K x N, its N index contiguous: the product A . B of two
   row-major matrices), N(0,1)*0.05, seed 6, bf16 output ("API Card:
@@ -43,7 +46,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str          # "f16", "bf16", or "e4m3" / "e2m1" (MX block-scaled)
+    dtype: str          # "f16", "bf16", or "e4m3" / "e2m1" / "e2m3" / "e3m2" (MX block-scaled)
     out_dtype: str      # "f32" or "bf16"
     seed: int
     dist: str           # "uniform", "normal" or "codes" (every code equally likely)
@@ -63,6 +66,7 @@ WORKLOADS = {
     "bf16_8192": Workload("bf16_8192", 1, 8192, 8192, 8192, "bf16", "bf16", 3, "normal", 0.05),
     "mxfp8_8192": Workload("mxfp8_8192", 1, 8192, 8192, 8192, "e4m3", "bf16", 4, "normal", 1.0),
     "mxfp4_8192": Workload("mxfp4_8192", 1, 8192, 8192, 8192, "e2m1", "bf16", 5, "codes"),
+    "mxfp6_8192": Workload("mxfp6_8192", 1, 8192, 8192, 8192, "e2m3", "bf16", 7, "codes"),
     "bf16_8192_nn": Workload("bf16_8192_nn", 1, 8192, 8192, 8192, "bf16", "bf16", 6, "normal", 0.05,
                              b_order="row"),
 }
@@ -101,6 +105,21 @@ def e2m1_codes(rows: int, k: int, gen) -> torch.Tensor:
     return (c[:, 0::2] | (c[:, 1::2] << 4)).to(torch.uint8)
 
 
+def pack_fp6(codes: torch.Tensor) -> torch.Tensor:
+    """6-bit codes (rows x k, k a multiple of 4) packed as one little-endian
+    bit stream per row, element t in bits 6t .. 6t+5: uint8 rows x 3k/4."""
+    c = codes.to(torch.int32)
+    w = c[:, 0::4] | (c[:, 1::4] << 6) | (c[:, 2::4] << 12) | (c[:, 3::4] << 18)
+    return torch.stack([w & 0xFF, (w >> 8) & 0xFF, (w >> 16) & 0xFF], dim=2).reshape(
+        c.shape[0], -1).to(torch.uint8)
+
+
+def fp6_codes(rows: int, k: int, gen) -> torch.Tensor:
+    """rows x k FP6 elements (E2M3 or E3M2), every 6-bit code equally likely,
+    packed by pack_fp6: uint8 of shape rows x 3k/4."""
+    return pack_fp6(torch.randint(0, 64, (rows, k), generator=gen, dtype=torch.int32))
+
+
 def e8m0_scales(shape, gen, lo=-4, hi=4) -> torch.Tensor:
     """E8M0 bytes 127+s with s uniform on the integers lo..hi."""
     return (torch.randint(lo, hi + 1, shape, generator=gen, dtype=torch.int32)
@@ -121,13 +140,16 @@ def make(w: Workload | str) -> dict:
     lead = (w.batch,) if w.batch > 1 else ()
     shp_a = lead + (w.M, w.K)
     shp_b = lead + ((w.K, w.N) if w.b_order == "row" else (w.N, w.K))
-    if w.dtype in ("e4m3", "e2m1"):
+    if w.dtype in ("e4m3", "e2m1", "e2m3", "e3m2"):
         if w.dtype == "e4m3":
             a = e4m3_normal(shp_a, g, w.sigma)
             b = e4m3_normal(shp_b, g, w.sigma)
-        else:
+        elif w.dtype == "e2m1":
             a = e2m1_codes(w.M, w.K, g)
             b = e2m1_codes(w.N, w.K, g)
+        else:
+            a = fp6_codes(w.M, w.K, g)
+            b = fp6_codes(w.N, w.K, g)
         lo, hi = w.scale_exp
         sa = e8m0_scales((w.M, w.K // 32), g, lo, hi)
         sb = e8m0_scales((w.N, w.K // 32), g, lo, hi)

@@ -19,6 +19,11 @@ applied to the wrong block -- fails at least one of them:
   torch's own E4M3 cast decoding the same, and the MXFP4 product equal to the
   MXFP8 product of the same values (E2M1 is a subset of E4M3), plus brute
   force;
+* FP6 (MXFP6, E2M3 and E3M2): the value sets as the OCP specification lays
+  them out (ranges and steps, not recomputed from bit fields), the bit order
+  of a hand-packed three-byte group, every value re-encoded by torch's E4M3
+  cast decoding the same (both formats are subsets of E4M3), the MXFP6
+  product equal to the MXFP8 product of the same values, and brute force;
 * operand arrangements and leading dimensions: every row-/column-major pair,
   stored through torch's own transposes inside NaN-padded rows, equals the
   pinned TN product bit for bit (a swapped index or an ignored leading
@@ -89,6 +94,82 @@ def test_decode_e2m1_all_codes_and_nibble_order():
     assert list(orc.decode(orc.E2M1, np.array([0x21, 0xF7], np.uint8))) == [0.5, 1.0, 6.0, -6.0]
     # each value, re-encoded by torch's E4M3 cast, decodes identically
     assert _same(orc.decode(orc.E4M3, _e2m1_to_e4m3(packed)), got)
+
+
+def _fp6_table(fmt):
+    """Non-negative values of the 32 positive FP6 codes as the OCP MX
+    specification lays them out: subnormals, then each binade's steps."""
+    if fmt == "e2m3":   # subnormals k/8; binades [1,2) step 1/8, [2,4) 1/4, [4,8) 1/2
+        return ([Fraction(k, 8) for k in range(8)] + [1 + Fraction(k, 8) for k in range(8)]
+                + [2 + Fraction(k, 4) for k in range(8)] + [4 + Fraction(k, 2) for k in range(8)])
+    # e3m2: subnormals k/16; binades from 1/4 to 16, four steps each (max 28)
+    vals = [Fraction(k, 16) for k in range(4)]
+    for e in range(-2, 5):
+        vals += [Fraction(2) ** e * (1 + Fraction(k, 4)) for k in range(4)]
+    return vals
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_decode_fp6_all_codes_and_bit_order(fmt):
+    dt = orc.DTYPE_NAMES[fmt]
+    table = _fp6_table(fmt)
+    assert len(table) == 32 and table == sorted(table)
+    assert max(table) == (Fraction(15, 2) if fmt == "e2m3" else 28)
+    codes = torch.arange(64, dtype=torch.int32).reshape(1, 64)
+    got = orc.decode(dt, inp.raw(inp.pack_fp6(codes)))[0]
+    assert [Fraction(v) for v in got[:32]] == table
+    assert [Fraction(-v) for v in got[32:]] == table and np.signbit(got[32])
+    # codes 1, 2, 3, 4 packed by hand: bits 0-5 = 1, 6-11 = 2, 12-17 = 3,
+    # 18-23 = 4 -> bytes 0x81, 0x30, 0x10
+    hand = np.array([[0x81, 0x30, 0x10]], np.uint8)
+    assert list(orc.decode(dt, hand)[0]) == [float(table[c]) for c in (1, 2, 3, 4)]
+    assert np.array_equal(inp.raw(inp.pack_fp6(torch.tensor([[1, 2, 3, 4]]))), hand)
+    # every value, re-encoded by torch's E4M3 cast, decodes identically
+    e4 = torch.from_numpy(got).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert _same(orc.decode(orc.E4M3, e4), got)
+
+
+def _fp6_to_e4m3(dt, packed: np.ndarray) -> np.ndarray:
+    v = orc.decode(dt, packed)
+    return torch.from_numpy(v).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_mxfp6_equals_mxfp8_of_the_same_values(fmt):
+    dt = orc.DTYPE_NAMES[fmt]
+    M, N, K = 9, 7, 128
+    g = inp.generator(49)
+    a, b = inp.fp6_codes(M, K, g), inp.fp6_codes(N, K, g)
+    sa, sb = inp.e8m0_scales((M, K // 32), g), inp.e8m0_scales((N, K // 32), g)
+    r6, s6 = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), dtype=dt)
+    r8, s8 = orc.gemm_mx(_fp6_to_e4m3(dt, inp.raw(a)), _fp6_to_e4m3(dt, inp.raw(b)),
+                         inp.raw(sa), inp.raw(sb))
+    assert _same(r6, r8) and _same(s6, s8)
+    ii, jj = np.array([0, 8, 4]), np.array([6, 0, 3])
+    re, se = orc.entries(dt, inp.raw(a), inp.raw(b), ii, jj, sa=inp.raw(sa), sb=inp.raw(sb))
+    assert _same(re, r6[ii, jj]) and _same(se, s6[ii, jj])
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (3, 4, 64)])
+def test_brute_force_mxfp6(shape):
+    M, N, K = shape
+    g = inp.generator(50 + K)
+    codes_a = torch.randint(0, 64, (M, K), generator=g, dtype=torch.int32)
+    codes_b = torch.randint(0, 64, (N, K), generator=g, dtype=torch.int32)
+    sa = inp.e8m0_scales((M, K // 32), g, -6, 6)
+    sb = inp.e8m0_scales((N, K // 32), g, -6, 6)
+    table = _fp6_table("e3m2")
+    val = lambda c: -table[c - 32] if c >= 32 else table[c]   # values from the codes
+    ref, _ = orc.gemm_mx(inp.raw(inp.pack_fp6(codes_a)), inp.raw(inp.pack_fp6(codes_b)),
+                         inp.raw(sa), inp.raw(sb), dtype=orc.E3M2)
+    ea = sa.numpy().astype(np.int64) - 127
+    eb = sb.numpy().astype(np.int64) - 127
+    for i in range(M):
+        for j in range(N):
+            ex = sum((val(int(codes_a[i, k])) * Fraction(2) ** int(ea[i, k // 32])
+                      * val(int(codes_b[j, k])) * Fraction(2) ** int(eb[j, k // 32])
+                      for k in range(K)), Fraction(0))
+            assert Fraction(ref[i, j]) == ex
 
 
 def test_decode_e8m0_all_patterns():
