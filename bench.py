@@ -6,7 +6,7 @@
 A step is one call of the product on the headline workload: bfloat16
 8192 x 8192 x 8192, fp32 accumulation, bf16 output (persistent 256 x 256 x 64
 tiles), inputs N(0,1)*0.05 from seed 3, already resident in HBM.  The other
-measured workloads (MXFP8 8192^3, bf16 4096^3, 1024 batched 128x256x64 and
+measured workloads (MXFP8, MXFP6 and MXFP4 8192^3, bf16 4096^3, 1024 batched 128x256x64 and
 the 128x64x64 single tile, and bf16 8192^3 with both operands row-major) are
 timed after it and reported in the same line.
 
@@ -31,10 +31,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s and % of MFMA dense peak (bf16 8192³; MXFP8 8192³)"
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.3}  # dense MFMA, MI355X
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.3,
+               "e2m3": 10066.3, "e3m2": 10066.3}  # dense MFMA, MI355X (fp6 as fp4)
 HBM_GBS = 8000.0
 KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pingpong.h", "tcm_device.h", "tcm_internal.h", "gemm_tn.hip",
-                  "gemm_mx.hip", "gemm_epi.hip", "gemm_mn.h", "gemm_mn_a.hip", "gemm_mn_b.hip",
+                  "gemm_mx.hip", "gemm_mx6.hip", "gemm_epi.hip", "gemm_mn.h", "gemm_mn_a.hip", "gemm_mn_b.hip",
                   "gemm_mn_ab.hip", "tcm_api.cpp"]
 
 
@@ -90,6 +91,9 @@ def prepare(name, torch, inp, tcm):
         out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
         mx = tcm.gemm_mx_fp8 if w.dtype == "e4m3" else tcm.gemm_mx_fp4
         fn = lambda: mx(x["A"], x["B"], x["SA"], x["SB"], out)
+    elif w.dtype in ("e2m3", "e3m2"):
+        out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
+        fn = lambda: tcm.gemm_mx_fp6(x["A"], x["B"], x["SA"], x["SB"], out, elem=w.dtype)
     elif w.batch > 1:
         out = torch.empty(w.batch, w.M, w.N, dtype=odt, device="cuda")
         fn = lambda: tcm.batched_gemm_tn(x["A"], x["B"], out)
@@ -172,8 +176,8 @@ def main() -> int:
     from tensor_core_matrix_amd import inputs as inp
 
     tcm.lib()
-    order = ["bf16_8192", "mxfp8_8192", "mxfp4_8192", "bf16_8192_nn", "bf16_4096", "batched",
-             "tile_f16"]
+    order = ["bf16_8192", "mxfp8_8192", "mxfp6_8192", "mxfp4_8192", "bf16_8192_nn", "bf16_4096",
+             "batched", "tile_f16"]
     if args.only:
         order = [args.only]
     results = {}
@@ -193,7 +197,7 @@ def main() -> int:
             "frac_of_peak": tflops / PEAK_TFLOPS[w.dtype],
             "gbs": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes,
             "plan": tcm.plan(w.M, w.N, w.K, batch=w.batch,
-                             mx={"e4m3": 1, "e2m1": 2}.get(w.dtype, 0),
+                             mx={"e4m3": 1, "e2m1": 2, "e2m3": 3, "e3m2": 3}.get(w.dtype, 0),
                              dtype=tcm.F16 if w.dtype == "f16" else tcm.BF16,
                              out_dtype=tcm.BF16 if w.out_dtype == "bf16" else tcm.F32,
                              num_cus=0),
@@ -224,7 +228,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": hw.dtype if hw.dtype in ("e4m3", "e2m1") else "bf16",
+        "dtype": hw.dtype if hw.dtype in ("e4m3", "e2m1", "e2m3", "e3m2") else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{head}: M=N=K={hw.M} TN, {hw.dtype} in, fp32 accumulate, "
                                f"{hw.out_dtype} out, seed {hw.seed}",

@@ -76,8 +76,10 @@ typedef enum tcm_dtype {
     TCM_F32 = 2,  /* IEEE binary32 */
     TCM_E4M3 = 3, /* OCP FP8 E4M3 ("FN": no infinities, max 448) */
     TCM_E8M0 = 4, /* OCP E8M0 scale: 2^(e-127), 0xFF = NaN */
-    TCM_E2M1 = 5  /* OCP FP4 E2M1, two per byte, element 2t in the low four bits of
+    TCM_E2M1 = 5, /* OCP FP4 E2M1, two per byte, element 2t in the low four bits of
                      byte t (no infinities, no NaN, max 6) */
+    TCM_E2M3 = 6, /* OCP FP6 E2M3 (bias 1, 3 mantissa bits, max 7.5), packed: see below */
+    TCM_E3M2 = 7  /* OCP FP6 E3M2 (bias 3, 2 mantissa bits, max 28), packed: see below */
 } tcm_dtype;
 
 /* Arrangement of a matrix in memory: row-major (the elements of one row
@@ -202,6 +204,23 @@ tcm_status tcm_gemm_mx_fp4(const void* A, const void* B, const void* scale_A, co
                            void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
                            void* stream);
 
+/*
+ * MXFP6 block-scaled Out = (A * SA) . (B * SB)^T (the 6-bit element formats of
+ * the scaled MMA kind mxf8f6f4 named in "Hopper and Blackwell GEMM", Concept,
+ * "FP8 and FP4, with block scaling"; OCP FP6 with one E8M0 scale per 32).
+ *   elem_dtype  TCM_E2M3 or TCM_E3M2, for both A and B
+ *   A        M x K codes packed as one little-endian bit stream per row: element
+ *            t of a row in bits 6t .. 6t+5 of its bytes (four elements per
+ *            three bytes), M x (3K/4) bytes
+ *   B        N x K codes packed the same way, N x (3K/4) bytes
+ *   scale_A, scale_B, Out, errors: as tcm_gemm_mx_fp8, except that K must be a
+ *            multiple of 64 (rows of whole 16-byte pieces; TCM_ERR_MISALIGNED
+ *            when K % 32 == 0 but K % 64 != 0).
+ */
+tcm_status tcm_gemm_mx_fp6(const void* A, const void* B, const void* scale_A, const void* scale_B,
+                           void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype elem_dtype,
+                           tcm_dtype out_dtype, void* stream);
+
 /* What a call with these arguments would launch (host only: no HIP call when
  * num_cus > 0; num_cus == 0 asks the current device for its CU count). */
 typedef struct tcm_plan {
@@ -217,7 +236,8 @@ typedef struct tcm_plan {
     int32_t kernel;                 /* internal kernel variant id */
 } tcm_plan;
 
-/* mx == 1 plans tcm_gemm_mx_fp8, mx == 2 tcm_gemm_mx_fp4 (dtype is then ignored). */
+/* mx == 1 plans tcm_gemm_mx_fp8, mx == 2 tcm_gemm_mx_fp4, mx == 3 tcm_gemm_mx_fp6 (dtype is
+ * then ignored). */
 tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
                          tcm_dtype out_dtype, int mx, int num_cus, tcm_plan* plan);
 

@@ -28,7 +28,7 @@ __all__ = ["gemm", "gemm_tn", "gemm_tn_ex", "batched_gemm_tn", "gemm_mx_fp8", "g
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtcm.so")
 
 # tcm_dtype codes
-F16, BF16, F32, E4M3, E8M0, E2M1 = 0, 1, 2, 3, 4, 5
+F16, BF16, F32, E4M3, E8M0, E2M1, E2M3, E3M2 = 0, 1, 2, 3, 4, 5, 6, 7
 # tcm_order codes
 ROW_MAJOR, COL_MAJOR = 0, 1
 # tcm_op codes
@@ -55,7 +55,7 @@ class Plan(ctypes.Structure):
 _lock = threading.Lock()
 _lib = None
 EXPORTS = ("tcm_gemm", "tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
-           "tcm_gemm_mx_fp4", "tcm_plan_gemm", "tcm_status_string")
+           "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_plan_gemm", "tcm_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -76,11 +76,12 @@ def lib() -> ctypes.CDLL:
                                    ci, ci, ci, cf, cf, ci, vp]
             L.tcm_gemm_mx_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_gemm_mx_fp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
+            L.tcm_gemm_mx_fp6.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
             L.tcm_plan_gemm.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(Plan)]
             L.tcm_status_string.argtypes = [ci]
             L.tcm_status_string.restype = ctypes.c_char_p
             for f in ("tcm_gemm", "tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
-                      "tcm_gemm_mx_fp4", "tcm_plan_gemm"):
+                      "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_plan_gemm"):
                 getattr(L, f).restype = ci
             _lib = L
     return _lib
@@ -285,9 +286,38 @@ def gemm(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None, op="identi
     return out
 
 
+def gemm_mx_fp6(a, b, scale_a, scale_b, out=None, out_dtype=None, elem="e2m3"):
+    """MXFP6 Out = (a * scale_a) . (b * scale_b)^T.  a (M, 3K/4), b (N, 3K/4)
+    uint8 holding packed 6-bit codes (element t of a row in bits 6t .. 6t+5);
+    scale_a (M, K/32), scale_b (N, K/32) E8M0 bytes; elem "e2m3" or "e3m2"."""
+    torch = _torch()
+    M, KB = a.shape
+    N = b.shape[0]
+    if KB % 3 or b.shape[1] != KB:
+        raise ValueError("packed FP6 rows of equal length, whole three-byte groups")
+    K = KB // 3 * 4
+    if K % 32 or tuple(scale_a.shape) != (M, K // 32) or tuple(scale_b.shape) != (N, K // 32):
+        raise ValueError("scale tensors must be (rows, K/32) with K a multiple of 32")
+    for t in (a, b):
+        if t.dtype != torch.uint8:
+            raise TypeError("MXFP6 codes must be packed in uint8")
+    for t in (scale_a, scale_b):
+        if t.dtype not in (torch.uint8, torch.float8_e8m0fnu):
+            raise TypeError("MX scales must be uint8 or float8_e8m0fnu")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be {(M, N)}")
+    code = {"e2m3": E2M3, "e3m2": E3M2}[elem]
+    with torch.cuda.device(a.device):
+        _check(lib().tcm_gemm_mx_fp6(_ptr(a), _ptr(b), _ptr(scale_a), _ptr(scale_b), _ptr(out),
+                                     M, N, K, code, _code(out.dtype), _stream(a)))
+    return out
+
+
 def plan(M, N, K, dtype=BF16, out_dtype=BF16, batch=1, mx=False, num_cus=256) -> dict:
     """The launch a call would make (tile, ring depth, LDS bytes, grid).  mx:
-    False (or 0) plain, True (or 1) MXFP8, 2 MXFP4."""
+    False (or 0) plain, True (or 1) MXFP8, 2 MXFP4, 3 MXFP6."""
     p = Plan()
     _check(lib().tcm_plan_gemm(batch, M, N, K, dtype, out_dtype, int(mx), num_cus,
                                ctypes.byref(p)))

@@ -108,6 +108,26 @@ struct OpMXFP4 {
     }
 };
 
+// MXFP6: E2M3 (format code 2) or E3M2 (code 3) x the same, one E8M0 scale
+// per 32 K values.  Like FP4, lane l + 32 b holds the whole block b of row
+// l % 32: 32 six-bit codes in six registers, code t in bits 6t .. 6t + 5 of
+// their little-endian concatenation -- the same bit stream as the packed
+// storage, so a block is its 24 stored bytes.  (Established on the device:
+// with block scales 1 and 2 on A and 1 and 4 on B, a 1.0 in any of the 32
+// slots of a lane of half-wave b scaled by block b's scales.)
+template <int FMT>
+struct OpMXFP6 {
+    static constexpr int kElemBytes = 0;
+    static constexpr int kElemBits = 6;
+    static constexpr int kK = 64;
+    static constexpr bool kScaled = true;
+    typedef i32x8_t frag_t;  // registers 0..5 used
+    template <int SEL>
+    __device__ static __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c, int sa, int sb) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, SEL, sa, SEL, sb);
+    }
+};
+
 struct TileCursor {
     int tl, kk, batch, tm, tn;
 };

@@ -51,9 +51,16 @@ __global__ __launch_bounds__(kPPThreads, 1) __attribute__((amdgpu_waves_per_eu(2
 void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256;
     constexpr int EBITS = Op::kElemBits;
+    constexpr bool FP6 = EBITS == 6;
     constexpr int BK = UNIT_K;
     constexpr int RB = BK * EBITS / 8;  // bytes of one operand row's K unit
     constexpr int CPR = RB / 16;        // 16-byte chunks per row
+    // FP6 rows of a unit are 48 (64-deep) or 96 (128-deep) bytes, CPR = 3 or
+    // 6 chunks: the stage holds groups of 16 rows, chunk-major within a group
+    // (chunk k of row r at chunk index (r / 16) 16 CPR + 16 k + r % 16 of the
+    // operand region), so that 16 lanes reading one chunk of 16 consecutive
+    // rows touch 16 consecutive chunks: every bank once.
+    constexpr int GROUP = 16 * CPR;  // chunks of a 16-row group (FP6)
     // chunk ^= row bits chosen so that the 16 rows read together by 16 lanes
     // fall on 16 different 16-byte bank groups (64 banks of 4 bytes)
     constexpr int SWZ = CPR == 8 ? 1 : 2;
@@ -84,15 +91,16 @@ void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int A_COPIES = A_BYTES / 1024;
     constexpr int PW = DATA / 1024 / NCW;              // operand copies per wave per unit
     constexpr int OPS = PW + (SC_LDS ? 1 : 0);         // DMA operations per wave per unit
-    constexpr int RPC = 1024 / RB;                     // rows per copy instruction
+    constexpr int RPC = FP6 ? 16 : 1024 / RB;          // rows per copy instruction (not FP6)
     // epilogue staging: 32 (or, where the ring leaves less room, 16) rows x
-    // 64 columns per wave (bf16 only)
-    constexpr bool EPI_LDS = sizeof(TOut) == 2;
+    // 64 columns per wave (bf16 only, and only where 16 rows fit)
     constexpr int STG_ROWB = WTN * (int)sizeof(TOut);
     constexpr int RING = S * STAGE + SC_CHUNK_TOTAL;
+    constexpr bool EPI_LDS = sizeof(TOut) == 2 && RING + 8 * 16 * STG_ROWB <= 160 * 1024;
     constexpr int STG_ROWS = RING + 8 * 32 * STG_ROWB <= 160 * 1024 ? 32 : 16;
     constexpr int STG_BYTES = EPI_LDS ? STG_ROWS * STG_ROWB : 0;
-    static_assert(CPR == 4 || CPR == 8, "64- or 128-byte rows");
+    static_assert(CPR == 4 || CPR == 8 || (FP6 && (BK == 64 || BK == 128)),
+                  "64- or 128-byte rows, or FP6 units of 64 or 128");
     static_assert(KSTEPS >= 1 && KSTEPS <= 4, "K steps per unit");
     static_assert(!Op::kScaled || KSTEPS <= 2, "scale bytes per register");
     static_assert((DATA / 1024) % NCW == 0, "copy split");
@@ -105,7 +113,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
                   "one scale DMA per wave: 4 x 64 A rows, 4 x 64 B rows");
     static_assert(!SC_CHUNK || UPC * KSTEPS == 8, "8 packed scale bytes per lane per chunk");
     static_assert(!SC_CHUNK || UPC >= 2, "a chunk lands two halves after its DMA");
-    static_assert((32 >> SWZ) % CPR == 0, "swizzle depends on the row within 32 only");
+    static_assert(FP6 || (32 >> SWZ) % CPR == 0, "swizzle depends on the row within 32 only");
 
     __shared__ __attribute__((aligned(1024))) char lds[RING + 8 * STG_BYTES];
 
@@ -140,7 +148,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // so a lane's chunk is the same in all of them: one lane offset serves
     // every copy, and each copy adds the wave-uniform row offset RPC qq K.
     const int cw = COPY_GROUPS == 2 ? wave : sub;
-    static_assert((NCW * RPC) % (CPR << SWZ) == 0 && (A_COPIES * RPC) % (CPR << SWZ) == 0,
+    static_assert(FP6 || ((NCW * RPC) % (CPR << SWZ) == 0 && (A_COPIES * RPC) % (CPR << SWZ) == 0),
                   "chunk independent of the copy");
     const int cp_row = lane / CPR;
     const int sw_row = cw * RPC + cp_row;  // congruent to every copied row of the lane
@@ -152,6 +160,23 @@ void pingpong_gemm_kernel(GemmArgs p) {
         const int qq = q < A_COPIES ? q : q - A_COPIES;
         return (uint32_t)(qq * RPC) * ROWB;
     };
+    // FP6: copy t fills chunk Qo = 64 qq + lane of its operand region (qq the
+    // copy's index within A or B): row 16 (Qo / 48) + Qo % 16, chunk
+    // (Qo % 48) / 16.  The pattern has no uniform step, so each copy keeps
+    // its own lane offset and chunk byte (for the K tail).
+    uint32_t off6[FP6 ? PW : 1];
+    int cb6[FP6 ? PW : 1];
+    if constexpr (FP6) {
+#pragma unroll
+        for (int t = 0; t < PW; ++t) {
+            const int q = cw + t * NCW;
+            const int qq = q < A_COPIES ? q : q - A_COPIES;
+            const int Qo = 64 * qq + lane;
+            const int r = 16 * (Qo / GROUP) + Qo % 16, k = (Qo % GROUP) / 16;
+            off6[t] = (uint32_t)r * ROWB + 16 * k;
+            cb6[t] = 16 * k;
+        }
+    }
     TileCursor fc = {0, 0, 0, 0, 0};
     __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
     const int kblocks = K / 32;
@@ -208,12 +233,19 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // for pieces past K.
     auto copy_base = [&]() -> uint32_t {
         const int k0 = fc.kk * BK;
-        return (fu < T && k0 + cp_k < K) ? cp_lane_off + (uint32_t)k0 * EBITS / 8 : kOutOfRange;
+        if constexpr (FP6)  // the unit's first byte within a row (the offsets are per copy)
+            return fu < T ? (uint32_t)k0 * EBITS / 8 : kOutOfRange;
+        else
+            return (fu < T && k0 + cp_k < K) ? cp_lane_off + (uint32_t)k0 * EBITS / 8 : kOutOfRange;
     };
     auto issue_one = [&](int t, uint32_t base) {
         const int q = cw + t * NCW;
-        copy16_to_lds(q < A_COPIES ? ra : rb, lds + (fu % S) * STAGE + q * 1024,
-                      base + copy_row_off(t));
+        uint32_t off;
+        if constexpr (FP6)
+            off = base != kOutOfRange && base + cb6[t] < ROWB ? base + off6[t] : kOutOfRange;
+        else
+            off = base + copy_row_off(t);
+        copy16_to_lds(q < A_COPIES ? ra : rb, lds + (fu % S) * STAGE + q * 1024, off);
     };
     auto issue_finish = [&]() {
         char* st = lds + (fu % S) * STAGE;
@@ -242,13 +274,27 @@ void pingpong_gemm_kernel(GemmArgs p) {
 
     // ---- fragments of one unit -------------------------------------------------
     const int xr = (l32 >> SWZ) & (CPR - 1);
-    const uint32_t a_frag = (uint32_t)(grp * WTM + l32) * RB;
-    const uint32_t b_frag = (uint32_t)A_BYTES + (uint32_t)(sub * WTN + l32) * RB;
+    // FP6: byte of chunk 0 of row R in the grouped layout; the block of
+    // half-wave hi is chunk 2 hi (16 bytes) and half hi of chunk 1 (8 bytes)
+    auto fp6_row = [&](int R) -> uint32_t { return (uint32_t)(((R / 16) * GROUP + R % 16) * 16); };
+    const uint32_t a_frag = FP6 ? fp6_row(grp * WTM + l32) : (uint32_t)(grp * WTM + l32) * RB;
+    const uint32_t b_frag = (uint32_t)A_BYTES +
+                            (FP6 ? fp6_row(sub * WTN + l32) : (uint32_t)(sub * WTN + l32) * RB);
+    // distance between fragment blocks of 32 rows
+    constexpr uint32_t FRAG_STRIDE = FP6 ? 2 * GROUP * 16 : 32 * RB;
     typedef typename Op::frag_t frag_t;
     frag_t fa[KSTEPS][FM], fb[KSTEPS][FN];
     auto read_frag = [&](const char* base, int s) -> frag_t {
         frag_t f;
-        if constexpr (EBITS == 4) {
+        if constexpr (FP6) {
+            // K step s holds blocks 2s and 2s + 1, chunks 3s .. 3s + 2: block
+            // 2s is chunk 3s then the low half of chunk 3s + 1, block 2s + 1
+            // the high half of chunk 3s + 1 then chunk 3s + 2
+            const i32x4_t c16 = *(const i32x4_t*)(base + 256 * (3 * s + 2 * hi));
+            const i32x2_t c8 = *(const i32x2_t*)(base + 256 * (3 * s + 1) + 8 * hi);
+            f = hi ? (i32x8_t){c8[0], c8[1], c16[0], c16[1], c16[2], c16[3], 0, 0}
+                   : (i32x8_t){c16[0], c16[1], c16[2], c16[3], c8[0], c8[1], 0, 0};
+        } else if constexpr (EBITS == 4) {
             // MXFP4: half-wave hi holds block hi of the MFMA's 64 K values,
             // the 16-byte chunk 2s + hi of the row
             f = *(const frag_t*)(base + (((2 * s + hi) ^ xr) * 16));
@@ -268,9 +314,9 @@ void pingpong_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fa[s][i] = read_frag(st + a_frag + i * 32 * RB, s);
+            for (int i = 0; i < FM; ++i) fa[s][i] = read_frag(st + a_frag + i * FRAG_STRIDE, s);
 #pragma unroll
-            for (int jj = 0; jj < FN; ++jj) fb[s][jj] = read_frag(st + b_frag + jj * 32 * RB, s);
+            for (int jj = 0; jj < FN; ++jj) fb[s][jj] = read_frag(st + b_frag + jj * FRAG_STRIDE, s);
         }
     };
 

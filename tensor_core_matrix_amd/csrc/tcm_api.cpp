@@ -38,6 +38,7 @@ VariantInfo variant_info(int32_t v) {
     case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 8, 512};
     case V_MXPP256_K64S4_CM: return {256, 256, 64, 4, 1, 8, 512};
     case V_MX4PP256: return {256, 256, 128, 4, 1, 4, 512};
+    case V_MX6PP256: return {256, 256, 64, 4, 1, 6, 512};
     }
     return {0, 0, 0, 0, 0, 0, kThreads};
 }
@@ -94,7 +95,9 @@ int elem_bytes(tcm_dtype d) {
     case TCM_F32: return 4;
     case TCM_E4M3:
     case TCM_E8M0: return 1;
-    case TCM_E2M1: return 0;  // two per byte
+    case TCM_E2M1:
+    case TCM_E2M3:
+    case TCM_E3M2: return 0;  // packed below a byte
     }
     return 0;
 }
@@ -138,15 +141,16 @@ int64_t max_grid() {
 
 // Tile choice: the largest tile whose tile count still gives every CU at
 // least one tile with little padding; small problems take the smallest tile.
-// Families by element bits: 16 (f16/bf16), 8 (MXFP8), 4 (MXFP4).
+// Families by element bits: 16 (f16/bf16), 8 (MXFP8), 6 (MXFP6), 4 (MXFP4).
 int32_t choose_variant(int64_t batch, int64_t M, int64_t N, int32_t bits, int cus) {
     const int32_t f = forced_variant();
     if (f >= 0 && variant_info(f).tile_m > 0 && variant_info(f).elem_bits == bits) return f;
     static const int32_t plain[] = {V_T256x256_SPLIT3, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MXPP256_K64S4, V_MX128x128};
     static const int32_t mx4[] = {V_MX4PP256};
-    const int32_t* cand = bits == 8 ? mxv : bits == 4 ? mx4 : plain;
-    const int n = bits == 8 ? 2 : bits == 4 ? 1 : 4;
+    static const int32_t mx6[] = {V_MX6PP256};
+    const int32_t* cand = bits == 8 ? mxv : bits == 4 ? mx4 : bits == 6 ? mx6 : plain;
+    const int n = bits == 8 ? 2 : bits == 4 ? 1 : bits == 6 ? 1 : 4;
     for (int i = 0; i < n; ++i) {
         VariantInfo vi = variant_info(cand[i]);
         int64_t tiles = batch * cdiv(M, vi.tile_m) * cdiv(N, vi.tile_n);
@@ -265,18 +269,22 @@ tcm_status tcm_batched_gemm_tn(const void* A, const void* B, void* Out, int64_t 
 
 namespace {
 
-// The MX entry points: elements of `bits` bits (8 = E4M3, 4 = E2M1 pairs).
+// The MX entry points: elements of `bits` bits (8 = E4M3, 6 = E2M3 or E3M2 as
+// elem_dtype says, 4 = E2M1 pairs).
 tcm_status run_mx(int32_t bits, const void* A, const void* B, const void* scale_A,
                   const void* scale_B, void* Out, int64_t M, int64_t N, int64_t K,
-                  tcm_dtype out_dtype, void* stream) {
+                  tcm_dtype out_dtype, void* stream, tcm_dtype elem_dtype = TCM_E4M3) {
     if (!(out_dtype == TCM_F32 || out_dtype == TCM_BF16)) return TCM_ERR_UNSUPPORTED_DTYPE;
+    if (bits == 6 && !(elem_dtype == TCM_E2M3 || elem_dtype == TCM_E3M2))
+        return TCM_ERR_UNSUPPORTED_DTYPE;
     bool empty = false;
     tcm_status s = check_sizes(1, M, N, K, &empty);
     if (s != TCM_OK || empty) return s;
     if (!Out || (K > 0 && (!A || !B || !scale_A || !scale_B))) return TCM_ERR_NULL_POINTER;
     if ((s = check_range(1, M, N, K)) != TCM_OK) return s;
     if (K % 32 != 0) return TCM_ERR_UNSUPPORTED_SHAPE;
-    // rows of K * bits / 8 bytes (K % 32 == 0 makes them whole 16-byte pieces)
+    // rows of K * bits / 8 bytes, whole 16-byte pieces (K % 32 == 0 suffices
+    // for 8 and 4 bits; 6 bits need K % 64 == 0)
     if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) || (K * bits / 8) % 16 != 0)
         return TCM_ERR_MISALIGNED;
     DeviceInfo dev;
@@ -300,8 +308,11 @@ tcm_status run_mx(int32_t bits, const void* A, const void* B, const void* scale_
         scale_mode = 2;
     else if (K > 0 && K % 128 == 0 && ((sa | sb) & 3u) == 0)
         scale_mode = 1;
-    hipError_t e = launch_gemm_mx(plan.kernel, (int32_t)out_dtype, scale_mode, a, plan.grid,
-                                  (hipStream_t)stream);
+    hipError_t e = bits == 6 ? launch_gemm_mx6(plan.kernel, (int32_t)out_dtype, scale_mode,
+                                               (int32_t)elem_dtype, a, plan.grid,
+                                               (hipStream_t)stream)
+                             : launch_gemm_mx(plan.kernel, (int32_t)out_dtype, scale_mode, a,
+                                              plan.grid, (hipStream_t)stream);
     return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
 }
 
@@ -319,6 +330,12 @@ tcm_status tcm_gemm_mx_fp4(const void* A, const void* B, const void* scale_A, co
                            void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
                            void* stream) {
     return run_mx(4, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream);
+}
+
+tcm_status tcm_gemm_mx_fp6(const void* A, const void* B, const void* scale_A, const void* scale_B,
+                           void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype elem_dtype,
+                           tcm_dtype out_dtype, void* stream) {
+    return run_mx(6, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream, elem_dtype);
 }
 
 tcm_status tcm_gemm_tn_ex(const void* A, const void* B, const void* C, void* Out, int64_t M,
@@ -451,7 +468,7 @@ tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dty
         num_cus = dev.cus;
     }
     make_plan(batch < 1 ? 1 : batch, M < 1 ? 1 : M, N < 1 ? 1 : N, K,
-              mx == 2 ? 4 : mx ? 8 : 16, num_cus, plan, nullptr);
+              mx == 3 ? 6 : mx == 2 ? 4 : mx ? 8 : 16, num_cus, plan, nullptr);
     if (empty) {
         plan->grid = 0;
         plan->tiles = 0;

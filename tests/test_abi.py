@@ -91,6 +91,23 @@ def test_alignment_rejected():
     assert L.tcm_gemm_mx_fp4(A, B, SA, SB, C + 2, 64, 64, 64, tcm.F32, None) == MISALIGNED
 
 
+def test_mxfp6_entry_validation():
+    L = tcm.lib()
+    f6 = lambda K=64, elem=tcm.E2M3, odt=tcm.BF16, a=A: L.tcm_gemm_mx_fp6(
+        a, B, SA, SB, C, 64, 64, K, elem, odt, None)
+    assert f6() in (OK, NO_DEVICE)
+    assert f6(elem=tcm.E3M2) in (OK, NO_DEVICE)
+    assert f6(elem=tcm.E4M3) == UNSUP_DTYPE
+    assert f6(odt=tcm.F16) == UNSUP_DTYPE
+    assert f6(K=48) == UNSUP_SHAPE          # not whole scale blocks
+    assert f6(K=96) == MISALIGNED           # 72-byte rows
+    assert f6(a=A + 8) == MISALIGNED
+    assert f6(a=None) == NULLP
+    p = tcm.plan(8192, 8192, 8192, mx=3)
+    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"]) == \
+        (256, 64, 24 * 1024, 4, 512)
+
+
 def test_valid_call_without_gpu_reports_no_device():
     try:
         import torch

@@ -1,0 +1,111 @@
+"""Parity of the MXFP6 path (FP6 E2M3 or E3M2 codes packed four per three
+bytes, E8M0 scales per 32) with the fp64 oracle, through the C ABI.  Same
+acceptance rule as the other products: |gpu - ref| <= 1e-4 * sum_k |a_ik b_jk|
+(+ one bf16 ulp for bf16 output).  With unit scales, E2M3 products and sums
+up to K = 1024 are exact in fp32, so those cases must match bit for bit.  The
+shapes reach all three ways of reading the scales (bytes: K = 576, 32-bit
+words: K = 640, 16-byte pieces: K = 1536)."""
+import numpy as np
+import pytest
+import torch
+
+import tensor_core_matrix_amd as tcm
+from oracle import oracle as orc
+from tensor_core_matrix_amd import inputs as inp
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+OUT = {"f32": torch.float32, "bf16": torch.bfloat16}
+GUARD = 256
+
+
+def run_fp6(a, b, sa, sb, out_dtype, elem):
+    n = a.shape[0] * b.shape[0]
+    buf = torch.full((n + 2 * GUARD,), float("nan"), dtype=OUT[out_dtype], device=DEV)
+    out = buf[GUARD:GUARD + n].view(a.shape[0], b.shape[0])
+    tcm.gemm_mx_fp6(a.to(DEV), b.to(DEV), sa.to(DEV), sb.to(DEV), out, elem=elem)
+    torch.cuda.synchronize()
+    canary = torch.cat([buf[:GUARD], buf[-GUARD:]]).float()
+    assert bool(torch.isnan(canary).all()), "write outside the output"
+    return out.cpu()
+
+
+def check(gpu, ref, s, out_dtype, what):
+    ok, worst, nbad = orc.check(gpu.double().numpy(), ref, s, out_dtype == "bf16")
+    assert ok, f"{what}: {nbad} violations, worst err/bound {worst:.3g}"
+
+
+def make(M, N, K, seed, lo=-4, hi=4):
+    g = inp.generator(seed)
+    a = inp.fp6_codes(M, K, g)
+    b = inp.fp6_codes(N, K, g)
+    sa = inp.e8m0_scales((M, K // 32), g, lo, hi)
+    sb = inp.e8m0_scales((N, K // 32), g, lo, hi)
+    return a, b, sa, sb
+
+
+def oracle(a, b, sa, sb, elem):
+    return orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb),
+                       dtype=orc.DTYPE_NAMES[elem])
+
+
+@pytest.fixture
+def grid_cap(monkeypatch):
+    def _set(n):
+        if n is None:
+            monkeypatch.delenv("TCM_MAX_GRID", raising=False)
+        else:
+            monkeypatch.setenv("TCM_MAX_GRID", str(n))
+    return _set
+
+
+@pytest.mark.parametrize("K", [576, 640, 1536])
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+@pytest.mark.parametrize("elem", ["e2m3", "e3m2"])
+def test_mxfp6_ragged(K, odt, elem, grid_cap):
+    M, N = 700, 520
+    a, b, sa, sb = make(M, N, K, 1000 + K)
+    ref, s = oracle(a, b, sa, sb, elem)
+    grid_cap(None)
+    check(run_fp6(a, b, sa, sb, odt, elem), ref, s, odt, f"mxfp6 {elem} K {K} {odt}")
+    grid_cap(3)
+    check(run_fp6(a, b, sa, sb, odt, elem), ref, s, odt, f"mxfp6 {elem} K {K} {odt} grid 3")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 64), (33, 17, 64), (256, 256, 128), (300, 260, 1024)])
+def test_mxfp6_unit_scales_exact(shape):
+    M, N, K = shape
+    a, b, _, _ = make(M, N, K, 1100 + K)
+    sa = torch.full((M, K // 32), 127, dtype=torch.uint8)
+    sb = torch.full((N, K // 32), 127, dtype=torch.uint8)
+    ref, _ = oracle(a, b, sa, sb, "e2m3")
+    got = run_fp6(a, b, sa, sb, "f32", "e2m3").double().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_mxfp6_scale_reaches_only_its_block():
+    M, N, K = 64, 48, 256
+    a, b, _, _ = make(M, N, K, 1110)
+    sa = torch.full((M, K // 32), 127, dtype=torch.uint8)
+    sb = torch.full((N, K // 32), 127, dtype=torch.uint8)
+    base = run_fp6(a, b, sa, sb, "f32", "e2m3").double().numpy()
+    sa2 = sa.clone()
+    sa2[5, 3] = 127 + 4
+    got = run_fp6(a, b, sa2, sb, "f32", "e2m3").double().numpy()
+    ref, _ = oracle(a, b, sa2, sb, "e2m3")
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.delete(got, 5, 0), np.delete(base, 5, 0))
+
+
+def test_workload_mxfp6():
+    w = inp.WORKLOADS["mxfp6_8192"]
+    x = inp.make(w)
+    out = run_fp6(x["A"], x["B"], x["SA"], x["SB"], "bf16", w.dtype)
+    rng = np.random.default_rng(w.seed)
+    ii = np.concatenate([rng.integers(0, w.M, 4096), [0, w.M - 1, 0, w.M - 1]])
+    jj = np.concatenate([rng.integers(0, w.N, 4096), [0, 0, w.N - 1, w.N - 1]])
+    dt = orc.DTYPE_NAMES[w.dtype]
+    ref, s = orc.entries(dt, inp.raw(x["A"]), inp.raw(x["B"]), ii, jj,
+                         sa=inp.raw(x["SA"]), sb=inp.raw(x["SB"]))
+    check(out[torch.from_numpy(ii), torch.from_numpy(jj)], ref, s, "bf16", "mxfp6 8192")
