@@ -530,3 +530,72 @@ int oracle_apply_op(int64_t n, int op, const double* x, double* out) {
     }
     return 0;
 }
+
+/*
+ * NVFP4 ("Hopper and Blackwell GEMM", Concept, "FP8 and FP4, with block
+ * scaling", the format table's NVFP4 row): E2M1 elements (stored as for
+ * MXFP4, two per byte), one E4M3 scale per 16 consecutive K elements of every
+ * row of A and of B (SA: M x K/16 bytes, SB: N x K/16), and one FP32 scale per
+ * tensor (gA, gB):
+ *
+ *   a(i,k) = e2m1(A[i][k]) * e4m3(SA[i][k/16]) * gA
+ *   b(j,k) = e2m1(B[j][k]) * e4m3(SB[j][k/16]) * gB
+ *
+ * and then the same sums as every other form.  gA, gB are the exact values of
+ * the fp32 arguments.
+ */
+static double nv4_value(const uint8_t* X, const uint8_t* SX, double g, int64_t K, int64_t r,
+                        int64_t k) {
+    const int64_t idx = r * K + k;
+    const uint8_t byte = X[idx / 2];
+    return dec_e2m1((idx & 1) ? byte >> 4 : byte & 0xF) * dec_e4m3(SX[r * (K / 16) + k / 16]) * g;
+}
+
+int oracle_gemm_nvfp4(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const uint8_t* SB,
+                      double gA, double gB, int64_t M, int64_t N, int64_t K, double* ref,
+                      double* abssum, int nthreads) {
+    if (!A || !B || !SA || !SB || !shape_ok(1, M, N, K) || K % 16 != 0)
+        return -1;
+    double* a = (double*)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
+    double* b = (double*)malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(double));
+    if (!a || !b) {
+        free(a);
+        free(b);
+        return -2;
+    }
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k)
+            a[i * K + k] = nv4_value(A, SA, gA, K, i, k);
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k)
+            b[j * K + k] = nv4_value(B, SB, gB, K, j, k);
+    int rc = run_rows(a, b, M, N, K, ref, abssum, nthreads);
+    free(a);
+    free(b);
+    return rc;
+}
+
+/* Selected entries (ii[t], jj[t]) of the NVFP4 product, one by one. */
+int oracle_entries_nvfp4(const uint8_t* A, const uint8_t* B, const uint8_t* SA,
+                         const uint8_t* SB, double gA, double gB, int64_t M, int64_t N, int64_t K,
+                         const int64_t* ii, const int64_t* jj, int64_t n, double* ref,
+                         double* abssum) {
+    if (!A || !B || !SA || !SB || !ii || !jj || !shape_ok(1, M, N, K) || K % 16 != 0)
+        return -1;
+    for (int64_t t = 0; t < n; ++t) {
+        const int64_t i = ii[t], j = jj[t];
+        if (i < 0 || i >= M || j < 0 || j >= N)
+            return -1;
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double prod = nv4_value(A, SA, gA, K, i, k) * nv4_value(B, SB, gB, K, j, k);
+            s += prod;
+            sa += fabs(prod);
+        }
+        if (ref)
+            ref[t] = s;
+        if (abssum)
+            abssum[t] = sa;
+    }
+    return 0;
+}

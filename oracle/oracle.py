@@ -83,9 +83,14 @@ def _load():
             lib.oracle_entries_ld.argtypes = [ci, vp, ci, i64, vp, ci, i64, i64, i64, i64, vp,
                                               vp, i64, dp, dp]
             lib.oracle_apply_op.argtypes = [i64, ci, dp, dp]
+            cd = ctypes.c_double
+            lib.oracle_gemm_nvfp4.argtypes = [vp, vp, vp, vp, cd, cd, i64, i64, i64, dp, dp, ci]
+            lib.oracle_entries_nvfp4.argtypes = [vp, vp, vp, vp, cd, cd, i64, i64, i64, vp, vp, i64,
+                                                 dp, dp]
             for f in (lib.oracle_decode, lib.oracle_gemm_tn, lib.oracle_gemm_mx,
                       lib.oracle_gemm_mx_typed, lib.oracle_entries, lib.oracle_axpby,
-                      lib.oracle_gemm_ld, lib.oracle_entries_ld, lib.oracle_apply_op):
+                      lib.oracle_gemm_ld, lib.oracle_entries_ld, lib.oracle_apply_op,
+                      lib.oracle_gemm_nvfp4, lib.oracle_entries_nvfp4):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -171,6 +176,43 @@ def gemm_mx(a: np.ndarray, b: np.ndarray, sa: np.ndarray, sb: np.ndarray,
                                       _ptr(ref), _ptr(s), nthreads or default_threads())
     if rc:
         raise ValueError(f"oracle_gemm_mx failed ({rc})")
+    return ref, s
+
+
+def _nv4_args(a, b, sa, sb):
+    a, b = _raw(a, E2M1), _raw(b, E2M1)
+    sa, sb = _raw(sa, E4M3), _raw(sb, E4M3)
+    M, N, K = a.shape[0], b.shape[0], a.shape[1] * 2
+    if b.shape[1] * 2 != K or K % 16 or sa.shape != (M, K // 16) or sb.shape != (N, K // 16):
+        raise ValueError("bad NVFP4 shapes")
+    return a, b, sa, sb, M, N, K
+
+
+def gemm_nvfp4(a, b, sa, sb, ga: float, gb: float, nthreads: int | None = None):
+    """ref, abssum for the NVFP4 product (see oracle.c): a M x K/2, b N x K/2
+    E2M1 pairs; sa M x K/16, sb N x K/16 E4M3 bytes; ga, gb the per-tensor
+    fp32 scales."""
+    a, b, sa, sb, M, N, K = _nv4_args(a, b, sa, sb)
+    ref = np.empty((M, N), np.float64)
+    s = np.empty((M, N), np.float64)
+    rc = _load().oracle_gemm_nvfp4(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), float(ga), float(gb), M,
+                                   N, K, _ptr(ref), _ptr(s), nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_gemm_nvfp4 failed ({rc})")
+    return ref, s
+
+
+def entries_nvfp4(a, b, sa, sb, ga: float, gb: float, ii, jj):
+    """ref, abssum at outputs (ii[t], jj[t]) of the NVFP4 product."""
+    a, b, sa, sb, M, N, K = _nv4_args(a, b, sa, sb)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    ref = np.empty(ii.size, np.float64)
+    s = np.empty(ii.size, np.float64)
+    rc = _load().oracle_entries_nvfp4(_ptr(a), _ptr(b), _ptr(sa), _ptr(sb), float(ga), float(gb),
+                                      M, N, K, _ptr(ii), _ptr(jj), ii.size, _ptr(ref), _ptr(s))
+    if rc:
+        raise ValueError(f"oracle_entries_nvfp4 failed ({rc})")
     return ref, s
 
 

@@ -120,6 +120,14 @@ def fp6_codes(rows: int, k: int, gen) -> torch.Tensor:
     return pack_fp6(torch.randint(0, 64, (rows, k), generator=gen, dtype=torch.int32))
 
 
+def e4m3_scales(shape, gen, lo=-4, hi=4) -> torch.Tensor:
+    """Positive E4M3 scale bytes with exponent uniform on the integers lo..hi
+    and every mantissa equally likely (NVFP4 block scales)."""
+    e = torch.randint(lo, hi + 1, shape, generator=gen, dtype=torch.int32) + 7
+    m = torch.randint(0, 8, shape, generator=gen, dtype=torch.int32)
+    return ((e << 3) | m).to(torch.uint8)
+
+
 def e8m0_scales(shape, gen, lo=-4, hi=4) -> torch.Tensor:
     """E8M0 bytes 127+s with s uniform on the integers lo..hi."""
     return (torch.randint(lo, hi + 1, shape, generator=gen, dtype=torch.int32)

@@ -24,6 +24,11 @@ applied to the wrong block -- fails at least one of them:
   of a hand-packed three-byte group, every value re-encoded by torch's E4M3
   cast decoding the same (both formats are subsets of E4M3), the MXFP6
   product equal to the MXFP8 product of the same values, and brute force;
+* NVFP4 (E2M1 with an E4M3 scale per 16 and an fp32 scale per tensor): with
+  power-of-two block scales equal across each 32-block and unit tensor scales
+  it is the MXFP4 product of the same powers; power-of-two tensor scales
+  scale exactly; brute force with the block scales decoded by torch's E4M3;
+  a scale read per 32 instead of per 16 breaks the pins;
 * operand arrangements and leading dimensions: every row-/column-major pair,
   stored through torch's own transposes inside NaN-padded rows, equals the
   pinned TN product bit for bit (a swapped index or an ignored leading
@@ -170,6 +175,71 @@ def test_brute_force_mxfp6(shape):
                       * val(int(codes_b[j, k])) * Fraction(2) ** int(eb[j, k // 32])
                       for k in range(K)), Fraction(0))
             assert Fraction(ref[i, j]) == ex
+
+
+def _nv4_case(M, N, K, seed):
+    g = inp.generator(seed)
+    return (inp.e2m1_codes(M, K, g), inp.e2m1_codes(N, K, g),
+            inp.e4m3_scales((M, K // 16), g), inp.e4m3_scales((N, K // 16), g))
+
+
+def test_nvfp4_power_of_two_scales_equal_mxfp4():
+    M, N, K = 9, 7, 128
+    g = inp.generator(51)
+    a, b = inp.e2m1_codes(M, K, g), inp.e2m1_codes(N, K, g)
+    ea = torch.randint(-5, 6, (M, K // 32), generator=g)
+    eb = torch.randint(-5, 6, (N, K // 32), generator=g)
+    # E4M3 2^e: exponent field e + 7, mantissa 0; each 32-block's two halves alike
+    sa4 = ((ea + 7) << 3).repeat_interleave(2, dim=1).to(torch.uint8)
+    sb4 = ((eb + 7) << 3).repeat_interleave(2, dim=1).to(torch.uint8)
+    ref, s = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa4), inp.raw(sb4), 1.0, 1.0)
+    mx, ms = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw((ea + 127).to(torch.uint8)),
+                         inp.raw((eb + 127).to(torch.uint8)), dtype=orc.E2M1)
+    assert _same(ref, mx) and _same(s, ms)
+    # power-of-two tensor scales scale exactly; others to within fp64 rounding
+    r2, _ = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa4), inp.raw(sb4), 4.0, 0.125)
+    assert _same(r2, 0.5 * ref)
+    r3, _ = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa4), inp.raw(sb4), 0.3, 1.0)
+    assert np.all(np.abs(r3 - 0.3 * ref) <= 1e-14 * 0.3 * s)   # relative to sum |terms|
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (3, 4, 64)])
+def test_brute_force_nvfp4(shape):
+    M, N, K = shape
+    a, b, sa, sb = _nv4_case(M, N, K, 52 + K)
+    ref, _ = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), 0.75, -2.0)
+    mag = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+           Fraction(4), Fraction(6)]
+
+    def val(packed, r, k):
+        byte = int(packed[r, k // 2])
+        c = (byte >> 4) if k % 2 else (byte & 15)
+        return -mag[c & 7] if c & 8 else mag[c & 7]
+
+    # block scales decoded by torch's own E4M3 type, not by the oracle
+    fa = sa.view(torch.float8_e4m3fn).double().numpy()
+    fb = sb.view(torch.float8_e4m3fn).double().numpy()
+    an, bn = a.numpy(), b.numpy()
+    for i in range(M):
+        for j in range(N):
+            ex = sum((val(an, i, k) * Fraction(fa[i, k // 16]) * val(bn, j, k) * Fraction(fb[j, k // 16])
+                      for k in range(K)), Fraction(0)) * Fraction(0.75) * Fraction(-2.0)
+            assert abs(Fraction(ref[i, j]) - ex) <= Fraction(K * 2.0 ** -52) * abs(ex) + Fraction(2.0 ** -1000)
+
+
+def test_nvfp4_entries_and_planted_block_size():
+    M, N, K = 13, 11, 96
+    a, b, sa, sb = _nv4_case(M, N, K, 53)
+    ref, s = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), 1.5, 0.5)
+    ii, jj = np.array([0, 12, 7]), np.array([10, 0, 4])
+    r, ss = orc.entries_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), 1.5, 0.5, ii, jj)
+    assert _same(r, ref[ii, jj]) and _same(ss, s[ii, jj])
+    # planted on the CPU: one scale per 32 (the even 16-blocks' scale used for
+    # both halves) is a different product
+    wrong_a = sa[:, 0::2].repeat_interleave(2, dim=1).contiguous()
+    wrong_b = sb[:, 0::2].repeat_interleave(2, dim=1).contiguous()
+    w, _ = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(wrong_a), inp.raw(wrong_b), 1.5, 0.5)
+    assert not _same(w, ref)
 
 
 def test_decode_e8m0_all_patterns():
