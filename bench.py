@@ -6,7 +6,7 @@
 A step is one call of the product on the headline workload: bfloat16
 8192 x 8192 x 8192, fp32 accumulation, bf16 output (persistent 256 x 256 x 64
 tiles), inputs N(0,1)*0.05 from seed 3, already resident in HBM.  The other
-measured workloads (MXFP8, MXFP6 and MXFP4 8192^3, bf16 4096^3, 1024 batched 128x256x64 and
+measured workloads (MXFP8, MXFP6, MXFP4 and NVFP4 8192^3, bf16 4096^3, 1024 batched 128x256x64 and
 the 128x64x64 single tile, and bf16 8192^3 with both operands row-major) are
 timed after it and reported in the same line.
 
@@ -32,10 +32,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s and % of MFMA dense peak (bf16 8192³; MXFP8 8192³)"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.3,
-               "e2m3": 10066.3, "e3m2": 10066.3}  # dense MFMA, MI355X (fp6 as fp4)
+               "e2m3": 10066.3, "e3m2": 10066.3,   # dense MFMA, MI355X (fp6 as fp4)
+               "nvfp4": 2516.6}  # NVFP4 runs on the fp16 matrix cores (dequantized in the copies)
 HBM_GBS = 8000.0
 KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pingpong.h", "tcm_device.h", "tcm_internal.h", "gemm_tn.hip",
-                  "gemm_mx.hip", "gemm_mx6.hip", "gemm_epi.hip", "gemm_mn.h", "gemm_mn_a.hip", "gemm_mn_b.hip",
+                  "gemm_mx.hip", "gemm_mx6.hip", "gemm_nv4.hip", "gemm_epi.hip", "gemm_mn.h", "gemm_mn_a.hip", "gemm_mn_b.hip",
                   "gemm_mn_ab.hip", "tcm_api.cpp"]
 
 
@@ -91,6 +92,10 @@ def prepare(name, torch, inp, tcm):
         out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
         mx = tcm.gemm_mx_fp8 if w.dtype == "e4m3" else tcm.gemm_mx_fp4
         fn = lambda: mx(x["A"], x["B"], x["SA"], x["SB"], out)
+    elif w.dtype == "nvfp4":
+        out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
+        ga, gb = w.globals
+        fn = lambda: tcm.gemm_nvfp4(x["A"], x["B"], x["SA"], x["SB"], ga, gb, out)
     elif w.dtype in ("e2m3", "e3m2"):
         out = torch.empty(w.M, w.N, dtype=odt, device="cuda")
         fn = lambda: tcm.gemm_mx_fp6(x["A"], x["B"], x["SA"], x["SB"], out, elem=w.dtype)
@@ -176,8 +181,8 @@ def main() -> int:
     from tensor_core_matrix_amd import inputs as inp
 
     tcm.lib()
-    order = ["bf16_8192", "mxfp8_8192", "mxfp6_8192", "mxfp4_8192", "bf16_8192_nn", "bf16_4096",
-             "batched", "tile_f16"]
+    order = ["bf16_8192", "mxfp8_8192", "mxfp6_8192", "mxfp4_8192", "nvfp4_8192", "bf16_8192_nn",
+             "bf16_4096", "batched", "tile_f16"]
     if args.only:
         order = [args.only]
     results = {}

@@ -221,6 +221,25 @@ tcm_status tcm_gemm_mx_fp6(const void* A, const void* B, const void* scale_A, co
                            void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype elem_dtype,
                            tcm_dtype out_dtype, void* stream);
 
+/*
+ * NVFP4 Out = gA gB (A * SA) . (B * SB)^T ("Hopper and Blackwell GEMM",
+ * Concept, "FP8 and FP4, with block scaling": the format table's NVFP4 row,
+ * E2M1 elements with an E4M3 scale per 16 values and one FP32 scale per
+ * tensor).
+ *   A        M x K E2M1 elements stored M x (K/2) bytes (TCM_E2M1 packing)
+ *   B        N x K E2M1 elements stored N x (K/2) bytes
+ *   scale_A  M x (K/16) E4M3 bytes: scale_A[i][q] multiplies A[i][16q .. 16q+15]
+ *   scale_B  N x (K/16) E4M3 bytes; both 2-byte aligned
+ *   global_scale_A, global_scale_B  the per-tensor scales gA, gB
+ *   Out      M x N of `out_dtype` (TCM_F16, TCM_BF16 or TCM_F32), overwritten
+ * K must be a multiple of 32 (TCM_ERR_UNSUPPORTED_SHAPE).  Each element times
+ * its block scale is exact in fp16; the products are summed in fp32 and
+ * multiplied by the fp32 product gA gB before the one rounding to out_dtype.
+ */
+tcm_status tcm_gemm_nvfp4(const void* A, const void* B, const void* scale_A, const void* scale_B,
+                          float global_scale_A, float global_scale_B, void* Out, int64_t M,
+                          int64_t N, int64_t K, tcm_dtype out_dtype, void* stream);
+
 /* What a call with these arguments would launch (host only: no HIP call when
  * num_cus > 0; num_cus == 0 asks the current device for its CU count). */
 typedef struct tcm_plan {

@@ -55,7 +55,8 @@ class Plan(ctypes.Structure):
 _lock = threading.Lock()
 _lib = None
 EXPORTS = ("tcm_gemm", "tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
-           "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_plan_gemm", "tcm_status_string")
+           "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_gemm_nvfp4", "tcm_plan_gemm",
+           "tcm_status_string")
 
 
 def lib() -> ctypes.CDLL:
@@ -77,11 +78,12 @@ def lib() -> ctypes.CDLL:
             L.tcm_gemm_mx_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_gemm_mx_fp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_gemm_mx_fp6.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
+            L.tcm_gemm_nvfp4.argtypes = [vp, vp, vp, vp, cf, cf, vp, i64, i64, i64, ci, vp]
             L.tcm_plan_gemm.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(Plan)]
             L.tcm_status_string.argtypes = [ci]
             L.tcm_status_string.restype = ctypes.c_char_p
             for f in ("tcm_gemm", "tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
-                      "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_plan_gemm"):
+                      "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_gemm_nvfp4", "tcm_plan_gemm"):
                 getattr(L, f).restype = ci
             _lib = L
     return _lib
@@ -312,6 +314,37 @@ def gemm_mx_fp6(a, b, scale_a, scale_b, out=None, out_dtype=None, elem="e2m3"):
     with torch.cuda.device(a.device):
         _check(lib().tcm_gemm_mx_fp6(_ptr(a), _ptr(b), _ptr(scale_a), _ptr(scale_b), _ptr(out),
                                      M, N, K, code, _code(out.dtype), _stream(a)))
+    return out
+
+
+def gemm_nvfp4(a, b, scale_a, scale_b, global_a=1.0, global_b=1.0, out=None, out_dtype=None):
+    """NVFP4 Out = global_a global_b (a * scale_a) . (b * scale_b)^T.  a (M, K/2),
+    b (N, K/2) uint8 E2M1 pairs (element 2t in the low four bits of byte t);
+    scale_a (M, K/16), scale_b (N, K/16) E4M3 block scales (uint8 or
+    float8_e4m3fn); global_a, global_b the fp32 per-tensor scales."""
+    torch = _torch()
+    M, KH = a.shape
+    N = b.shape[0]
+    K = 2 * KH
+    if b.shape[1] != KH:
+        raise ValueError("K mismatch")
+    if K % 32 or tuple(scale_a.shape) != (M, K // 16) or tuple(scale_b.shape) != (N, K // 16):
+        raise ValueError("scale tensors must be (rows, K/16) with K a multiple of 32")
+    for t in (a, b):
+        if t.dtype != torch.uint8:
+            raise TypeError("NVFP4 elements must be uint8 pairs")
+    for t in (scale_a, scale_b):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError("NVFP4 scales must be uint8 or float8_e4m3fn")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be {(M, N)}")
+    codes = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+    with torch.cuda.device(a.device):
+        _check(lib().tcm_gemm_nvfp4(_ptr(a), _ptr(b), _ptr(scale_a), _ptr(scale_b),
+                                    float(global_a), float(global_b), _ptr(out), M, N, K,
+                                    codes[out.dtype], _stream(a)))
     return out
 
 

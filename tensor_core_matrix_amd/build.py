@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtcm.so")
 ARCH = "gfx950"
-SOURCES = ["tcm_api.cpp", "gemm_tn.hip", "gemm_mx.hip", "gemm_mx6.hip", "gemm_epi.hip",
+SOURCES = ["tcm_api.cpp", "gemm_tn.hip", "gemm_mx.hip", "gemm_mx6.hip", "gemm_nv4.hip", "gemm_epi.hip",
            "gemm_mn_a.hip", "gemm_mn_b.hip", "gemm_mn_ab.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -48,6 +48,7 @@ namespace tcm {
 // ---------------------------------------------------------------------------
 struct OpBF16 {
     static constexpr int kElemBytes = 2;
+    static constexpr bool kNV4 = false;
     static constexpr int kElemBits = 16;
     static constexpr int kK = 16;  // K per MFMA
     static constexpr bool kScaled = false;
@@ -59,6 +60,7 @@ struct OpBF16 {
 
 struct OpF16 {
     static constexpr int kElemBytes = 2;
+    static constexpr bool kNV4 = false;
     static constexpr int kElemBits = 16;
     static constexpr int kK = 16;
     static constexpr bool kScaled = false;
@@ -75,6 +77,7 @@ struct OpF16 {
 // 32-bit scale register.
 struct OpMXFP8 {
     static constexpr int kElemBytes = 1;
+    static constexpr bool kNV4 = false;
     static constexpr int kElemBits = 8;
     static constexpr int kK = 64;
     static constexpr bool kScaled = true;
@@ -95,6 +98,7 @@ struct OpMXFP8 {
 // took scale 1, every nibble of lanes 32..63 scale 2.
 struct OpMXFP4 {
     static constexpr int kElemBytes = 0;  // two elements per byte
+    static constexpr bool kNV4 = false;
     static constexpr int kElemBits = 4;
     static constexpr int kK = 64;
     static constexpr bool kScaled = true;
@@ -118,6 +122,7 @@ struct OpMXFP4 {
 template <int FMT>
 struct OpMXFP6 {
     static constexpr int kElemBytes = 0;
+    static constexpr bool kNV4 = false;
     static constexpr int kElemBits = 6;
     static constexpr int kK = 64;
     static constexpr bool kScaled = true;
@@ -125,6 +130,23 @@ struct OpMXFP6 {
     template <int SEL>
     __device__ static __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c, int sa, int sb) {
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, SEL, sa, SEL, sb);
+    }
+};
+
+// NVFP4 (E2M1 with an E4M3 scale per 16 and an fp32 scale per tensor).  No
+// matrix-core form takes E4M3 block scales, but an E2M1 value times an E4M3
+// scale is exact in fp16 (at most 5 significant bits, magnitudes 2^-10 ..
+// 2688): the copies dequantize into the fp16 LDS tile and the product runs on
+// the fp16 MFMA; the tensor scales enter as the epilogue's alpha.
+struct OpNVFP4 {
+    static constexpr int kElemBytes = 2;  // of the LDS tile (fp16)
+    static constexpr int kElemBits = 16;
+    static constexpr bool kNV4 = true;
+    static constexpr int kK = 16;
+    static constexpr bool kScaled = false;
+    typedef f16x8_t frag_t;
+    __device__ static __forceinline__ f32x16_t mma(frag_t a, frag_t b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
 };
 
@@ -154,8 +176,11 @@ void tiled_gemm_kernel(GemmArgs p) {
     constexpr int A_BYTES = BM * RB;
     constexpr int B_BYTES = BN * RB;
     constexpr int STAGE = A_BYTES + B_BYTES;
-    constexpr int A_LOADS = A_BYTES / (kThreads * 16);  // copies per thread per slice
-    constexpr int B_LOADS = B_BYTES / (kThreads * 16);
+    // NVFP4: a copy ("task") is half a row's slice, 32 elements: task t of
+    // thread tid is row (tid + 256 t) % R, half (tid + 256 t) / R of A or B
+    constexpr bool NV4 = Op::kNV4;
+    constexpr int A_LOADS = NV4 ? 2 * BM / kThreads : A_BYTES / (kThreads * 16);  // copies per thread per slice
+    constexpr int B_LOADS = NV4 ? 2 * BN / kThreads : B_BYTES / (kThreads * 16);
     constexpr int ROWS_PER_WAVE_COPY = kWaveSize * 16 / RB;
     constexpr int WTM = BM / 2, WTN = BN / 2;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -177,6 +202,8 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert((32 >> SWZ) % CPR == 0, "swizzle must depend on the row within 32 only");
     static_assert(!Op::kScaled || (BK == 128 && S == 2), "MX path: 128-deep slices, 2 stages");
     static_assert(!VG || (!Op::kScaled && S == 2), "register-staged copies: plain types, 2 stages");
+    static_assert(!NV4 || (VG && BK == 64 && (2 * BM) % kThreads == 0 && (2 * BN) % kThreads == 0),
+                  "NVFP4: register-staged copies of 64-deep slices, whole tasks per thread");
     static_assert(Op::kElemBits >= 8, "whole-byte elements");
     constexpr bool ANY_MN = A_MN || B_MN;
     static_assert(!ANY_MN || (ESZ == 2 && !Op::kScaled && !VG), "M/N-major: 16-bit, DMA copies");
@@ -261,6 +288,7 @@ void tiled_gemm_kernel(GemmArgs p) {
     // with an M/N-major operand, at every slice).
     TileCursor fc = {0, 0, 0, 0, 0};
     __amdgpu_buffer_rsrc_t ra, rb;
+    __amdgpu_buffer_rsrc_t rsa, rsb;  // NVFP4 block scales
     // K-major: the tile's rows r0 .. r0 + rows - 1; rows past the tile's last
     // (r >= rows) start at or beyond the bound.
     auto kmajor_rsrc = [&](const char* base, int r0, int R, int BR, int ld) {
@@ -280,6 +308,17 @@ void tiled_gemm_kernel(GemmArgs p) {
     auto feed_resources = [&]() {
         const char* abase = (const char*)p.A + fc.batch * p.stride_a;
         const char* bbase = (const char*)p.B + fc.batch * p.stride_b;
+        if constexpr (NV4) {
+            // rows of K/2 bytes of E2M1 pairs and of K/16 E4M3 scales
+            const int rows_a = min(BM, p.M - fc.tm * BM), rows_b = min(BN, p.N - fc.tn * BN);
+            ra = make_rsrc(abase + (int64_t)fc.tm * BM * (K / 2), (uint32_t)rows_a * (K / 2));
+            rb = make_rsrc(bbase + (int64_t)fc.tn * BN * (K / 2), (uint32_t)rows_b * (K / 2));
+            rsa = make_rsrc((const char*)p.SA + (int64_t)fc.tm * BM * (K / 16),
+                            (uint32_t)rows_a * (K / 16));
+            rsb = make_rsrc((const char*)p.SB + (int64_t)fc.tn * BN * (K / 16),
+                            (uint32_t)rows_b * (K / 16));
+            return;
+        }
         if constexpr (A_MN)
             ra = mn_rsrc(abase, fc.tm * BM, p.M, BM, lda, fc.kk * BK);
         else
@@ -308,7 +347,12 @@ void tiled_gemm_kernel(GemmArgs p) {
     // that is never read again.  (An M/N-major slice's resource starts at
     // its own first k row, so its offsets do not move with k.)
     uint32_t foff_a0, foff_b0;
+    int nv_k0 = -1;  // NVFP4: first K element of the stream's slice, -1 past the last one
     auto feed_offsets = [&](bool live) {
+        if constexpr (NV4) {
+            nv_k0 = live ? fc.kk * BK : -1;
+            return;
+        }
         const uint32_t k0b = (uint32_t)(fc.kk * BK) * ESZ;
         const bool kin = fc.kk * BK + cp_k < K;
         foff_a0 = A_MN ? (live ? geo_a.off : kOutOfRange)
@@ -486,19 +530,67 @@ void tiled_gemm_kernel(GemmArgs p) {
     // slice whose loads refill stg.  Lane l of copy x writes the same LDS
     // bytes as the DMA form would.
     i32x4_t stg[VG ? LOADS : 1];
+    int stsc[NV4 ? LOADS : 1];  // NVFP4: the two E4M3 scales of a task
+    auto nv_task = [&](int x, int& r, int& h) {
+        const int R = x < A_LOADS ? BM : BN;
+        const int tau = tid + kThreads * (x < A_LOADS ? x : x - A_LOADS);
+        r = tau % R;
+        h = tau / R;
+    };
     auto load_one = [&](int x) {
-        if constexpr (VG) {
+        if constexpr (NV4) {
+            int r, h;
+            nv_task(x, r, h);
+            const bool ok = nv_k0 >= 0 && nv_k0 + 32 * h < K;
+            const uint32_t off = ok ? (uint32_t)r * (K / 2) + nv_k0 / 2 + 16 * h : kOutOfRange;
+            const uint32_t soff = ok ? (uint32_t)r * (K / 16) + nv_k0 / 16 + 2 * h : kOutOfRange;
+            stg[x] = __builtin_bit_cast(
+                i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x < A_LOADS ? ra : rb, off, 0, 0));
+            stsc[x] = (int)__builtin_amdgcn_raw_buffer_load_b16(x < A_LOADS ? rsa : rsb, soff, 0, 0);
+        } else if constexpr (VG) {
             const __amdgpu_buffer_rsrc_t r = x < A_LOADS ? ra : rb;
             const uint32_t off = x < A_LOADS ? foff_a(x) : foff_b(x - A_LOADS);
             stg[x] = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
         }
     };
-    auto copy_one = [&](int st, int x) {
+    // Register-staged copy x into stage st.  NVFP4: dword j of the 16 bytes
+    // holds elements 8j .. 8j+7 of the half (element 2i in the low nibble of
+    // byte i); each byte converts to two fp16 values (v_cvt_scalef32_pk_f16_fp4
+    // with scale 1; its scale operand takes only a power of two) and is
+    // multiplied by its block's scale in fp16, exactly: logical fp16 chunk
+    // 4 h + j of row r.
+    auto write_one = [&](int st, int x) {
         char* sa = lds + st * STAGE;
-        if constexpr (VG) {
+        if constexpr (NV4) {
+            int r, h;
+            nv_task(x, r, h);
+            char* row = sa + (x < A_LOADS ? 0 : A_BYTES) + r * RB;
+            const int xs = (r >> SWZ) & (CPR - 1);
+            const uint32_t sc = (uint32_t)stsc[x];
+            const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sc, 0);
+            const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sc, 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t w = (uint32_t)stg[x][j];
+                const f16x2_t s = j < 2 ? (f16x2_t){s0, s0} : (f16x2_t){s1, s1};
+                const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+                const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+                const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+                const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+                const i32x4_t chunk = {__builtin_bit_cast(int, v0), __builtin_bit_cast(int, v1),
+                                       __builtin_bit_cast(int, v2), __builtin_bit_cast(int, v3)};
+                *(i32x4_t*)(row + ((4 * h + j) ^ xs) * 16) = chunk;
+            }
+        } else {
             char* dst = x < A_LOADS ? sa + (4 * x + wave) * 1024
                                     : sa + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024;
             *(i32x4_t*)(dst + lane * 16) = stg[x];
+        }
+    };
+    auto copy_one = [&](int st, int x) {
+        char* sa = lds + st * STAGE;
+        if constexpr (VG) {
+            write_one(st, x);
             load_one(x);
         } else if (x < A_LOADS) {
             dma(ra, sa + (4 * x + wave) * 1024, foff_a(x));
@@ -816,13 +908,8 @@ void tiled_gemm_kernel(GemmArgs p) {
         // stream moved on to slice 2, and part 0 of slice 1 written
 #pragma unroll
         for (int x = 0; x < LOADS; ++x) load_one(x);
-        char* s0 = lds;
 #pragma unroll
-        for (int x = 0; x < LOADS; ++x) {
-            char* dst = x < A_LOADS ? s0 + (4 * x + wave) * 1024
-                                    : s0 + A_BYTES + (4 * (x - A_LOADS) + wave) * 1024;
-            *(i32x4_t*)(dst + lane * 16) = stg[x];
-        }
+        for (int x = 0; x < LOADS; ++x) write_one(0, x);
         feed_advance();
         feed_offsets(1 < total);
 #pragma unroll

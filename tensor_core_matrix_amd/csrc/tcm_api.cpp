@@ -39,6 +39,9 @@ VariantInfo variant_info(int32_t v) {
     case V_MXPP256_K64S4_CM: return {256, 256, 64, 4, 1, 8, 512};
     case V_MX4PP256: return {256, 256, 128, 4, 1, 4, 512};
     case V_MX6PP256: return {256, 256, 64, 4, 1, 6, 512};
+    // NVFP4: the LDS tiles hold fp16
+    case V_NV4_256: return {256, 256, 64, 2, 1, 16, kThreads};
+    case V_NV4_128: return {128, 128, 64, 2, 2, 16, kThreads};
     }
     return {0, 0, 0, 0, 0, 0, kThreads};
 }
@@ -144,7 +147,9 @@ int64_t max_grid() {
 // Families by element bits: 16 (f16/bf16), 8 (MXFP8), 6 (MXFP6), 4 (MXFP4).
 int32_t choose_variant(int64_t batch, int64_t M, int64_t N, int32_t bits, int cus) {
     const int32_t f = forced_variant();
-    if (f >= 0 && variant_info(f).tile_m > 0 && variant_info(f).elem_bits == bits) return f;
+    if (f >= 0 && variant_info(f).tile_m > 0 && variant_info(f).elem_bits == bits &&
+        f != V_NV4_256 && f != V_NV4_128)
+        return f;
     static const int32_t plain[] = {V_T256x256_SPLIT3, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MXPP256_K64S4, V_MX128x128};
     static const int32_t mx4[] = {V_MX4PP256};
@@ -330,6 +335,53 @@ tcm_status tcm_gemm_mx_fp4(const void* A, const void* B, const void* scale_A, co
                            void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype out_dtype,
                            void* stream) {
     return run_mx(4, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream);
+}
+
+tcm_status tcm_gemm_nvfp4(const void* A, const void* B, const void* scale_A, const void* scale_B,
+                          float global_scale_A, float global_scale_B, void* Out, int64_t M,
+                          int64_t N, int64_t K, tcm_dtype out_dtype, void* stream) {
+    if (!(out_dtype == TCM_F16 || out_dtype == TCM_BF16 || out_dtype == TCM_F32))
+        return TCM_ERR_UNSUPPORTED_DTYPE;
+    bool empty = false;
+    tcm_status s = check_sizes(1, M, N, K, &empty);
+    if (s != TCM_OK || empty) return s;
+    if (!Out || (K > 0 && (!A || !B || !scale_A || !scale_B))) return TCM_ERR_NULL_POINTER;
+    if ((s = check_range(1, M, N, K)) != TCM_OK) return s;
+    if (K % 32 != 0) return TCM_ERR_UNSUPPORTED_SHAPE;
+    // rows of K/2 bytes (whole 16-byte pieces); scales read two at a time
+    auto aligned2 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; };
+    if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) ||
+        (scale_A && !aligned2(scale_A)) || (scale_B && !aligned2(scale_B)))
+        return TCM_ERR_MISALIGNED;
+    DeviceInfo dev;
+    if ((s = device_info(&dev)) != TCM_OK) return s;
+    // the 256 x 256 tile where it fills the CUs with little padding
+    int32_t v = V_NV4_128;
+    const int32_t f = forced_variant();
+    if (f == V_NV4_256 || f == V_NV4_128) {
+        v = f;
+    } else {
+        const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
+        const double fill = double(M) * N / (double(tiles) * 256 * 256);
+        if (tiles >= dev.cus && fill >= 0.9) v = V_NV4_256;
+    }
+    tcm_plan plan;
+    GemmArgs a;
+    plan_variant(v, 1, M, N, K, dev.cus, &plan, &a);
+    a.A = A;
+    a.B = B;
+    a.SA = scale_A;
+    a.SB = scale_B;
+    a.C = Out;
+    a.stride_a = M * K / 2;
+    a.stride_b = N * K / 2;
+    a.stride_c = M * N * elem_bytes(out_dtype);
+    a.alpha = global_scale_A * global_scale_B;
+    a.beta = 0.0f;
+    a.c_dtype = (int32_t)TCM_F32;
+    a.op = TCM_OP_IDENTITY;
+    hipError_t e = launch_gemm_nv4(v, (int32_t)out_dtype, a, plan.grid, (hipStream_t)stream);
+    return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
 }
 
 tcm_status tcm_gemm_mx_fp6(const void* A, const void* B, const void* scale_A, const void* scale_B,

@@ -61,6 +61,8 @@ enum Variant : int32_t {
     V_T256x256_SPLIT3 = 19, // 256x256x64, 2-stage ring, copies split over 3 K steps (5/5/6)
     V_MX4PP256 = 20,        // MXFP4 256x256x128 ping-pong, 4-stage ring
     V_MX6PP256 = 21,        // MXFP6 256x256x64 ping-pong, 4-stage ring, grouped row layout
+    V_NV4_256 = 22,         // NVFP4 256x256x64, dequantizing register-staged copies, fp16 MFMA
+    V_NV4_128 = 23,         // NVFP4 128x128x64, the same
     V_MX256x256 = 10, // MXFP8 256x256x128, 2-stage ring
     V_MX128x128 = 11, // MXFP8 128x128x128, 2-stage ring
     V_MX256x256_SPLIT2 = 12, // MXFP8 256x256x128, copies split over 2 K steps
@@ -92,6 +94,10 @@ hipError_t launch_gemm_mn(int32_t variant, int32_t in_dtype, int32_t out_dtype, 
                           int grid, hipStream_t stream);
 hipError_t launch_gemm_mx(int32_t variant, int32_t out_dtype, int32_t scale_mode, const GemmArgs& a,
                           int grid, hipStream_t stream);
+// NVFP4 (variants V_NV4_*): GemmArgs.SA/SB hold the E4M3 block scales and
+// alpha the product of the two tensor scales.
+hipError_t launch_gemm_nv4(int32_t variant, int32_t out_dtype, const GemmArgs& a, int grid,
+                           hipStream_t stream);
 // MXFP6; elem_dtype is the tcm_dtype of both operands' elements (E2M3 or E3M2).
 hipError_t launch_gemm_mx6(int32_t variant, int32_t out_dtype, int32_t scale_mode,
                            int32_t elem_dtype, const GemmArgs& a, int grid, hipStream_t stream);

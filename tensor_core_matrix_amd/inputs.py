@@ -24,6 +24,9 @@ problems):
 * ``mxfp6_8192`` -- the same with FP6 E2M3 elements (MXFP6, the table's 6-bit
   rows): every 6-bit code equally likely, packed four per three bytes, seed
   7, bf16 output.
+* ``nvfp4_8192`` -- A, B 8192x8192 E2M1 codes (every code equally likely),
+  one E4M3 scale per 16 (exponent uniform on -4..4, every mantissa), tensor
+  scales 0.5 and 1.25, seed 8, bf16 output (the format table's NVFP4 row).
 * ``bf16_8192_nn`` -- A 8192x8192 and B 8192x8192 bfloat16, both row-major
   (B stored K x N, its N index contiguous: the product A . B of two
   row-major matrices), N(0,1)*0.05, seed 6, bf16 output ("API Card:
@@ -53,6 +56,7 @@ class Workload:
     sigma: float = 1.0
     scale_exp: tuple = field(default=(-4, 4))
     b_order: str = "col"  # "col": B stored N x K (the TN form); "row": stored K x N
+    globals: tuple = field(default=(1.0, 1.0))  # NVFP4 per-tensor scales gA, gB
 
     @property
     def flops(self) -> int:
@@ -67,6 +71,8 @@ WORKLOADS = {
     "mxfp8_8192": Workload("mxfp8_8192", 1, 8192, 8192, 8192, "e4m3", "bf16", 4, "normal", 1.0),
     "mxfp4_8192": Workload("mxfp4_8192", 1, 8192, 8192, 8192, "e2m1", "bf16", 5, "codes"),
     "mxfp6_8192": Workload("mxfp6_8192", 1, 8192, 8192, 8192, "e2m3", "bf16", 7, "codes"),
+    "nvfp4_8192": Workload("nvfp4_8192", 1, 8192, 8192, 8192, "nvfp4", "bf16", 8, "codes",
+                           globals=(0.5, 1.25)),
     "bf16_8192_nn": Workload("bf16_8192_nn", 1, 8192, 8192, 8192, "bf16", "bf16", 6, "normal", 0.05,
                              b_order="row"),
 }
@@ -148,6 +154,11 @@ def make(w: Workload | str) -> dict:
     lead = (w.batch,) if w.batch > 1 else ()
     shp_a = lead + (w.M, w.K)
     shp_b = lead + ((w.K, w.N) if w.b_order == "row" else (w.N, w.K))
+    if w.dtype == "nvfp4":
+        a, b = e2m1_codes(w.M, w.K, g), e2m1_codes(w.N, w.K, g)
+        lo, hi = w.scale_exp
+        return {"A": a, "B": b, "SA": e4m3_scales((w.M, w.K // 16), g, lo, hi),
+                "SB": e4m3_scales((w.N, w.K // 16), g, lo, hi)}
     if w.dtype in ("e4m3", "e2m1", "e2m3", "e3m2"):
         if w.dtype == "e4m3":
             a = e4m3_normal(shp_a, g, w.sigma)

@@ -108,6 +108,20 @@ def test_mxfp6_entry_validation():
         (256, 64, 24 * 1024, 4, 512)
 
 
+def test_nvfp4_entry_validation():
+    L = tcm.lib()
+    f = lambda K=64, odt=tcm.BF16, a=A, sa=SA: L.tcm_gemm_nvfp4(a, B, sa, SB, 0.5, 2.0, C, 64, 64,
+                                                                K, odt, None)
+    assert f() in (OK, NO_DEVICE)
+    assert f(odt=tcm.F16) in (OK, NO_DEVICE)
+    assert f(odt=tcm.E4M3) == UNSUP_DTYPE
+    assert f(K=48) == UNSUP_SHAPE
+    assert f(a=A + 8) == MISALIGNED
+    assert f(sa=SA + 1) == MISALIGNED       # scales are read two at a time
+    assert f(sa=SA + 2) in (OK, NO_DEVICE)
+    assert f(a=None) == NULLP
+
+
 def test_valid_call_without_gpu_reports_no_device():
     try:
         import torch

@@ -1,0 +1,122 @@
+"""Parity of the NVFP4 path (E2M1 elements, an E4M3 scale per 16, an fp32
+scale per tensor) with the fp64 oracle, through the C ABI.  The elements
+times their block scales are exact in fp16 and the fp16 products exact in
+fp32, so the error is the fp32 sum's (1e-4 sum|a b|), the fp32 rounding of
+gA gB and of the final multiply (2^-22 |x|), and one ulp of a bf16 / fp16
+output (oracle.check_epi with alpha 1 and the tensor scales inside the
+oracle's sums).  Unit block and tensor scales make everything exact: those
+fp32 outputs must match bit for bit."""
+import contextlib
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import tensor_core_matrix_amd as tcm
+from oracle import oracle as orc
+from tensor_core_matrix_amd import inputs as inp
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+OUT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+GUARD = 256
+
+
+@contextlib.contextmanager
+def env(**kv):
+    old = {k: os.environ.get(k) for k in kv}
+    os.environ.update({k: str(v) for k, v in kv.items()})
+    try:
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def make(M, N, K, seed):
+    g = inp.generator(seed)
+    return (inp.e2m1_codes(M, K, g), inp.e2m1_codes(N, K, g),
+            inp.e4m3_scales((M, K // 16), g), inp.e4m3_scales((N, K // 16), g))
+
+
+def run(a, b, sa, sb, ga, gb, odt):
+    n = a.shape[0] * b.shape[0]
+    buf = torch.full((n + 2 * GUARD,), float("nan"), dtype=OUT[odt], device=DEV)
+    out = buf[GUARD:GUARD + n].view(a.shape[0], b.shape[0])
+    tcm.gemm_nvfp4(a.to(DEV), b.to(DEV), sa.to(DEV), sb.to(DEV), ga, gb, out)
+    torch.cuda.synchronize()
+    canary = torch.cat([buf[:GUARD], buf[-GUARD:]]).float()
+    assert bool(torch.isnan(canary).all()), "write outside the output"
+    return out.cpu()
+
+
+def check(gpu, ref, s, odt, what):
+    ok, worst, nbad = orc.check_epi(gpu.double().numpy(), ref, 1.0, s, np.zeros_like(ref), odt)
+    assert ok, f"{what}: {nbad} violations, worst err/bound {worst:.3g}"
+
+
+@pytest.mark.parametrize("K", [640, 608, 1024])
+@pytest.mark.parametrize("odt", ["f32", "bf16", "f16"])
+def test_nvfp4_ragged(K, odt):
+    M, N = 700, 520
+    a, b, sa, sb = make(M, N, K, 1200 + K)
+    # tensor scales that keep the results inside the fp16 range (65504)
+    ga, gb = (0.3, -1.7) if odt != "f16" else (0.03, -0.17)
+    ref, s = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), ga, gb)
+    check(run(a, b, sa, sb, ga, gb, odt), ref, s, odt, f"nvfp4 K {K} {odt}")
+
+
+@pytest.mark.parametrize("variant", [22, 23])
+def test_nvfp4_each_tile_with_persistent_grid(variant):
+    M, N, K = 777, 645, 352
+    a, b, sa, sb = make(M, N, K, 1210 + variant)
+    ref, s = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), 2.0, 0.75)
+    with env(TCM_FORCE_VARIANT=variant, TCM_MAX_GRID=3):
+        got = run(a, b, sa, sb, 2.0, 0.75, "bf16")
+    check(got, ref, s, "bf16", f"variant {variant}")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (33, 17, 64), (256, 256, 128), (300, 260, 1024)])
+def test_nvfp4_unit_scales_exact(shape):
+    M, N, K = shape
+    a, b, _, _ = make(M, N, K, 1220 + K)
+    one = 0x38  # E4M3 1.0
+    sa = torch.full((M, K // 16), one, dtype=torch.uint8)
+    sb = torch.full((N, K // 16), one, dtype=torch.uint8)
+    ref, _ = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), 1.0, 1.0)
+    got = run(a, b, sa, sb, 1.0, 1.0, "f32").double().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_nvfp4_block_scale_reaches_only_its_16():
+    """Changing one 16-element scale of A changes exactly row 5's outputs, and
+    those as the oracle says (positions in K pinned by the oracle)."""
+    M, N, K = 64, 48, 256
+    a, b, _, _ = make(M, N, K, 1230)
+    sa = torch.full((M, K // 16), 0x38, dtype=torch.uint8)
+    sb = torch.full((N, K // 16), 0x38, dtype=torch.uint8)
+    base = run(a, b, sa, sb, 1.0, 1.0, "f32").double().numpy()
+    sa2 = sa.clone()
+    sa2[5, 7] = 0x4C  # E4M3 3.5
+    got = run(a, b, sa2, sb, 1.0, 1.0, "f32").double().numpy()
+    ref, _ = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa2), inp.raw(sb), 1.0, 1.0)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.delete(got, 5, 0), np.delete(base, 5, 0))
+
+
+def test_workload_nvfp4():
+    w = inp.WORKLOADS["nvfp4_8192"]
+    x = inp.make(w)
+    ga, gb = w.globals
+    out = run(x["A"], x["B"], x["SA"], x["SB"], ga, gb, "bf16")
+    rng = np.random.default_rng(w.seed)
+    ii = np.concatenate([rng.integers(0, w.M, 4096), [0, w.M - 1, 0, w.M - 1]])
+    jj = np.concatenate([rng.integers(0, w.N, 4096), [0, 0, w.N - 1, w.N - 1]])
+    ref, s = orc.entries_nvfp4(inp.raw(x["A"]), inp.raw(x["B"]), inp.raw(x["SA"]),
+                               inp.raw(x["SB"]), ga, gb, ii, jj)
+    check(out[torch.from_numpy(ii), torch.from_numpy(jj)], ref, s, "bf16", "nvfp4 8192")
