@@ -137,8 +137,12 @@ struct OpMXFP6 {
 // matrix-core form takes E4M3 block scales, but an E2M1 value times an E4M3
 // scale is exact in fp16 (at most 5 significant bits, magnitudes 2^-10 ..
 // 2688): the copies dequantize into the fp16 LDS tile and the product runs on
-// the fp16 MFMA; the tensor scales enter as the epilogue's alpha.
+// the fp16 MFMA; the tensor scales enter as the epilogue's alpha.  WIDE: a
+// row's scales of four slices come in one 16-byte load (K a multiple of 256,
+// scale rows 16-byte aligned); otherwise two bytes per half row and slice.
+template <bool WIDE>
 struct OpNVFP4 {
+    static constexpr bool kWide = WIDE;
     static constexpr int kElemBytes = 2;  // of the LDS tile (fp16)
     static constexpr int kElemBits = 16;
     static constexpr bool kNV4 = true;
@@ -149,6 +153,14 @@ struct OpNVFP4 {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
 };
+
+template <class Op>
+constexpr bool nv4_wide() {
+    if constexpr (Op::kNV4)
+        return Op::kWide;
+    else
+        return false;
+}
 
 struct TileCursor {
     int tl, kk, batch, tm, tn;
@@ -176,17 +188,18 @@ void tiled_gemm_kernel(GemmArgs p) {
     constexpr int A_BYTES = BM * RB;
     constexpr int B_BYTES = BN * RB;
     constexpr int STAGE = A_BYTES + B_BYTES;
-    // NVFP4: a copy ("task") is half a row's slice, 32 elements: task t of
-    // thread tid is row (tid + 256 t) % R, half (tid + 256 t) / R of A or B
+    // NVFP4: a copy ("task") is one row's 64-element slice: task x of thread
+    // tid is row tid + 256 x of the A tile stacked on the B tile.  A wave's
+    // 64 rows lie in one operand, so the operand choice is wave-uniform.
     constexpr bool NV4 = Op::kNV4;
-    constexpr int A_LOADS = NV4 ? 2 * BM / kThreads : A_BYTES / (kThreads * 16);  // copies per thread per slice
-    constexpr int B_LOADS = NV4 ? 2 * BN / kThreads : B_BYTES / (kThreads * 16);
+    constexpr int A_LOADS = NV4 ? 0 : A_BYTES / (kThreads * 16);  // DMA copies per thread per slice
+    constexpr int B_LOADS = NV4 ? 0 : B_BYTES / (kThreads * 16);
     constexpr int ROWS_PER_WAVE_COPY = kWaveSize * 16 / RB;
     constexpr int WTM = BM / 2, WTN = BN / 2;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int KSTEPS = BK / Op::kK;
     constexpr int CPL = Op::kK * ESZ / 32;  // 16-byte chunks per lane per MFMA
-    constexpr int LOADS = A_LOADS + B_LOADS;
+    constexpr int LOADS = NV4 ? (BM + BN) / kThreads : A_LOADS + B_LOADS;
     static_assert(KSTEPS % 2 == 0, "fragment double buffer alternates per K step");
     static_assert(((4 * ROWS_PER_WAVE_COPY) >> SWZ) % CPR == 0, "copy chunk independent of i");
     static_assert((S - 1) * LOADS < 64, "vmcnt range");
@@ -202,8 +215,8 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert((32 >> SWZ) % CPR == 0, "swizzle must depend on the row within 32 only");
     static_assert(!Op::kScaled || (BK == 128 && S == 2), "MX path: 128-deep slices, 2 stages");
     static_assert(!VG || (!Op::kScaled && S == 2), "register-staged copies: plain types, 2 stages");
-    static_assert(!NV4 || (VG && BK == 64 && (2 * BM) % kThreads == 0 && (2 * BN) % kThreads == 0),
-                  "NVFP4: register-staged copies of 64-deep slices, whole tasks per thread");
+    static_assert(!NV4 || (VG && BK == 64 && BM % kWaveSize == 0 && (BM + BN) % kThreads == 0),
+                  "NVFP4: register-staged copies of 64-deep slices, whole rows per thread");
     static_assert(Op::kElemBits >= 8, "whole-byte elements");
     constexpr bool ANY_MN = A_MN || B_MN;
     static_assert(!ANY_MN || (ESZ == 2 && !Op::kScaled && !VG), "M/N-major: 16-bit, DMA copies");
@@ -529,57 +542,105 @@ void tiled_gemm_kernel(GemmArgs p) {
     // (the copy stream's slice fg); `fc`/`foff` run one slice ahead, on the
     // slice whose loads refill stg.  Lane l of copy x writes the same LDS
     // bytes as the DMA form would.
-    i32x4_t stg[VG ? LOADS : 1];
-    int stsc[NV4 ? LOADS : 1];  // NVFP4: the two E4M3 scales of a task
-    auto nv_task = [&](int x, int& r, int& h) {
-        const int R = x < A_LOADS ? BM : BN;
-        const int tau = tid + kThreads * (x < A_LOADS ? x : x - A_LOADS);
-        r = tau % R;
-        h = tau / R;
+    // NVFP4: stg[2x + h] holds half h (32 elements) of task x's row, and the
+    // scales stay in their loaded form up to their use (a widening or a
+    // merge right after the load would wait for it): two bytes per half, or
+    // (WIDE) the 16 bytes of four slices with stq[x] = the slice's place in
+    // that group.
+    constexpr bool NV4W = nv4_wide<Op>();
+    i32x4_t stg[VG ? (NV4 ? 2 * LOADS : LOADS) : 1];
+    uint16_t stsc[NV4 && !NV4W ? 2 * LOADS : 1];
+    i32x4_t stsw[NV4W ? LOADS : 1];
+    int stq[NV4W ? LOADS : 1];
+    // Lane l takes row 16 (l / 16) + 2 (l % 8) + (l / 8) % 2 of its wave's 64:
+    // each 8-lane group of a 16-byte LDS write then holds 8 rows of one
+    // parity whose swizzles (r / 2) % 8 all differ, so the group's 128 bytes
+    // fall in distinct banks (consecutive rows would pair up on each bank).
+    const int nv_rho = 16 * (lane >> 4) + 2 * (lane & 7) + ((lane >> 3) & 1);
+    auto nv_task = [&](int x, bool& in_a, int& r) {
+        const int tw = kWaveSize * wave + kThreads * x;  // wave-uniform
+        in_a = tw < BM;
+        r = tw + nv_rho - (in_a ? 0 : BM);
     };
     auto load_one = [&](int x) {
         if constexpr (NV4) {
-            int r, h;
-            nv_task(x, r, h);
-            const bool ok = nv_k0 >= 0 && nv_k0 + 32 * h < K;
-            const uint32_t off = ok ? (uint32_t)r * (K / 2) + nv_k0 / 2 + 16 * h : kOutOfRange;
-            const uint32_t soff = ok ? (uint32_t)r * (K / 16) + nv_k0 / 16 + 2 * h : kOutOfRange;
-            stg[x] = __builtin_bit_cast(
-                i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x < A_LOADS ? ra : rb, off, 0, 0));
-            stsc[x] = (int)__builtin_amdgcn_raw_buffer_load_b16(x < A_LOADS ? rsa : rsb, soff, 0, 0);
+            bool in_a;
+            int r;
+            nv_task(x, in_a, r);
+            const uint32_t eoff = (uint32_t)r * (K / 2) + nv_k0 / 2;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = nv_k0 >= 0 && nv_k0 + 32 * h < K;
+                stg[2 * x + h] = __builtin_bit_cast(
+                    i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(in_a ? ra : rb,
+                                                                   ok ? eoff + 16 * h : kOutOfRange, 0, 0));
+            }
+            const uint32_t soff = (uint32_t)r * (K / 16) + nv_k0 / 16;
+            if constexpr (NV4W) {
+                // (nv_k0 = -1 past the last slice gives place 3: nothing loaded)
+                stq[x] = (nv_k0 >> 6) & 3;
+                if (stq[x] == 0)
+                    stsw[x] = __builtin_bit_cast(
+                        i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(in_a ? rsa : rsb, soff, 0, 0));
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const bool ok = nv_k0 >= 0 && nv_k0 + 32 * h < K;
+                    stsc[2 * x + h] = __builtin_amdgcn_raw_buffer_load_b16(
+                        in_a ? rsa : rsb, ok ? soff + 2 * h : kOutOfRange, 0, 0);
+                }
+            }
         } else if constexpr (VG) {
             const __amdgpu_buffer_rsrc_t r = x < A_LOADS ? ra : rb;
             const uint32_t off = x < A_LOADS ? foff_a(x) : foff_b(x - A_LOADS);
             stg[x] = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
         }
     };
-    // Register-staged copy x into stage st.  NVFP4: dword j of the 16 bytes
-    // holds elements 8j .. 8j+7 of the half (element 2i in the low nibble of
-    // byte i); each byte converts to two fp16 values (v_cvt_scalef32_pk_f16_fp4
+    // Register-staged copy x into stage st.  NVFP4: dword j of half h holds
+    // elements 8j .. 8j+7 of the half (element 2i in the low nibble of byte
+    // i); each byte converts to two fp16 values (v_cvt_scalef32_pk_f16_fp4
     // with scale 1; its scale operand takes only a power of two) and is
     // multiplied by its block's scale in fp16, exactly: logical fp16 chunk
-    // 4 h + j of row r.
+    // 4 h + j of row r.  The row's scale bytes of the slice: byte 2h + b
+    // scales elements 16b .. 16b+15 of half h.
     auto write_one = [&](int st, int x) {
         char* sa = lds + st * STAGE;
         if constexpr (NV4) {
-            int r, h;
-            nv_task(x, r, h);
-            char* row = sa + (x < A_LOADS ? 0 : A_BYTES) + r * RB;
+            bool in_a;
+            int r;
+            nv_task(x, in_a, r);
+            char* row = sa + (in_a ? 0 : A_BYTES) + r * RB;
             const int xs = (r >> SWZ) & (CPR - 1);
-            const uint32_t sc = (uint32_t)stsc[x];
-            const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sc, 0);
-            const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sc, 1);
+            uint32_t sw = 0;
+            if constexpr (NV4W) {
+                const int q = stq[x];
+                const i32x4_t v = stsw[x];
+                sw = (uint32_t)(q == 0 ? v[0] : q == 1 ? v[1] : q == 2 ? v[2] : v[3]);
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t w = (uint32_t)stg[x][j];
-                const f16x2_t s = j < 2 ? (f16x2_t){s0, s0} : (f16x2_t){s1, s1};
-                const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-                const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-                const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-                const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
-                const i32x4_t chunk = {__builtin_bit_cast(int, v0), __builtin_bit_cast(int, v1),
-                                       __builtin_bit_cast(int, v2), __builtin_bit_cast(int, v3)};
-                *(i32x4_t*)(row + ((4 * h + j) ^ xs) * 16) = chunk;
+            for (int h = 0; h < 2; ++h) {
+                _Float16 s0, s1;
+                if constexpr (NV4W) {
+                    s0 = (_Float16)(h == 0 ? __builtin_amdgcn_cvt_f32_fp8(sw, 0)
+                                           : __builtin_amdgcn_cvt_f32_fp8(sw, 2));
+                    s1 = (_Float16)(h == 0 ? __builtin_amdgcn_cvt_f32_fp8(sw, 1)
+                                           : __builtin_amdgcn_cvt_f32_fp8(sw, 3));
+                } else {
+                    s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((uint32_t)stsc[2 * x + h], 0);
+                    s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((uint32_t)stsc[2 * x + h], 1);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t w = (uint32_t)stg[2 * x + h][j];
+                    const f16x2_t s = j < 2 ? (f16x2_t){s0, s0} : (f16x2_t){s1, s1};
+                    const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+                    const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+                    const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+                    const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+                    const i32x4_t chunk = {__builtin_bit_cast(int, v0), __builtin_bit_cast(int, v1),
+                                           __builtin_bit_cast(int, v2), __builtin_bit_cast(int, v3)};
+                    *(i32x4_t*)(row + ((4 * h + j) ^ xs) * 16) = chunk;
+                }
             }
         } else {
             char* dst = x < A_LOADS ? sa + (4 * x + wave) * 1024

@@ -6,10 +6,10 @@
 
 namespace tcm {
 
-template <typename TOut, int BM, int BN, int OCC, int NSPLIT>
+template <typename TOut, int BM, int BN, int OCC, int NSPLIT, bool WIDE>
 static hipError_t launch_nv4(const GemmArgs& a, int grid, hipStream_t st) {
     // swizzle shift 1: 128-byte fp16 rows of 64-deep slices
-    hipLaunchKernelGGL((tiled_gemm_kernel<OpNVFP4, TOut, BM, BN, 64, 2, OCC, 1, false, NSPLIT, false,
+    hipLaunchKernelGGL((tiled_gemm_kernel<OpNVFP4<WIDE>, TOut, BM, BN, 64, 2, OCC, 1, false, NSPLIT, false,
                                           true, true, false, false, false>),
                        dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
@@ -18,8 +18,10 @@ static hipError_t launch_nv4(const GemmArgs& a, int grid, hipStream_t st) {
 template <typename TOut>
 static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t st) {
     switch (v) {
-    case V_NV4_256: return launch_nv4<TOut, 256, 256, 1, 2>(a, grid, st);
-    case V_NV4_128: return launch_nv4<TOut, 128, 128, 2, 1>(a, grid, st);
+    case V_NV4_256: return launch_nv4<TOut, 256, 256, 1, 2, false>(a, grid, st);
+    case V_NV4_128: return launch_nv4<TOut, 128, 128, 2, 1, false>(a, grid, st);
+    case V_NV4W_256: return launch_nv4<TOut, 256, 256, 1, 2, true>(a, grid, st);
+    case V_NV4W_128: return launch_nv4<TOut, 128, 128, 2, 1, true>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

@@ -42,6 +42,8 @@ VariantInfo variant_info(int32_t v) {
     // NVFP4: the LDS tiles hold fp16
     case V_NV4_256: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_NV4_128: return {128, 128, 64, 2, 2, 16, kThreads};
+    case V_NV4W_256: return {256, 256, 64, 2, 1, 16, kThreads};
+    case V_NV4W_128: return {128, 128, 64, 2, 2, 16, kThreads};
     }
     return {0, 0, 0, 0, 0, 0, kThreads};
 }
@@ -124,6 +126,10 @@ tcm_status check_range(int64_t batch, int64_t M, int64_t N, int64_t K) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool is_nv4_variant(int32_t v) {
+    return v == V_NV4_256 || v == V_NV4_128 || v == V_NV4W_256 || v == V_NV4W_128;
+}
+
 // TCM_FORCE_VARIANT=<id> (read at every call) forces a kernel variant of the
 // matching family, for tuning sweeps and per-variant tests; unset or invalid,
 // the heuristic below chooses.
@@ -148,7 +154,7 @@ int64_t max_grid() {
 int32_t choose_variant(int64_t batch, int64_t M, int64_t N, int32_t bits, int cus) {
     const int32_t f = forced_variant();
     if (f >= 0 && variant_info(f).tile_m > 0 && variant_info(f).elem_bits == bits &&
-        f != V_NV4_256 && f != V_NV4_128)
+        !is_nv4_variant(f))
         return f;
     static const int32_t plain[] = {V_T256x256_SPLIT3, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MXPP256_K64S4, V_MX128x128};
@@ -355,16 +361,17 @@ tcm_status tcm_gemm_nvfp4(const void* A, const void* B, const void* scale_A, con
         return TCM_ERR_MISALIGNED;
     DeviceInfo dev;
     if ((s = device_info(&dev)) != TCM_OK) return s;
-    // the 256 x 256 tile where it fills the CUs with little padding
-    int32_t v = V_NV4_128;
+    // the 256 x 256 tile where it fills the CUs with little padding; a row's
+    // scales of four slices in one 16-byte load where K and the scale
+    // tensors allow it
+    const bool wide = K % 256 == 0 && (!scale_A || aligned16(scale_A)) &&
+                      (!scale_B || aligned16(scale_B));
+    const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
+    const double fill = double(M) * N / (double(tiles) * 256 * 256);
+    const bool big = tiles >= dev.cus && fill >= 0.9;
+    int32_t v = wide ? (big ? V_NV4W_256 : V_NV4W_128) : (big ? V_NV4_256 : V_NV4_128);
     const int32_t f = forced_variant();
-    if (f == V_NV4_256 || f == V_NV4_128) {
-        v = f;
-    } else {
-        const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
-        const double fill = double(M) * N / (double(tiles) * 256 * 256);
-        if (tiles >= dev.cus && fill >= 0.9) v = V_NV4_256;
-    }
+    if (f == V_NV4_256 || f == V_NV4_128 || (wide && (f == V_NV4W_256 || f == V_NV4W_128))) v = f;
     tcm_plan plan;
     GemmArgs a;
     plan_variant(v, 1, M, N, K, dev.cus, &plan, &a);

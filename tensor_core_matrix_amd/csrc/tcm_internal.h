@@ -63,6 +63,8 @@ enum Variant : int32_t {
     V_MX6PP256 = 21,        // MXFP6 256x256x64 ping-pong, 4-stage ring, grouped row layout
     V_NV4_256 = 22,         // NVFP4 256x256x64, dequantizing register-staged copies, fp16 MFMA
     V_NV4_128 = 23,         // NVFP4 128x128x64, the same
+    V_NV4W_256 = 24,        // V_NV4_256 with a row's scales of four slices in one load
+    V_NV4W_128 = 25,        // V_NV4_128, the same
     V_MX256x256 = 10, // MXFP8 256x256x128, 2-stage ring
     V_MX128x128 = 11, // MXFP8 128x128x128, 2-stage ring
     V_MX256x256_SPLIT2 = 12, // MXFP8 256x256x128, copies split over 2 K steps

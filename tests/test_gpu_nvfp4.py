@@ -71,14 +71,40 @@ def test_nvfp4_ragged(K, odt):
     check(run(a, b, sa, sb, ga, gb, odt), ref, s, odt, f"nvfp4 K {K} {odt}")
 
 
-@pytest.mark.parametrize("variant", [22, 23])
-def test_nvfp4_each_tile_with_persistent_grid(variant):
-    M, N, K = 777, 645, 352
+# 22 / 23: 256 and 128 tiles with two scale bytes per half row and slice;
+# 24 / 25: the same tiles with a row's scales of four slices in one load
+# (K a multiple of 256: here three such groups per tile)
+@pytest.mark.parametrize("variant,K", [(22, 352), (23, 352), (22, 768), (23, 768), (24, 768),
+                                       (25, 768)])
+def test_nvfp4_each_tile_with_persistent_grid(variant, K):
+    M, N = 777, 645
     a, b, sa, sb = make(M, N, K, 1210 + variant)
     ref, s = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), 2.0, 0.75)
     with env(TCM_FORCE_VARIANT=variant, TCM_MAX_GRID=3):
         got = run(a, b, sa, sb, 2.0, 0.75, "bf16")
-    check(got, ref, s, "bf16", f"variant {variant}")
+    check(got, ref, s, "bf16", f"variant {variant} K {K}")
+
+
+@pytest.mark.parametrize("variant", [24, 25])
+def test_nvfp4_wide_form_declined(variant):
+    """A wide variant asked for where K is not a multiple of 256, or where a
+    scale tensor is only 2-byte aligned, runs the two-bytes-per-half form."""
+    M, N = 300, 260
+    for K, shift in [(352, 0), (512, 2)]:
+        a, b, sa, sb = make(M, N, K, 1240 + K)
+        ref, s = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), 1.5, 0.5)
+        # scale_B at a 2-byte offset inside a larger buffer
+        holder = torch.zeros(N * K // 16 + 16, dtype=torch.uint8, device=DEV)
+        sb_dev = holder[shift:shift + N * K // 16].view(N, K // 16)
+        sb_dev.copy_(sb.to(DEV))
+        n = M * N
+        buf = torch.full((n + 2 * GUARD,), float("nan"), dtype=torch.float32, device=DEV)
+        out = buf[GUARD:GUARD + n].view(M, N)
+        with env(TCM_FORCE_VARIANT=variant):
+            tcm.gemm_nvfp4(a.to(DEV), b.to(DEV), sa.to(DEV), sb_dev, 1.5, 0.5, out)
+        torch.cuda.synchronize()
+        assert bool(torch.isnan(torch.cat([buf[:GUARD], buf[-GUARD:]])).all())
+        check(out.cpu(), ref, s, "f32", f"variant {variant} K {K} scale offset {shift}")
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 32), (33, 17, 64), (256, 256, 128), (300, 260, 1024)])
