@@ -135,7 +135,7 @@ struct OpMXFP6 {
 
 // NVFP4 (E2M1 with an E4M3 scale per 16 and an fp32 scale per tensor).  No
 // matrix-core form takes E4M3 block scales, but an E2M1 value times an E4M3
-// scale is exact in fp16 (at most 5 significant bits, magnitudes 2^-10 ..
+// scale is exact in fp16 (at most 6 significant bits, magnitudes 2^-10 ..
 // 2688): the copies dequantize into the fp16 LDS tile and the product runs on
 // the fp16 MFMA; the tensor scales enter as the epilogue's alpha.  WIDE: a
 // row's scales of four slices come in one 16-byte load (K a multiple of 256,
