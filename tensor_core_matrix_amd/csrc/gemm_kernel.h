@@ -542,16 +542,23 @@ void tiled_gemm_kernel(GemmArgs p) {
     // (the copy stream's slice fg); `fc`/`foff` run one slice ahead, on the
     // slice whose loads refill stg.  Lane l of copy x writes the same LDS
     // bytes as the DMA form would.
-    // NVFP4: stg[2x + h] holds half h (32 elements) of task x's row, and the
-    // scales stay in their loaded form up to their use (a widening or a
-    // merge right after the load would wait for it): two bytes per half, or
-    // (WIDE) the 16 bytes of four slices with stq[x] = the slice's place in
-    // that group.
+    // NVFP4: stg[2x + h] holds half h (32 elements) of task x's row.  WIDE:
+    // stg[4x + 2p + h] holds half h of slice p of a pair of slices, all four
+    // loaded together at the pair's first slice (its 64 bytes are one fetch
+    // of the row's cache line instead of two), and stq[x] is the slice's
+    // place in its group of four.  The scales stay in their loaded form up
+    // to their use (a widening or a merge right after the load would wait
+    // for it): two bytes per half, or (WIDE) the 16 bytes of four slices.
     constexpr bool NV4W = nv4_wide<Op>();
-    i32x4_t stg[VG ? (NV4 ? 2 * LOADS : LOADS) : 1];
+    i32x4_t stg[VG ? (NV4 ? (NV4W ? 4 : 2) * LOADS : LOADS) : 1];
     uint16_t stsc[NV4 && !NV4W ? 2 * LOADS : 1];
     i32x4_t stsw[NV4W ? LOADS : 1];
     int stq[NV4W ? LOADS : 1];
+    // WIDE: parity of the slice the copies now being issued write (their
+    // loads fetch the next slice, so a pair is fetched when this is 1).  The
+    // slice loop sets it before each step that carries copies; unrolled by
+    // two, it is a constant there and the copies carry no branch.
+    int nv_wpar = 0;
     // Lane l takes row 16 (l / 16) + 2 (l % 8) + (l / 8) % 2 of its wave's 64:
     // each 8-lane group of a 16-byte LDS write then holds 8 rows of one
     // parity whose swizzles (r / 2) % 8 all differ, so the group's 128 bytes
@@ -568,21 +575,29 @@ void tiled_gemm_kernel(GemmArgs p) {
             int r;
             nv_task(x, in_a, r);
             const uint32_t eoff = (uint32_t)r * (K / 2) + nv_k0 / 2;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool ok = nv_k0 >= 0 && nv_k0 + 32 * h < K;
-                stg[2 * x + h] = __builtin_bit_cast(
-                    i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(in_a ? ra : rb,
-                                                                   ok ? eoff + 16 * h : kOutOfRange, 0, 0));
-            }
             const uint32_t soff = (uint32_t)r * (K / 16) + nv_k0 / 16;
             if constexpr (NV4W) {
-                // (nv_k0 = -1 past the last slice gives place 3: nothing loaded)
+                // K % 256 == 0: a pair of slices and a group of four are
+                // whole.  nv_k0 = -1 past the last slice gives place 3:
+                // nothing loaded.
                 stq[x] = (nv_k0 >> 6) & 3;
+                if (nv_wpar == 1) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        stg[4 * x + c] = __builtin_bit_cast(
+                            i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(in_a ? ra : rb, eoff + 16 * c, 0, 0));
+                }
                 if (stq[x] == 0)
                     stsw[x] = __builtin_bit_cast(
                         i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(in_a ? rsa : rsb, soff, 0, 0));
             } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const bool ok = nv_k0 >= 0 && nv_k0 + 32 * h < K;
+                    stg[2 * x + h] = __builtin_bit_cast(
+                        i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(in_a ? ra : rb,
+                                                                       ok ? eoff + 16 * h : kOutOfRange, 0, 0));
+                }
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const bool ok = nv_k0 >= 0 && nv_k0 + 32 * h < K;
@@ -629,9 +644,19 @@ void tiled_gemm_kernel(GemmArgs p) {
                     s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((uint32_t)stsc[2 * x + h], 0);
                     s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((uint32_t)stsc[2 * x + h], 1);
                 }
+                // (both candidates read as values first: a choice between two
+                // array elements would become a load from a chosen address,
+                // which keeps the array out of registers)
+                i32x4_t src;
+                if constexpr (NV4W) {
+                    const i32x4_t first = stg[4 * x + h], second = stg[4 * x + 2 + h];
+                    src = nv_wpar ? second : first;
+                } else {
+                    src = stg[2 * x + h];
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint32_t w = (uint32_t)stg[2 * x + h][j];
+                    const uint32_t w = (uint32_t)src[j];
                     const f16x2_t s = j < 2 ? (f16x2_t){s0, s0} : (f16x2_t){s1, s1};
                     const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
                     const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
@@ -967,17 +992,20 @@ void tiled_gemm_kernel(GemmArgs p) {
     if constexpr (VG) {
         // slice 0 straight into stage 0; slice 1 into registers, the load
         // stream moved on to slice 2, and part 0 of slice 1 written
+        nv_wpar = 1;  // (the loads of slice 0 start a pair)
 #pragma unroll
         for (int x = 0; x < LOADS; ++x) load_one(x);
+        nv_wpar = 0;
 #pragma unroll
         for (int x = 0; x < LOADS; ++x) write_one(0, x);
         feed_advance();
         feed_offsets(1 < total);
 #pragma unroll
-        for (int x = 0; x < LOADS; ++x) load_one(x);
+        for (int x = 0; x < LOADS; ++x) load_one(x);  // slice 1: nothing for WIDE (nv_wpar 0)
         feed_advance();
         fg = 1;
         feed_offsets(2 < total);
+        nv_wpar = 1;
 #pragma unroll
         for (int x = 0; x < PART; ++x) copy_one(1, x);
         if constexpr (NSPLIT == 1) feed_next();
@@ -1004,7 +1032,9 @@ void tiled_gemm_kernel(GemmArgs p) {
     // g + 1 are read while the last K step's MFMAs run.  ZERO marks a tile's
     // first slice, whose first MFMAs take a zero accumulator.
     bool after_epilogue = false;
-    auto slice = [&](int g, auto ZERO) {
+    // PAR: g's parity as a constant (0 or 1), or -1 where it is not fixed.
+    auto slice = [&](int g, auto ZERO, auto PAR) {
+        constexpr int par = decltype(PAR)::value;
         const char* st = lds + (g % S) * STAGE;
         const char* st_next = lds + ((g + 1) % S) * STAGE;
         if constexpr (Op::kScaled) {
@@ -1022,6 +1052,7 @@ void tiled_gemm_kernel(GemmArgs p) {
                 if (s + 1 < NSPLIT) {
                     // a later part of slice g - 1 + S, into stage (g - 1) % S
                     const int cst = (g + S - 1) % S;
+                    nv_wpar = par >= 0 ? (par + S - 1) & 1 : (g + S - 1) & 1;
                     if (zero)
                         kstep(cur, s, st, s + 1, cst, part_base(s + 1),
                               part_base(s + 2) - part_base(s + 1), std::true_type{});
@@ -1047,6 +1078,7 @@ void tiled_gemm_kernel(GemmArgs p) {
                 after_epilogue = false;
                 barrier_lds();
                 __builtin_amdgcn_sched_barrier(0);
+                nv_wpar = par >= 0 ? (par + S) & 1 : (g + S) & 1;  // part 0 of slice g + S
                 if (zero)
                     kstep(cur, s, st_next, 0, g % S, 0, PART, std::true_type{});
                 else
@@ -1057,8 +1089,30 @@ void tiled_gemm_kernel(GemmArgs p) {
     };
 
     int g = 0;
+    using P_ANY = std::integral_constant<int, -1>;
+    using P_EVEN = std::integral_constant<int, 0>;
+    using P_ODD = std::integral_constant<int, 1>;
     for (int tl = 0; tl < my_tiles; ++tl) {
-        slice(g, std::true_type{});
+        if constexpr (NV4W) {
+            // slices in pairs (a tile's slice count is a multiple of 4 here,
+            // and g counts from 0): first, (odd, even) pairs, last
+            slice(g, std::true_type{}, P_EVEN{});
+            ++g;
+            for (int kk = 1; kk + 1 < p.ksteps; kk += 2, g += 2) {
+                slice(g, std::false_type{}, P_ODD{});
+                slice(g + 1, std::false_type{}, P_EVEN{});
+            }
+            slice(g, std::false_type{}, P_ODD{});
+            ++g;
+            TileCursor ec = {tl, 0, 0, 0, 0};
+            locate(ec);
+            __builtin_amdgcn_sched_barrier(0);
+            epilogue(ec);
+            __builtin_amdgcn_sched_barrier(0);
+            after_epilogue = true;
+            continue;
+        }
+        slice(g, std::true_type{}, P_ANY{});
         if constexpr (Op::kScaled) {
             advance(cc);
 #pragma unroll
@@ -1068,7 +1122,7 @@ void tiled_gemm_kernel(GemmArgs p) {
         }
         ++g;
         for (int kk = 1; kk < p.ksteps; ++kk, ++g) {
-            slice(g, std::false_type{});
+            slice(g, std::false_type{}, P_ANY{});
             if constexpr (Op::kScaled) {
                 advance(cc);
 #pragma unroll
