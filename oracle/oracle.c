@@ -493,6 +493,88 @@ int oracle_entries_ld(int dtype, const void* A, int a_order, int64_t lda, const 
 }
 
 /*
+ * MXFP8 operands in either arrangement.  "API Card: Blackwell Pipeline
+ * (tcgen05)", "Descriptor.": fp8 types, like the 16-bit ones, reach the fast
+ * path in either majorness; "Hopper and Blackwell GEMM", Concept, "FP8 and
+ * FP4, with block scaling": the scale blocks run along K, one per 32
+ * elements of a row of A and of a column of B, whatever the elements'
+ * storage.  So, with the element index of the arrangement above:
+ *
+ *   a(i,k) = e4m3(A[a_index]) * e8m0(SA[i * (K/32) + k/32])
+ *   b(k,j) = e4m3(B[b_index]) * e8m0(SB[j * (K/32) + k/32])
+ *
+ * (SA is M x K/32 and SB N x K/32 in both arrangements), then the same sums.
+ */
+static int mx_ld_ok(int a_order, int64_t lda, int b_order, int64_t ldb, int64_t M, int64_t N,
+                    int64_t K) {
+    if (!shape_ok(1, M, N, K) || K % 32 != 0)
+        return 0;
+    if ((a_order != OR_ROW_MAJOR && a_order != OR_COL_MAJOR) ||
+        (b_order != OR_ROW_MAJOR && b_order != OR_COL_MAJOR))
+        return 0;
+    return lda >= (a_order == OR_ROW_MAJOR ? K : M) && lda >= 1 &&
+           ldb >= (b_order == OR_ROW_MAJOR ? N : K) && ldb >= 1;
+}
+
+static double mx_a(const uint8_t* A, int a_order, int64_t lda, const uint8_t* SA, int64_t K,
+                   int64_t i, int64_t k) {
+    return dec_e4m3(A[a_index(a_order, lda, i, k)]) * dec_e8m0(SA[i * (K / 32) + k / 32]);
+}
+
+static double mx_b(const uint8_t* B, int b_order, int64_t ldb, const uint8_t* SB, int64_t K,
+                   int64_t k, int64_t j) {
+    return dec_e4m3(B[b_index(b_order, ldb, k, j)]) * dec_e8m0(SB[j * (K / 32) + k / 32]);
+}
+
+int oracle_gemm_mx_ld(const uint8_t* A, int a_order, int64_t lda, const uint8_t* B, int b_order,
+                      int64_t ldb, const uint8_t* SA, const uint8_t* SB, int64_t M, int64_t N,
+                      int64_t K, double* ref, double* abssum, int nthreads) {
+    if (!A || !B || !SA || !SB || !mx_ld_ok(a_order, lda, b_order, ldb, M, N, K))
+        return -1;
+    double* a = (double*)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
+    double* b = (double*)malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(double));
+    if (!a || !b) {
+        free(a);
+        free(b);
+        return -2;
+    }
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k)
+            a[i * K + k] = mx_a(A, a_order, lda, SA, K, i, k);
+    for (int64_t j = 0; j < N; ++j)
+        for (int64_t k = 0; k < K; ++k)
+            b[j * K + k] = mx_b(B, b_order, ldb, SB, K, k, j);
+    int rc = run_rows(a, b, M, N, K, ref, abssum, nthreads);
+    free(a);
+    free(b);
+    return rc;
+}
+
+int oracle_entries_mx_ld(const uint8_t* A, int a_order, int64_t lda, const uint8_t* B,
+                         int b_order, int64_t ldb, const uint8_t* SA, const uint8_t* SB,
+                         int64_t M, int64_t N, int64_t K, const int64_t* ii, const int64_t* jj,
+                         int64_t n, double* ref, double* abssum) {
+    if (!A || !B || !SA || !SB || !ii || !jj || !mx_ld_ok(a_order, lda, b_order, ldb, M, N, K))
+        return -1;
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t i = ii[t], j = jj[t];
+        if (i < 0 || i >= M || j < 0 || j >= N)
+            return -1;
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double prod = mx_a(A, a_order, lda, SA, K, i, k) * mx_b(B, b_order, ldb, SB, K, k, j);
+            s += prod;
+            sa += fabs(prod);
+        }
+        if (ref)
+            ref[t] = s;
+        if (abssum)
+            abssum[t] = sa;
+    }
+    return 0;
+}
+
+/*
  * Per-element operation of the epilogue.  "API Card: Blackwell Pipeline
  * (tcgen05)", "Device side.", lists process_and_store(out, op) among the
  * epilogue accessors: an operation applied to every result element as it is

@@ -83,6 +83,10 @@ def _load():
             lib.oracle_entries_ld.argtypes = [ci, vp, ci, i64, vp, ci, i64, i64, i64, i64, vp,
                                               vp, i64, dp, dp]
             lib.oracle_apply_op.argtypes = [i64, ci, dp, dp]
+            lib.oracle_gemm_mx_ld.argtypes = [vp, ci, i64, vp, ci, i64, vp, vp, i64, i64, i64, dp,
+                                              dp, ci]
+            lib.oracle_entries_mx_ld.argtypes = [vp, ci, i64, vp, ci, i64, vp, vp, i64, i64, i64,
+                                                 vp, vp, i64, dp, dp]
             cd = ctypes.c_double
             lib.oracle_gemm_nvfp4.argtypes = [vp, vp, vp, vp, cd, cd, i64, i64, i64, dp, dp, ci]
             lib.oracle_entries_nvfp4.argtypes = [vp, vp, vp, vp, cd, cd, i64, i64, i64, vp, vp, i64,
@@ -90,7 +94,8 @@ def _load():
             for f in (lib.oracle_decode, lib.oracle_gemm_tn, lib.oracle_gemm_mx,
                       lib.oracle_gemm_mx_typed, lib.oracle_entries, lib.oracle_axpby,
                       lib.oracle_gemm_ld, lib.oracle_entries_ld, lib.oracle_apply_op,
-                      lib.oracle_gemm_nvfp4, lib.oracle_entries_nvfp4):
+                      lib.oracle_gemm_nvfp4, lib.oracle_entries_nvfp4, lib.oracle_gemm_mx_ld,
+                      lib.oracle_entries_mx_ld):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -291,6 +296,46 @@ def entries_ld(dtype: int, a, a_order: int, lda: int, b, b_order: int, ldb: int,
                                    _ptr(ii), _ptr(jj), ii.size, _ptr(ref), _ptr(s))
     if rc:
         raise ValueError(f"oracle_entries_ld failed ({rc})")
+    return ref, s
+
+
+def _mx_ld_args(a, a_order, lda, b, b_order, ldb, sa, sb, M, N, K):
+    a, b = _ld_args(E4M3, a, a_order, lda, b, b_order, ldb, M, N, K)
+    sa, sb = _raw(sa, E8M0), _raw(sb, E8M0)
+    if K % 32 or sa.shape != (M, K // 32) or sb.shape != (N, K // 32):
+        raise ValueError("MX scales must be M x K/32 and N x K/32 with K a multiple of 32")
+    return a, b, sa, sb
+
+
+def gemm_mx_ld(a, a_order: int, lda: int, b, b_order: int, ldb: int, sa, sb, M: int, N: int,
+               K: int, nthreads: int | None = None):
+    """ref, abssum of the MXFP8 product with A (M x K) and B (K x N) E4M3
+    elements in either arrangement with leading dimensions (raw storage, read
+    flat), sa M x K/32 and sb N x K/32 E8M0 scales (see oracle.c)."""
+    a, b, sa, sb = _mx_ld_args(a, a_order, lda, b, b_order, ldb, sa, sb, M, N, K)
+    ref = np.empty((M, N), np.float64)
+    s = np.empty((M, N), np.float64)
+    rc = _load().oracle_gemm_mx_ld(_ptr(a), a_order, lda, _ptr(b), b_order, ldb, _ptr(sa),
+                                   _ptr(sb), M, N, K, _ptr(ref), _ptr(s),
+                                   nthreads or default_threads())
+    if rc:
+        raise ValueError(f"oracle_gemm_mx_ld failed ({rc})")
+    return ref, s
+
+
+def entries_mx_ld(a, a_order: int, lda: int, b, b_order: int, ldb: int, sa, sb, M: int, N: int,
+                  K: int, ii, jj):
+    """ref, abssum at outputs (ii[t], jj[t]) of the gemm_mx_ld product."""
+    a, b, sa, sb = _mx_ld_args(a, a_order, lda, b, b_order, ldb, sa, sb, M, N, K)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    ref = np.empty(ii.size, np.float64)
+    s = np.empty(ii.size, np.float64)
+    rc = _load().oracle_entries_mx_ld(_ptr(a), a_order, lda, _ptr(b), b_order, ldb, _ptr(sa),
+                                      _ptr(sb), M, N, K, _ptr(ii), _ptr(jj), ii.size, _ptr(ref),
+                                      _ptr(s))
+    if rc:
+        raise ValueError(f"oracle_entries_mx_ld failed ({rc})")
     return ref, s
 
 

@@ -33,6 +33,11 @@ applied to the wrong block -- fails at least one of them:
   stored through torch's own transposes inside NaN-padded rows, equals the
   pinned TN product bit for bit (a swapped index or an ignored leading
   dimension reads a NaN or a wrong element);
+* MXFP8 operands in either arrangement: every row-/column-major pair with
+  E4M3 elements stored through torch's transposes inside rows padded with
+  the E4M3 NaN byte, each element scaled by the block of its logical row of
+  A (column of B), equals the pinned TN MX product bit for bit; a wrong
+  order flag or A's scales applied to B break it;
 * the epilogue's per-element operations: relu's closed form; x * Phi(x)
   against printed standard normal table values; op(x) - op(-x) = x for the
   odd-part forms (gelu, silu); silu at +-ln 3, where the logistic function is
@@ -593,6 +598,75 @@ def test_planted_arrangement_mistakes_fail_the_pin():
     wrong_ld, _ = orc.gemm_ld(orc.BF16, inp.raw(ast), orc.COL_MAJOR, M, inp.raw(bst),
                               orc.ROW_MAJOR, ldb, M, N, K)
     assert not _same(wrong_ld, want)
+
+
+def _stored_bytes(a, b, a_order, b_order, pad):
+    """As _stored, for E4M3 operands held as bytes: the padding is the E4M3
+    NaN byte 0x7F."""
+    ast = a if a_order == orc.ROW_MAJOR else a.T
+    bst = b.T if b_order == orc.ROW_MAJOR else b
+    lda, ldb = ast.shape[1] + pad, bst.shape[1] + pad
+    def rows(x, ld):
+        out = torch.full((x.shape[0], ld), 0x7F, dtype=torch.uint8)
+        out[:, : x.shape[1]] = x
+        return out
+    return rows(ast, lda), lda, rows(bst, ldb), ldb
+
+
+@pytest.mark.parametrize("a_order", [0, 1])
+@pytest.mark.parametrize("b_order", [0, 1])
+@pytest.mark.parametrize("pad", [0, 7])
+def test_mx_arrangements_equal_tn_mx_product(a_order, b_order, pad):
+    """MXFP8 in either arrangement: the E4M3 elements found through the
+    arrangement, each scaled by the block of its logical row of A (column of
+    B), equal the pinned TN MX product bit for bit."""
+    M, N, K = 13, 11, 96
+    g = inp.generator(49 + a_order + 2 * b_order)
+    a = inp.raw(inp.e4m3_normal((M, K), g))
+    b = inp.raw(inp.e4m3_normal((N, K), g))
+    sa, sb = inp.e8m0_scales((M, K // 32), g), inp.e8m0_scales((N, K // 32), g)
+    want, ws = orc.gemm_mx(a, b, inp.raw(sa), inp.raw(sb))
+    ast, lda, bst, ldb = _stored_bytes(torch.from_numpy(a), torch.from_numpy(b), a_order, b_order,
+                                       pad)
+    got, gs = orc.gemm_mx_ld(ast.numpy(), a_order, lda, bst.numpy(), b_order, ldb, inp.raw(sa),
+                             inp.raw(sb), M, N, K)
+    assert _same(got, want) and _same(gs, ws)
+    ii, jj = np.array([0, 12, 7]), np.array([10, 0, 4])
+    r, rs = orc.entries_mx_ld(ast.numpy(), a_order, lda, bst.numpy(), b_order, ldb, inp.raw(sa),
+                              inp.raw(sb), M, N, K, ii, jj)
+    assert _same(r, want[ii, jj]) and _same(rs, ws[ii, jj])
+
+
+def test_mx_arrangement_planted_mistakes_fail_the_pin():
+    """Planted on the CPU: the order flag or leading dimension read wrongly,
+    or A's scales applied to B, must break the equality."""
+    M = N = 32
+    K = 64
+    g = inp.generator(50)
+    a = inp.raw(inp.e4m3_normal((M, K), g))
+    b = inp.raw(inp.e4m3_normal((N, K), g))
+    sa, sb = inp.raw(inp.e8m0_scales((M, K // 32), g)), inp.raw(inp.e8m0_scales((N, K // 32), g))
+    want, _ = orc.gemm_mx(a, b, sa, sb)
+    ast, lda, bst, ldb = _stored_bytes(torch.from_numpy(a), torch.from_numpy(b), orc.COL_MAJOR,
+                                       orc.ROW_MAJOR, 0)
+    ast, bst = ast.numpy(), bst.numpy()
+    ok, _ = orc.gemm_mx_ld(ast, orc.COL_MAJOR, lda, bst, orc.ROW_MAJOR, ldb, sa, sb, M, N, K)
+    assert _same(ok, want)
+    bad, _ = orc.gemm_mx_ld(ast, orc.ROW_MAJOR, K, bst, orc.ROW_MAJOR, ldb, sa, sb, M, N, K)
+    assert not _same(bad, want)
+    bad, _ = orc.gemm_mx_ld(ast, orc.COL_MAJOR, lda, bst, orc.ROW_MAJOR, ldb, sb, sa, M, N, K)
+    assert not _same(bad, want)
+
+
+def test_mx_arrangement_validation():
+    z8 = np.zeros(4096, np.uint8)
+    s = np.zeros((4, 1), np.uint8)
+    with pytest.raises(ValueError):   # K not a multiple of 32
+        orc.gemm_mx_ld(z8, orc.ROW_MAJOR, 48, z8, orc.COL_MAJOR, 48, s, s, 4, 4, 48)
+    with pytest.raises(ValueError):   # column-major A needs lda >= M
+        orc.gemm_mx_ld(z8, orc.COL_MAJOR, 2, z8, orc.COL_MAJOR, 32, s, s, 4, 4, 32)
+    with pytest.raises(ValueError):   # scale tensor of the wrong shape
+        orc.gemm_mx_ld(z8, orc.ROW_MAJOR, 32, z8, orc.COL_MAJOR, 32, s[:3], s, 4, 4, 32)
 
 
 # --------------------------------------------- per-element epilogue ops
