@@ -37,7 +37,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.3,
 HBM_GBS = 8000.0
 KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pingpong.h", "tcm_device.h", "tcm_internal.h", "gemm_tn.hip",
                   "gemm_mx.hip", "gemm_mx6.hip", "gemm_nv4.hip", "gemm_epi.hip", "gemm_mn.h", "gemm_mn_a.hip", "gemm_mn_b.hip",
-                  "gemm_mn_ab.hip", "tcm_api.cpp"]
+                  "gemm_mn_ab.hip", "gemm_mx_mn.h", "gemm_mx_ld.hip", "gemm_mx_mn_a.hip", "gemm_mx_mn_b.hip",
+                  "gemm_mx_mn_ab.hip", "tcm_api.cpp"]
 
 
 def kernel_hash() -> str:

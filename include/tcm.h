@@ -222,6 +222,35 @@ tcm_status tcm_gemm_mx_fp6(const void* A, const void* B, const void* scale_A, co
                            tcm_dtype out_dtype, void* stream);
 
 /*
+ * MXFP8 with operands in either arrangement and leading dimensions:
+ * Out = (A * SA) . (B * SB) with A the M x K and B the K x N matrix of E4M3
+ * elements ("API Card: Blackwell Pipeline (tcgen05)", Descriptor.: fp8
+ * types, like the 16-bit ones, reach the fast path in either majorness;
+ * "Hopper and Blackwell GEMM", Concept, FP8 and FP4 with block scaling).
+ *   A        a_order TCM_ROW_MAJOR: A[i * lda + k] (K contiguous, lda >= K);
+ *            TCM_COL_MAJOR: A[k * lda + i] (M contiguous, lda >= M)
+ *   B        b_order TCM_ROW_MAJOR: B[k * ldb + j] (N contiguous, ldb >= N);
+ *            TCM_COL_MAJOR: B[j * ldb + k] (K contiguous, ldb >= K: the TN
+ *            form of tcm_gemm_mx_fp8)
+ *   scale_A  M x (K/32) E8M0 bytes: scale_A[i][q] multiplies a(i, 32q .. 32q+31)
+ *   scale_B  N x (K/32) E8M0 bytes: scale_B[j][q] multiplies b(32q .. 32q+31, j)
+ *            (the scale layout does not depend on the arrangement)
+ *   Out      M x N of out_dtype (TCM_F32 or TCM_BF16), row-major, rows ldo >= N
+ *            apart, overwritten
+ * elem_dtype must be TCM_E4M3 (TCM_ERR_UNSUPPORTED_DTYPE otherwise).  K must
+ * be a multiple of 32 (TCM_ERR_UNSUPPORTED_SHAPE); lda and ldb are multiples
+ * of 16 and A, B, Out 16-byte aligned (TCM_ERR_MISALIGNED); lda, ldb <= 2^21
+ * (TCM_ERR_UNSUPPORTED_SHAPE); a leading dimension below its minimum is
+ * TCM_ERR_INVALID_SHAPE and an unknown order TCM_ERR_INVALID_ARGUMENT.  Sums
+ * and rounding as tcm_gemm_mx_fp8, which dense TN storage (A row-major with
+ * lda = K, B column-major with ldb = K, ldo = N) runs exactly.
+ */
+tcm_status tcm_gemm_mx(const void* A, tcm_order a_order, int64_t lda, const void* B,
+                       tcm_order b_order, int64_t ldb, const void* scale_A, const void* scale_B,
+                       void* Out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                       tcm_dtype elem_dtype, tcm_dtype out_dtype, void* stream);
+
+/*
  * NVFP4 Out = gA gB (A * SA) . (B * SB)^T ("Hopper and Blackwell GEMM",
  * Concept, "FP8 and FP4, with block scaling": the format table's NVFP4 row,
  * E2M1 elements with an E4M3 scale per 16 values and one FP32 scale per

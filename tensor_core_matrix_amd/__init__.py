@@ -12,9 +12,15 @@ kernels; there is no fallback.  If the library is missing, every call raises.
     gemm_mx_fp8(a, b, scale_a, scale_b, out=None, out_dtype=torch.bfloat16)
     gemm_mx_fp4(a, b, scale_a, scale_b, out=None, out_dtype=torch.bfloat16)
                                                        a: M x K/2, b: N x K/2 E2M1 pairs
-    gemm(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None)
-                                                       Out = alpha a . b + beta c, a: M x K
+    gemm_mx_fp6(a, b, scale_a, scale_b, out=None, out_dtype=None, elem="e2m3")
+                                                       a: M x 3K/4, b: N x 3K/4 packed FP6
+    gemm_nvfp4(a, b, scale_a, scale_b, global_a, global_b, out=None, out_dtype=None)
+                                                       E2M1 pairs, E4M3 scales per 16
+    gemm(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None, op="identity")
+                                                       Out = op(alpha a . b + beta c), a: M x K
                                                        and b: K x N strided views
+    gemm_mx(a, b, scale_a, scale_b, out=None, out_dtype=None)
+                                                       MXFP8, a: M x K and b: K x N strided views
 """
 from __future__ import annotations
 
@@ -22,8 +28,10 @@ import ctypes
 import os
 import threading
 
-__all__ = ["gemm", "gemm_tn", "gemm_tn_ex", "batched_gemm_tn", "gemm_mx_fp8", "gemm_mx_fp4", "plan", "lib", "TcmError",
-           "LIB_PATH", "F16", "BF16", "F32", "E4M3", "E8M0", "E2M1"]
+__all__ = ["gemm", "gemm_tn", "gemm_tn_ex", "batched_gemm_tn", "gemm_mx_fp8", "gemm_mx_fp4",
+           "gemm_mx_fp6", "gemm_nvfp4", "gemm_mx", "order_ld", "plan", "lib", "TcmError",
+           "LIB_PATH", "F16", "BF16", "F32", "E4M3", "E8M0", "E2M1", "E2M3", "E3M2", "ROW_MAJOR",
+           "COL_MAJOR", "OPS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtcm.so")
 
@@ -55,7 +63,7 @@ class Plan(ctypes.Structure):
 _lock = threading.Lock()
 _lib = None
 EXPORTS = ("tcm_gemm", "tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
-           "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_gemm_nvfp4", "tcm_plan_gemm",
+           "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_gemm_mx", "tcm_gemm_nvfp4", "tcm_plan_gemm",
            "tcm_status_string")
 
 
@@ -79,11 +87,14 @@ def lib() -> ctypes.CDLL:
             L.tcm_gemm_mx_fp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, vp]
             L.tcm_gemm_mx_fp6.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
             L.tcm_gemm_nvfp4.argtypes = [vp, vp, vp, vp, cf, cf, vp, i64, i64, i64, ci, vp]
+            L.tcm_gemm_mx.argtypes = [vp, ci, i64, vp, ci, i64, vp, vp, vp, i64, i64, i64, i64, ci,
+                                      ci, vp]
             L.tcm_plan_gemm.argtypes = [i64, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(Plan)]
             L.tcm_status_string.argtypes = [ci]
             L.tcm_status_string.restype = ctypes.c_char_p
             for f in ("tcm_gemm", "tcm_gemm_tn", "tcm_gemm_tn_ex", "tcm_batched_gemm_tn", "tcm_gemm_mx_fp8",
-                      "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_gemm_nvfp4", "tcm_plan_gemm"):
+                      "tcm_gemm_mx_fp4", "tcm_gemm_mx_fp6", "tcm_gemm_mx", "tcm_gemm_nvfp4",
+                      "tcm_plan_gemm"):
                 getattr(L, f).restype = ci
             _lib = L
     return _lib
@@ -285,6 +296,43 @@ def gemm(a, b, c=None, out=None, alpha=1.0, beta=0.0, out_dtype=None, op="identi
                               None if c is None else c.data_ptr(), ldc, out.data_ptr(), ldo,
                               M, N, K, _code(a.dtype), codes[c.dtype] if c is not None else F32,
                               codes[out.dtype], float(alpha), float(beta), OPS[op], _stream(a)))
+    return out
+
+
+def gemm_mx(a, b, scale_a, scale_b, out=None, out_dtype=None):
+    """MXFP8 Out = (a * scale_a) . (b * scale_b) for 2-D views: a (M, K) and
+    b (K, N) of E4M3 elements (float8_e4m3fn or uint8) with rows or columns
+    contiguous (transposed views and slices of larger tensors are taken by
+    their strides); scale_a (M, K/32) and scale_b (N, K/32) E8M0 bytes, one
+    per 32 K values of a row of a and of a column of b; out (M, N)
+    float32/bfloat16 with contiguous rows."""
+    torch = _torch()
+    M, K = a.shape
+    K2, N = b.shape
+    if K2 != K:
+        raise ValueError("a (M, K) and b (K, N) must share K")
+    if K % 32 or tuple(scale_a.shape) != (M, K // 32) or tuple(scale_b.shape) != (N, K // 32):
+        raise ValueError("scale tensors must be (M, K/32) and (N, K/32) with K a multiple of 32")
+    for t in (a, b):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError("MXFP8 elements must be float8_e4m3fn or uint8")
+    for t in (scale_a, scale_b):
+        if t.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not t.is_contiguous():
+            raise TypeError("MX scales must be contiguous uint8 or float8_e8m0fnu")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=a.device)
+    codes = {torch.bfloat16: BF16, torch.float32: F32}
+    if tuple(out.shape) != (M, N) or out.dtype not in codes:
+        raise ValueError(f"out must be {(M, N)} float32 or bfloat16")
+    ao, lda = order_ld(a)
+    bo, ldb = order_ld(b)
+    oo, ldo = order_ld(out)
+    if oo != ROW_MAJOR:
+        raise ValueError("out needs contiguous rows")
+    with torch.cuda.device(a.device):
+        _check(lib().tcm_gemm_mx(a.data_ptr(), ao, lda, b.data_ptr(), bo, ldb, scale_a.data_ptr(),
+                                 scale_b.data_ptr(), out.data_ptr(), ldo, M, N, K, E4M3,
+                                 codes[out.dtype], _stream(a)))
     return out
 
 

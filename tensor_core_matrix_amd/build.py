@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtcm.so")
 ARCH = "gfx950"
 SOURCES = ["tcm_api.cpp", "gemm_tn.hip", "gemm_mx.hip", "gemm_mx6.hip", "gemm_nv4.hip", "gemm_epi.hip",
-           "gemm_mn_a.hip", "gemm_mn_b.hip", "gemm_mn_ab.hip"]
+           "gemm_mn_a.hip", "gemm_mn_b.hip", "gemm_mn_ab.hip", "gemm_mx_ld.hip", "gemm_mx_mn_a.hip",
+           "gemm_mx_mn_b.hip", "gemm_mx_mn_ab.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]

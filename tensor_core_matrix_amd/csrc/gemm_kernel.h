@@ -219,10 +219,13 @@ void tiled_gemm_kernel(GemmArgs p) {
                   "NVFP4: register-staged copies of 64-deep slices, whole rows per thread");
     static_assert(Op::kElemBits >= 8, "whole-byte elements");
     constexpr bool ANY_MN = A_MN || B_MN;
-    static_assert(!ANY_MN || (ESZ == 2 && !Op::kScaled && !VG), "M/N-major: 16-bit, DMA copies");
+    static_assert(!ANY_MN || (!VG && ((ESZ == 2 && !Op::kScaled) || (ESZ == 1 && Op::kScaled && CPL == 2))),
+                  "M/N-major: 16-bit or MXFP8, DMA copies");
     static_assert(!(DENSE && ANY_MN), "dense storage: both operands K-major");
-    static_assert((!A_MN || BM * ESZ >= 256) && (!B_MN || BN * ESZ >= 256),
-                  "M/N-major rows of at least 16 chunks (bank spread of the transposing reads)");
+    static_assert((!A_MN || BM * ESZ >= (ESZ == 2 ? 256 : 128)) &&
+                      (!B_MN || BN * ESZ >= (ESZ == 2 ? 256 : 128)),
+                  "M/N-major rows of at least 16 chunks (16-bit) or 8 chunks (8-bit): bank "
+                  "spread of the transposing reads");
 
     // Epilogue staging: one 32-row block of a wave's output at a time, in a
     // wave-private LDS area after the ring.
@@ -266,8 +269,15 @@ void tiled_gemm_kernel(GemmArgs p) {
     const int cp_k = cp_chunk * (16 / ESZ);  // first K element of the chunk
     // M-major (N-major) operand: the region holds BK rows, one per k of the
     // slice, of the tile's BM (BN) values; chunk q is row q / cpr, physical
-    // chunk q % cpr, holding logical chunk (q % cpr) ^ 4 (row % 4), so that
-    // the four rows a transposing read touches sit in different bank groups.
+    // chunk q % cpr, holding logical chunk (q % cpr) ^ swz(row), so that the
+    // rows a transposing read touches sit in different bank groups: 16-bit
+    // reads cover 4 rows (swz = 4 (row % 4)); 8-bit reads cover 8 rows, with
+    // the neighbouring 16-lane group on the next chunk (swz = 2 (row % 8) for
+    // rows of 16 or more chunks; 2 ((row / 2) % 4) for rows of 8 chunks,
+    // where two rows share a 256-byte bank line).
+    auto mn_swz = [](int row, int cpr) {
+        return ESZ == 2 ? 4 * (row & 3) : cpr >= 16 ? 2 * (row & 7) : 2 * ((row >> 1) & 3);
+    };
     struct CopyGeo {
         uint32_t off, step;  // buffer offset of copy 0, and from copy i to i + 1
     };
@@ -278,7 +288,7 @@ void tiled_gemm_kernel(GemmArgs p) {
     auto mn_geo = [&](int rows, int ld) -> CopyGeo {
         const int cpr = rows * ESZ / 16, rpw = kWaveSize / cpr;
         const int row = wave * rpw + lane / cpr;
-        const int ch = (lane % cpr) ^ (4 * (row & 3));
+        const int ch = (lane % cpr) ^ mn_swz(row, cpr);
         return {(uint32_t)row * (uint32_t)ld * ESZ + ch * 16, 4u * rpw * (uint32_t)ld * ESZ};
     };
     const int lda = DENSE ? K : p.lda;
@@ -310,11 +320,13 @@ void tiled_gemm_kernel(GemmArgs p) {
     };
     // M/N-major: k rows k0 .. k0 + kv - 1 of the slice, columns r0 .. r0 + BR - 1;
     // the bound ends with the last row's last 16-byte piece that holds a
-    // valid column (ld is a multiple of 8), so rows past K read as zeros
-    // and no read leaves the operand's storage.
+    // valid column (ld is a whole number of pieces: a multiple of 8 16-bit
+    // or 16 8-bit elements), so rows past K read as zeros and no read leaves
+    // the operand's storage.
     auto mn_rsrc = [&](const char* base, int r0, int R, int BR, int ld, int k0) {
+        constexpr int EPC = 16 / ESZ;  // elements per 16-byte piece
         const int kv = min(BK, K - k0);
-        const int cols = min(BR, ((R + 7) & ~7) - r0);
+        const int cols = min(BR, ((R + EPC - 1) & ~(EPC - 1)) - r0);
         const uint32_t bytes = kv > 0 ? (uint32_t)((kv - 1) * ld + cols) * ESZ : 0u;
         return make_rsrc(base + ((int64_t)k0 * ld + r0) * ESZ, bytes);
     };
@@ -430,10 +442,25 @@ void tiled_gemm_kernel(GemmArgs p) {
     // c + 16 (g % 2) + t, which is the MFMA operand layout (row l % 32,
     // K values 8 (l / 32) .. + 7).  k % 4 = t / 4 for every such read, so the
     // row's chunk swizzle is a per-lane constant folded into the offset.
+    //
+    // 8-bit (MXFP8) regions: ds_read_b64_tr_b8 gives lane t of a 16-lane
+    // group byte t of each of the 8 rows its group addresses (row r from
+    // lanes 2r and 2r + 1, bytes 0..7 and 8..15; probed on the device).  The
+    // scaled MFMA wants, in lane l of half-wave h, row l % 32 with bytes
+    // 0..15 = k 16 h .. 16 h + 15 and bytes 16..31 = k 32 + 16 h .. + 15, so
+    // four reads (k offsets 0, 8, 32, 40) fill its 32 bytes: lane 16 g + t
+    // reads k row 64 s + off + 16 (g / 2) + t / 2, columns
+    // c + 16 (g % 2) + 8 (t % 2) .. + 7; k % 8 = t / 2, so the row's swizzle
+    // is again a per-lane constant.
     const int g16 = lane >> 4, t16 = lane & 15;
     auto mn_frag_off = [&](int rowb, int col_byte) -> uint32_t {
-        return (uint32_t)((8 * (g16 >> 1) + (t16 >> 2)) * rowb + (col_byte ^ (64 * (t16 >> 2))) +
-                          32 * (g16 & 1) + 8 * (t16 & 3));
+        if constexpr (ESZ == 1)
+            return (uint32_t)((16 * (g16 >> 1) + (t16 >> 1)) * rowb +
+                              (col_byte ^ (16 * mn_swz(t16 >> 1, rowb / 16))) + 16 * (g16 & 1) +
+                              8 * (t16 & 1));
+        else
+            return (uint32_t)((8 * (g16 >> 1) + (t16 >> 2)) * rowb + (col_byte ^ (64 * (t16 >> 2))) +
+                              32 * (g16 & 1) + 8 * (t16 & 3));
     };
     constexpr int RBA = BM * ESZ, RBB = BN * ESZ;  // bytes of one k row, M/N-major regions
     uint32_t a_mn[A_MN ? FM : 1], b_mn[B_MN ? FN : 1];
@@ -447,7 +474,15 @@ void tiled_gemm_kernel(GemmArgs p) {
             b_mn[j] = (uint32_t)A_BYTES + mn_frag_off(RBB, (wn * WTN + 32 * j) * ESZ);
     }
     auto read_frag_tr = [&](const char* at, int rowb) -> frag_t {
-        if constexpr (ANY_MN) {
+        if constexpr (ANY_MN && ESZ == 1) {
+            const i32x2_t q0 = lds_read_tr8(at);
+            const i32x2_t q1 = lds_read_tr8(at + 8 * rowb);
+            const i32x2_t q2 = lds_read_tr8(at + 32 * rowb);
+            const i32x2_t q3 = lds_read_tr8(at + 40 * rowb);
+            const i32x4_t lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3);
+            const i32x4_t up = __builtin_shufflevector(q2, q3, 0, 1, 2, 3);
+            return __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else if constexpr (ANY_MN) {
             const s16x4_t lo = lds_read_tr16(at);
             const s16x4_t up = lds_read_tr16(at + 4 * rowb);
             return __builtin_bit_cast(frag_t,
@@ -456,15 +491,16 @@ void tiled_gemm_kernel(GemmArgs p) {
             return frag_t{};
         }
     };
+    // k rows of one K step: Op::kK (16 for the 16-bit MFMA, 64 for MXFP8)
     auto frag_a = [&](const char* st, int i, int s) -> frag_t {
         if constexpr (A_MN)
-            return read_frag_tr(st + a_mn[i] + 16 * s * RBA, RBA);
+            return read_frag_tr(st + a_mn[i] + Op::kK * s * RBA, RBA);
         else
             return read_frag(st + a_frag + i * 32 * RB, s);
     };
     auto frag_b = [&](const char* st, int j, int s) -> frag_t {
         if constexpr (B_MN)
-            return read_frag_tr(st + b_mn[j] + 16 * s * RBB, RBB);
+            return read_frag_tr(st + b_mn[j] + Op::kK * s * RBB, RBB);
         else
             return read_frag(st + b_frag + j * 32 * RB, s);
     };

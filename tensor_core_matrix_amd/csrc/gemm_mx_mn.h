@@ -1,0 +1,37 @@
+// MXFP8 (E4M3 + E8M0 per 32) with operands in either arrangement and
+// leading dimensions: the 4-wave kernel's 128 x 128 x 128 tile (at 256 x 256
+// the 32-byte MX fragments push the kernel past its registers), an M-major A
+// and/or N-major B staged k row by k row and read with ds_read_b64_tr_b8
+// (A_MN / B_MN in gemm_kernel.h).  One translation unit per arrangement.
+#pragma once
+#include "gemm_kernel.h"
+
+namespace tcm {
+
+// LDS rows of a K-major 128-deep fp8 slice are 128 bytes (8 chunks), chunk
+// XORed with (row / 2) % 8, as for the TN MX kernels.
+constexpr int kMxMnSwizzle = 1;
+
+template <typename TOut, bool A_MN, bool B_MN, bool WORDS>
+static hipError_t launch_mx_mn_one(const GemmArgs& a, int grid, hipStream_t st) {
+    constexpr int BM = 128, BN = 128;
+    constexpr bool epi = 2 * (BM + BN) * 128 + 4 * 32 * (BN / 2) * (int)sizeof(TOut) <= 160 * 1024;
+    hipLaunchKernelGGL((tiled_gemm_kernel<OpMXFP8, TOut, BM, BN, 128, 2, 1, kMxMnSwizzle, WORDS, 1,
+                                          epi, false, false, A_MN, B_MN, false>),
+                       dim3(grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+// scale_mode >= 1: each fragment row's scales of a slice read as one word
+template <bool A_MN, bool B_MN>
+hipError_t launch_gemm_mx_mn(int32_t variant, int32_t out_dtype, int32_t scale_mode,
+                             const GemmArgs& a, int grid, hipStream_t st) {
+    if (variant != V_MX128x128) return hipErrorInvalidValue;
+    if (out_dtype == 1)
+        return scale_mode >= 1 ? launch_mx_mn_one<__bf16, A_MN, B_MN, true>(a, grid, st)
+                               : launch_mx_mn_one<__bf16, A_MN, B_MN, false>(a, grid, st);
+    return scale_mode >= 1 ? launch_mx_mn_one<float, A_MN, B_MN, true>(a, grid, st)
+                           : launch_mx_mn_one<float, A_MN, B_MN, false>(a, grid, st);
+}
+
+}  // namespace tcm

@@ -1,0 +1,7 @@
+// MXFP8 instances: A M-major, B K-major, with leading dimensions.
+#include "gemm_mx_mn.h"
+
+namespace tcm {
+template hipError_t launch_gemm_mx_mn<true, false>(int32_t, int32_t, int32_t, const GemmArgs&, int,
+                                              hipStream_t);
+}  // namespace tcm

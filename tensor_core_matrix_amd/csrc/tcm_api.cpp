@@ -391,6 +391,66 @@ tcm_status tcm_gemm_nvfp4(const void* A, const void* B, const void* scale_A, con
     return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
 }
 
+tcm_status tcm_gemm_mx(const void* A, tcm_order a_order, int64_t lda, const void* B,
+                       tcm_order b_order, int64_t ldb, const void* scale_A, const void* scale_B,
+                       void* Out, int64_t ldo, int64_t M, int64_t N, int64_t K,
+                       tcm_dtype elem_dtype, tcm_dtype out_dtype, void* stream) {
+    if (elem_dtype != TCM_E4M3 || !(out_dtype == TCM_F32 || out_dtype == TCM_BF16))
+        return TCM_ERR_UNSUPPORTED_DTYPE;
+    bool empty = false;
+    tcm_status s = check_sizes(1, M, N, K, &empty);
+    if (s != TCM_OK) return s;
+    auto order_ok = [](tcm_order o) { return o == TCM_ROW_MAJOR || o == TCM_COL_MAJOR; };
+    if (!order_ok(a_order) || !order_ok(b_order)) return TCM_ERR_INVALID_ARGUMENT;
+    const bool a_mn = a_order == TCM_COL_MAJOR;  // A's M index contiguous
+    const bool b_mn = b_order == TCM_ROW_MAJOR;  // B's N index contiguous
+    auto at_least = [](int64_t ld, int64_t n) { return ld >= (n > 1 ? n : 1); };
+    if (!at_least(lda, a_mn ? M : K) || !at_least(ldb, b_mn ? N : K) || !at_least(ldo, N))
+        return TCM_ERR_INVALID_SHAPE;
+    if (!mul_ok(M, ldo, 1)) return TCM_ERR_INVALID_SHAPE;
+    if (empty) return TCM_OK;
+    if (!Out || (K > 0 && (!A || !B || !scale_A || !scale_B))) return TCM_ERR_NULL_POINTER;
+    if ((s = check_range(1, M, N, K)) != TCM_OK) return s;
+    if (lda > kMaxLd || ldb > kMaxLd || ldo > INT32_MAX || K % 32 != 0)
+        return TCM_ERR_UNSUPPORTED_SHAPE;
+    // stored rows of whole 16-byte pieces (16 E4M3 elements)
+    if ((A && !aligned16(A)) || (B && !aligned16(B)) || !aligned16(Out) || lda % 16 != 0 ||
+        ldb % 16 != 0)
+        return TCM_ERR_MISALIGNED;
+    // dense TN storage: the same kernels as tcm_gemm_mx_fp8
+    if (!a_mn && !b_mn && lda == K && ldb == K && ldo == N)
+        return run_mx(8, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream);
+    DeviceInfo dev;
+    if ((s = device_info(&dev)) != TCM_OK) return s;
+    tcm_plan plan;
+    GemmArgs a;
+    plan_variant(V_MX128x128, 1, M, N, K, dev.cus, &plan, &a);
+    a.A = A;
+    a.B = B;
+    a.SA = scale_A;
+    a.SB = scale_B;
+    a.C = Out;
+    a.lda = (int32_t)lda;
+    a.ldb = (int32_t)ldb;
+    a.ldc = (int32_t)ldo;
+    // each fragment row's four scale bytes of a 128-deep slice as one word
+    // when they are whole words
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(scale_A), sb = reinterpret_cast<uintptr_t>(scale_B);
+    const int32_t scale_mode = K > 0 && K % 128 == 0 && ((sa | sb) & 3u) == 0 ? 1 : 0;
+    const int32_t od = (int32_t)out_dtype;
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (a_mn && b_mn)
+        e = launch_gemm_mx_mn<true, true>(V_MX128x128, od, scale_mode, a, plan.grid, st);
+    else if (a_mn)
+        e = launch_gemm_mx_mn<true, false>(V_MX128x128, od, scale_mode, a, plan.grid, st);
+    else if (b_mn)
+        e = launch_gemm_mx_mn<false, true>(V_MX128x128, od, scale_mode, a, plan.grid, st);
+    else
+        e = launch_gemm_mx_mn<false, false>(V_MX128x128, od, scale_mode, a, plan.grid, st);
+    return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
+}
+
 tcm_status tcm_gemm_mx_fp6(const void* A, const void* B, const void* scale_A, const void* scale_B,
                            void* Out, int64_t M, int64_t N, int64_t K, tcm_dtype elem_dtype,
                            tcm_dtype out_dtype, void* stream) {

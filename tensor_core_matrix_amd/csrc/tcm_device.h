@@ -81,6 +81,13 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const void* p) {
         (__attribute__((address_space(3))) s16x4_t*)(p));
 }
 
+// ds_read_b64_tr_b8: lane t of each 16-lane group receives byte t of the 8
+// rows of 16 bytes its group addresses (row r from lanes 2r, 2r + 1).
+__device__ __forceinline__ i32x2_t lds_read_tr8(const void* p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) i32x2_t*)(p));
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

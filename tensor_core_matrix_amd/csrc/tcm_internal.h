@@ -96,6 +96,12 @@ hipError_t launch_gemm_mn(int32_t variant, int32_t in_dtype, int32_t out_dtype, 
                           int grid, hipStream_t stream);
 hipError_t launch_gemm_mx(int32_t variant, int32_t out_dtype, int32_t scale_mode, const GemmArgs& a,
                           int grid, hipStream_t stream);
+// MXFP8 with an M-major A (A_MN) and/or N-major B (B_MN) and leading
+// dimensions (lda, ldb, ldc); variant V_MX128x128 only.  One translation
+// unit per arrangement.
+template <bool A_MN, bool B_MN>
+hipError_t launch_gemm_mx_mn(int32_t variant, int32_t out_dtype, int32_t scale_mode,
+                             const GemmArgs& a, int grid, hipStream_t stream);
 // NVFP4 (variants V_NV4_*): GemmArgs.SA/SB hold the E4M3 block scales and
 // alpha the product of the two tensor scales.
 hipError_t launch_gemm_nv4(int32_t variant, int32_t out_dtype, const GemmArgs& a, int grid,

@@ -245,6 +245,46 @@ def test_general_entry_validation():
     assert call_gen(ldo=67, ldc=65) in ok                         # Out / C rows are free
 
 
+def call_mx(a=A, ao=ROW, lda=64, b=B, bo=COL, ldb=64, sa=SA, sb=SB, o=C, ldo=64, M=64, N=64,
+            K=64, edt=tcm.E4M3, odt=tcm.BF16):
+    return tcm.lib().tcm_gemm_mx(a, ao, lda, b, bo, ldb, sa, sb, o, ldo, M, N, K, edt, odt, None)
+
+
+def test_mx_general_entry_validation():
+    ok = (OK, NO_DEVICE)
+    for ao in (ROW, COL):
+        for bo in (ROW, COL):
+            assert call_mx(ao=ao, bo=bo) in ok
+    assert call_mx(odt=tcm.F32) in ok
+    # element and output types: E4M3 in, f32 / bf16 out
+    assert call_mx(edt=tcm.E2M1) == UNSUP_DTYPE
+    assert call_mx(edt=tcm.BF16) == UNSUP_DTYPE
+    assert call_mx(odt=tcm.F16) == UNSUP_DTYPE
+    # orders and leading dimensions
+    assert call_mx(ao=2) == BADARG
+    assert call_mx(bo=-1) == BADARG
+    assert call_mx(lda=48, K=64) == BADSHAPE                       # row-major A: lda >= K
+    assert call_mx(ao=COL, lda=48, M=64, K=32) == BADSHAPE         # column-major A: lda >= M
+    assert call_mx(ao=COL, lda=64, M=64, K=256, ldb=256) in ok     # ... and K is free of lda
+    assert call_mx(bo=ROW, ldb=48, N=64) == BADSHAPE               # row-major B: ldb >= N
+    assert call_mx(ldo=63) == BADSHAPE
+    assert call_mx(M=0, a=None, b=None, sa=None, sb=None, o=None) == OK   # empty: no-op
+    # pointers
+    assert call_mx(o=None) == NULLP
+    assert call_mx(sa=None) == NULLP
+    assert call_mx(b=None) == NULLP
+    # range and shape: K a multiple of 32, ld within 2^21
+    assert call_mx(K=48, lda=64, ldb=64) == UNSUP_SHAPE
+    assert call_mx(lda=1 << 22) == UNSUP_SHAPE
+    assert call_mx(M=-1) == BADSHAPE
+    # alignment: rows of whole 16-byte pieces, 16-byte aligned operands
+    assert call_mx(lda=72) == MISALIGNED
+    assert call_mx(bo=ROW, ldb=72, N=64) == MISALIGNED
+    assert call_mx(a=A + 8) == MISALIGNED
+    assert call_mx(o=C + 4) == MISALIGNED
+    assert call_mx(ldo=67) in ok                                  # Out rows are free
+
+
 def test_order_ld_of_views():
     import torch
     x = torch.empty(40, 24)
