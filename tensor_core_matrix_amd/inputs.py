@@ -27,6 +27,10 @@ problems):
 * ``nvfp4_8192`` -- A, B 8192x8192 E2M1 codes (every code equally likely),
   one E4M3 scale per 16 (exponent uniform on -4..4, every mantissa), tensor
   scales 0.5 and 1.25, seed 8, bf16 output (the format table's NVFP4 row).
+* ``mxfp8_8192_mn`` -- MXFP8 8192^3 with A column-major (stored K x M, its M
+  index contiguous) and B row-major (stored K x N): E4M3 N(0,1) elements and
+  E8M0 scales as ``mxfp8_8192``, seed 9, bf16 output ("API Card: Blackwell
+  Pipeline (tcgen05)", Descriptor.: fp8 types in either majorness).
 * ``bf16_8192_nn`` -- A 8192x8192 and B 8192x8192 bfloat16, both row-major
   (B stored K x N, its N index contiguous: the product A . B of two
   row-major matrices), N(0,1)*0.05, seed 6, bf16 output ("API Card:
@@ -56,6 +60,7 @@ class Workload:
     sigma: float = 1.0
     scale_exp: tuple = field(default=(-4, 4))
     b_order: str = "col"  # "col": B stored N x K (the TN form); "row": stored K x N
+    a_order: str = "row"  # "row": A stored M x K (the TN form); "col": stored K x M
     globals: tuple = field(default=(1.0, 1.0))  # NVFP4 per-tensor scales gA, gB
 
     @property
@@ -75,6 +80,8 @@ WORKLOADS = {
                            globals=(0.5, 1.25)),
     "bf16_8192_nn": Workload("bf16_8192_nn", 1, 8192, 8192, 8192, "bf16", "bf16", 6, "normal", 0.05,
                              b_order="row"),
+    "mxfp8_8192_mn": Workload("mxfp8_8192_mn", 1, 8192, 8192, 8192, "e4m3", "bf16", 9, "normal", 1.0,
+                              b_order="row", a_order="col"),
 }
 
 TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
@@ -152,7 +159,7 @@ def make(w: Workload | str) -> dict:
         w = WORKLOADS[w]
     g = generator(w.seed)
     lead = (w.batch,) if w.batch > 1 else ()
-    shp_a = lead + (w.M, w.K)
+    shp_a = lead + ((w.K, w.M) if w.a_order == "col" else (w.M, w.K))
     shp_b = lead + ((w.K, w.N) if w.b_order == "row" else (w.N, w.K))
     if w.dtype == "nvfp4":
         a, b = e2m1_codes(w.M, w.K, g), e2m1_codes(w.N, w.K, g)

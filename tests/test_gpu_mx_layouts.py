@@ -177,3 +177,21 @@ def test_mx_dense_tn_through_the_general_entry_is_the_tn_product():
     got = tcm.gemm_mx(ad, btd.t(), sad, sbd, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+
+
+def test_workload_mxfp8_8192_mn():
+    """The measured workload (A stored K x M, B stored K x N, 8192^3) in the
+    launch the bench times, on sampled outputs."""
+    w = inp.WORKLOADS["mxfp8_8192_mn"]
+    x = inp.make(w)
+    A = x["A"].to(DEV).t()      # (M, K) view, M contiguous
+    B = x["B"].to(DEV)          # (K, N), N contiguous
+    out = tcm.gemm_mx(A, B, x["SA"].to(DEV), x["SB"].to(DEV), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    ii = np.concatenate([rng.integers(0, w.M, 4096), [0, w.M - 1, 0, w.M - 1]])
+    jj = np.concatenate([rng.integers(0, w.N, 4096), [0, 0, w.N - 1, w.N - 1]])
+    ref, s = orc.entries_mx_ld(inp.raw(x["A"]), C, w.M, inp.raw(x["B"]), R, w.N, inp.raw(x["SA"]),
+                               inp.raw(x["SB"]), w.M, w.N, w.K, ii, jj)
+    got = out.cpu()[torch.from_numpy(ii), torch.from_numpy(jj)]
+    check(got, ref, s, "bf16", "mxfp8_8192_mn sampled")
