@@ -44,6 +44,7 @@ VariantInfo variant_info(int32_t v) {
     case V_NV4_128: return {128, 128, 64, 2, 2, 16, kThreads};
     case V_NV4W_256: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_NV4W_128: return {128, 128, 64, 2, 2, 16, kThreads};
+    case V_MX256x128: return {256, 128, 128, 2, 1, 8, kThreads};
     }
     return {0, 0, 0, 0, 0, 0, kThreads};
 }
@@ -130,6 +131,9 @@ bool is_nv4_variant(int32_t v) {
     return v == V_NV4_256 || v == V_NV4_128 || v == V_NV4W_256 || v == V_NV4W_128;
 }
 
+// variants launched only by their own entry point (not forceable elsewhere)
+bool own_entry_variant(int32_t v) { return is_nv4_variant(v) || v == V_MX256x128; }
+
 // TCM_FORCE_VARIANT=<id> (read at every call) forces a kernel variant of the
 // matching family, for tuning sweeps and per-variant tests; unset or invalid,
 // the heuristic below chooses.
@@ -154,7 +158,7 @@ int64_t max_grid() {
 int32_t choose_variant(int64_t batch, int64_t M, int64_t N, int32_t bits, int cus) {
     const int32_t f = forced_variant();
     if (f >= 0 && variant_info(f).tile_m > 0 && variant_info(f).elem_bits == bits &&
-        !is_nv4_variant(f))
+        !own_entry_variant(f))
         return f;
     static const int32_t plain[] = {V_T256x256_SPLIT3, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MXPP256_K64S4, V_MX128x128};
@@ -422,9 +426,15 @@ tcm_status tcm_gemm_mx(const void* A, tcm_order a_order, int64_t lda, const void
         return run_mx(8, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream);
     DeviceInfo dev;
     if ((s = device_info(&dev)) != TCM_OK) return s;
+    // 256 x 128 tiles where they fill the CUs with little padding
+    const int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
+    const double fill = double(M) * N / (double(tiles) * 256 * 128);
+    int32_t v = tiles >= dev.cus && fill >= 0.9 ? V_MX256x128 : V_MX128x128;
+    const int32_t f = forced_variant();
+    if (f == V_MX256x128 || f == V_MX128x128) v = f;
     tcm_plan plan;
     GemmArgs a;
-    plan_variant(V_MX128x128, 1, M, N, K, dev.cus, &plan, &a);
+    plan_variant(v, 1, M, N, K, dev.cus, &plan, &a);
     a.A = A;
     a.B = B;
     a.SA = scale_A;
@@ -441,13 +451,13 @@ tcm_status tcm_gemm_mx(const void* A, tcm_order a_order, int64_t lda, const void
     const hipStream_t st = (hipStream_t)stream;
     hipError_t e;
     if (a_mn && b_mn)
-        e = launch_gemm_mx_mn<true, true>(V_MX128x128, od, scale_mode, a, plan.grid, st);
+        e = launch_gemm_mx_mn<true, true>(v, od, scale_mode, a, plan.grid, st);
     else if (a_mn)
-        e = launch_gemm_mx_mn<true, false>(V_MX128x128, od, scale_mode, a, plan.grid, st);
+        e = launch_gemm_mx_mn<true, false>(v, od, scale_mode, a, plan.grid, st);
     else if (b_mn)
-        e = launch_gemm_mx_mn<false, true>(V_MX128x128, od, scale_mode, a, plan.grid, st);
+        e = launch_gemm_mx_mn<false, true>(v, od, scale_mode, a, plan.grid, st);
     else
-        e = launch_gemm_mx_mn<false, false>(V_MX128x128, od, scale_mode, a, plan.grid, st);
+        e = launch_gemm_mx_mn<false, false>(v, od, scale_mode, a, plan.grid, st);
     return e == hipSuccess ? TCM_OK : TCM_ERR_HIP;
 }
 

@@ -65,6 +65,7 @@ enum Variant : int32_t {
     V_NV4_128 = 23,         // NVFP4 128x128x64, the same
     V_NV4W_256 = 24,        // V_NV4_256 with a row's scales of four slices in one load
     V_NV4W_128 = 25,        // V_NV4_128, the same
+    V_MX256x128 = 26,       // MXFP8 256x128x128, 2-stage ring (arrangements and leading dimensions)
     V_MX256x256 = 10, // MXFP8 256x256x128, 2-stage ring
     V_MX128x128 = 11, // MXFP8 128x128x128, 2-stage ring
     V_MX256x256_SPLIT2 = 12, // MXFP8 256x256x128, copies split over 2 K steps
@@ -97,7 +98,7 @@ hipError_t launch_gemm_mn(int32_t variant, int32_t in_dtype, int32_t out_dtype, 
 hipError_t launch_gemm_mx(int32_t variant, int32_t out_dtype, int32_t scale_mode, const GemmArgs& a,
                           int grid, hipStream_t stream);
 // MXFP8 with an M-major A (A_MN) and/or N-major B (B_MN) and leading
-// dimensions (lda, ldb, ldc); variant V_MX128x128 only.  One translation
+// dimensions (lda, ldb, ldc); variants V_MX256x128 and V_MX128x128.  One translation
 // unit per arrangement.
 template <bool A_MN, bool B_MN>
 hipError_t launch_gemm_mx_mn(int32_t variant, int32_t out_dtype, int32_t scale_mode,

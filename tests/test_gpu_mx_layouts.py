@@ -109,15 +109,17 @@ def test_mx_arrangements(ao, bo, shape):
     check(got, ref, s, odt, f"A {'RC'[ao]} B {'RC'[bo]} {shape} {odt}")
 
 
+# variants 26 (256 x 128 tiles) and 11 (128 x 128), forced
+@pytest.mark.parametrize("variant", [26, 11])
 @pytest.mark.parametrize("ao,bo", [(C, R), (R, R), (C, C), (R, C)])
-def test_mx_arrangement_leading_dimensions_and_persistent_grid(ao, bo):
+def test_mx_arrangement_leading_dimensions_and_persistent_grid(ao, bo, variant):
     """Leading dimensions past the rows on every matrix (operand pads are NaN),
-    and a grid of 3 workgroups walking many tiles each."""
+    and a grid of 3 workgroups walking many tiles each, for each tile."""
     M, N, K = 777, 645, 768
-    a, bt, sa, sb = make(M, N, K, 1320 + 2 * ao + bo)
-    with env(TCM_MAX_GRID=3):
+    a, bt, sa, sb = make(M, N, K, 1320 + 2 * ao + bo + variant)
+    with env(TCM_MAX_GRID=3, TCM_FORCE_VARIANT=variant):
         got, ref, s = run(a, bt, sa, sb, ao, bo, "f32", extra=48, ldo_extra=24)
-    check(got, ref, s, "f32", f"ld, A {'RC'[ao]} B {'RC'[bo]}")
+    check(got, ref, s, "f32", f"ld, A {'RC'[ao]} B {'RC'[bo]}, variant {variant}")
 
 
 def test_mx_arrangement_unaligned_scales():
