@@ -205,9 +205,12 @@ void tiled_gemm_kernel(GemmArgs p) {
     static_assert((S - 1) * LOADS < 64, "vmcnt range");
     static_assert(NSPLIT >= 1 && NSPLIT <= KSTEPS && NSPLIT <= LOADS, "copy split");
     // Part p of a slice's copies: copies part_base(p) .. part_base(p + 1) - 1.
-    auto part_base = [](int p) { return p * LOADS / NSPLIT; };
-    constexpr int PART = LOADS / NSPLIT;                 // copies in part 0
-    constexpr int PMAX = (LOADS + NSPLIT - 1) / NSPLIT;  // largest part
+    // Uneven splits put the larger parts first (16 copies in 3 parts: 6/5/5),
+    // since an earlier part has longer to land before the next hand-off
+    // (measured +1 % over 5/5/6 on the bf16 256 x 256 kernel).
+    auto part_base = [](int p) { return (p * LOADS + NSPLIT - 1) / NSPLIT; };
+    constexpr int PART = (LOADS + NSPLIT - 1) / NSPLIT;  // copies in part 0 (the largest)
+    constexpr int PMAX = PART;                           // largest part
     static_assert(CPR == 4 || CPR == 8, "row slice must be 64 or 128 bytes");
     static_assert(A_BYTES % (kThreads * 16) == 0 && B_BYTES % (kThreads * 16) == 0, "copy split");
     static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");

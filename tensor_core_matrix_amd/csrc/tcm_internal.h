@@ -58,7 +58,7 @@ enum Variant : int32_t {
     V_PP256_K32S4_CM = 16, // variant 9 with the copies issued between the MFMAs
     V_T256x256_VG2 = 17,   // variant 6 with register-staged copies (loads + ds_write)
     V_T256x256_VG4 = 18,   // variant 7 with register-staged copies
-    V_T256x256_SPLIT3 = 19, // 256x256x64, 2-stage ring, copies split over 3 K steps (5/5/6)
+    V_T256x256_SPLIT3 = 19, // 256x256x64, 2-stage ring, copies split over 3 K steps (6/5/5)
     V_MX4PP256 = 20,        // MXFP4 256x256x128 ping-pong, 4-stage ring
     V_MX6PP256 = 21,        // MXFP6 256x256x64 ping-pong, 4-stage ring, grouped row layout
     V_NV4_256 = 22,         // NVFP4 256x256x64, dequantizing register-staged copies, fp16 MFMA
