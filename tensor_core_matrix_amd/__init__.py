@@ -398,7 +398,8 @@ def gemm_nvfp4(a, b, scale_a, scale_b, global_a=1.0, global_b=1.0, out=None, out
 
 def plan(M, N, K, dtype=BF16, out_dtype=BF16, batch=1, mx=False, num_cus=256) -> dict:
     """The launch a call would make (tile, ring depth, LDS bytes, grid).  mx:
-    False (or 0) plain, True (or 1) MXFP8, 2 MXFP4, 3 MXFP6."""
+    False (or 0) plain, True (or 1) MXFP8, 2 MXFP4, 3 MXFP6, 4 NVFP4, 5 MXFP8
+    with an M- or N-major operand (gemm_mx)."""
     p = Plan()
     _check(lib().tcm_plan_gemm(batch, M, N, K, dtype, out_dtype, int(mx), num_cus,
                                ctypes.byref(p)))

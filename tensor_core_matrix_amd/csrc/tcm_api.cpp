@@ -234,6 +234,30 @@ tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t bit
     return plan_variant(choose_variant(batch, M, N, bits, cus), batch, M, N, K, cus, plan, args);
 }
 
+// NVFP4: the 256 x 256 tile where it fills the CUs with little padding; a
+// row's scales of four slices in one 16-byte load where K and the scale
+// tensors allow it (wide).
+int32_t nv4_variant(int64_t M, int64_t N, bool wide, int cus) {
+    const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
+    const double fill = double(M) * N / (double(tiles) * 256 * 256);
+    const bool big = tiles >= cus && fill >= 0.9;
+    int32_t v = wide ? (big ? V_NV4W_256 : V_NV4W_128) : (big ? V_NV4_256 : V_NV4_128);
+    const int32_t f = forced_variant();
+    if (f == V_NV4_256 || f == V_NV4_128 || (wide && (f == V_NV4W_256 || f == V_NV4W_128))) v = f;
+    return v;
+}
+
+// MXFP8 in other arrangements: 256 x 128 tiles where they fill the CUs with
+// little padding, else 128 x 128.
+int32_t mx_mn_variant(int64_t M, int64_t N, int cus) {
+    const int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
+    const double fill = double(M) * N / (double(tiles) * 256 * 128);
+    int32_t v = tiles >= cus && fill >= 0.9 ? V_MX256x128 : V_MX128x128;
+    const int32_t f = forced_variant();
+    if (f == V_MX256x128 || f == V_MX128x128) v = f;
+    return v;
+}
+
 bool plain_pair(tcm_dtype in, tcm_dtype out) {
     return (in == TCM_F16 || in == TCM_BF16) && (out == TCM_F32 || out == TCM_BF16);
 }
@@ -365,17 +389,9 @@ tcm_status tcm_gemm_nvfp4(const void* A, const void* B, const void* scale_A, con
         return TCM_ERR_MISALIGNED;
     DeviceInfo dev;
     if ((s = device_info(&dev)) != TCM_OK) return s;
-    // the 256 x 256 tile where it fills the CUs with little padding; a row's
-    // scales of four slices in one 16-byte load where K and the scale
-    // tensors allow it
     const bool wide = K % 256 == 0 && (!scale_A || aligned16(scale_A)) &&
                       (!scale_B || aligned16(scale_B));
-    const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
-    const double fill = double(M) * N / (double(tiles) * 256 * 256);
-    const bool big = tiles >= dev.cus && fill >= 0.9;
-    int32_t v = wide ? (big ? V_NV4W_256 : V_NV4W_128) : (big ? V_NV4_256 : V_NV4_128);
-    const int32_t f = forced_variant();
-    if (f == V_NV4_256 || f == V_NV4_128 || (wide && (f == V_NV4W_256 || f == V_NV4W_128))) v = f;
+    const int32_t v = nv4_variant(M, N, wide, dev.cus);
     tcm_plan plan;
     GemmArgs a;
     plan_variant(v, 1, M, N, K, dev.cus, &plan, &a);
@@ -426,12 +442,7 @@ tcm_status tcm_gemm_mx(const void* A, tcm_order a_order, int64_t lda, const void
         return run_mx(8, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream);
     DeviceInfo dev;
     if ((s = device_info(&dev)) != TCM_OK) return s;
-    // 256 x 128 tiles where they fill the CUs with little padding
-    const int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
-    const double fill = double(M) * N / (double(tiles) * 256 * 128);
-    int32_t v = tiles >= dev.cus && fill >= 0.9 ? V_MX256x128 : V_MX128x128;
-    const int32_t f = forced_variant();
-    if (f == V_MX256x128 || f == V_MX128x128) v = f;
+    const int32_t v = mx_mn_variant(M, N, dev.cus);
     tcm_plan plan;
     GemmArgs a;
     plan_variant(v, 1, M, N, K, dev.cus, &plan, &a);
@@ -584,8 +595,10 @@ tcm_status tcm_gemm(const void* A, tcm_order a_order, int64_t lda, const void* B
 tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
                          tcm_dtype out_dtype, int mx, int num_cus, tcm_plan* plan) {
     if (!plan) return TCM_ERR_NULL_POINTER;
-    if (mx ? !(out_dtype == TCM_F32 || out_dtype == TCM_BF16) : !plain_pair(dtype, out_dtype))
-        return TCM_ERR_UNSUPPORTED_DTYPE;
+    if (mx < 0 || mx > 5) return TCM_ERR_INVALID_ARGUMENT;
+    const bool out_ok = out_dtype == TCM_F32 || out_dtype == TCM_BF16 ||
+                        (mx == 4 && out_dtype == TCM_F16);
+    if (mx ? !out_ok : !plain_pair(dtype, out_dtype)) return TCM_ERR_UNSUPPORTED_DTYPE;
     bool empty = false;
     tcm_status s = check_sizes(batch, M, N, K, &empty);
     if (s != TCM_OK) return s;
@@ -596,8 +609,14 @@ tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dty
         if ((s = device_info(&dev)) != TCM_OK) return s;
         num_cus = dev.cus;
     }
-    make_plan(batch < 1 ? 1 : batch, M < 1 ? 1 : M, N < 1 ? 1 : N, K,
-              mx == 3 ? 6 : mx == 2 ? 4 : mx ? 8 : 16, num_cus, plan, nullptr);
+    const int64_t b1 = batch < 1 ? 1 : batch, m1 = M < 1 ? 1 : M, n1 = N < 1 ? 1 : N;
+    if (mx == 4)
+        plan_variant(nv4_variant(m1, n1, K % 256 == 0, num_cus), b1, m1, n1, K, num_cus, plan,
+                     nullptr);
+    else if (mx == 5)
+        plan_variant(mx_mn_variant(m1, n1, num_cus), b1, m1, n1, K, num_cus, plan, nullptr);
+    else
+        make_plan(b1, m1, n1, K, mx == 3 ? 6 : mx == 2 ? 4 : mx ? 8 : 16, num_cus, plan, nullptr);
     if (empty) {
         plan->grid = 0;
         plan->tiles = 0;

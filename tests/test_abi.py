@@ -182,6 +182,21 @@ def test_plans_of_the_workloads():
     p = tcm.plan(8192, 8192, 8192, mx=2)
     assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"]) == \
         (256, 128, 32 * 1024, 4, 512)
+    # NVFP4 8192^3: the 256 x 256 fp16 tile, a row's scales of four slices per
+    # load (variant 24); K not a multiple of 256: variant 22; small: 128 x 128
+    p = tcm.plan(8192, 8192, 8192, mx=4)
+    assert (p["tile_m"], p["tile_n"], p["tile_k"], p["kernel"]) == (256, 256, 64, 24)
+    assert tcm.plan(8192, 8192, 8160, mx=4)["kernel"] == 22
+    assert tcm.plan(1024, 1024, 1024, mx=4, out_dtype=tcm.F16)["kernel"] == 25
+    # MXFP8 with an M- or N-major operand: 256 x 128 x 128 tiles (variant 26),
+    # 128 x 128 for problems they would not fill
+    p = tcm.plan(8192, 8192, 8192, mx=5)
+    assert (p["tile_m"], p["tile_n"], p["tile_k"], p["kernel"]) == (256, 128, 128, 26)
+    assert tcm.plan(512, 512, 512, mx=5)["kernel"] == 11
+    with pytest.raises(tcm.TcmError):
+        tcm.plan(64, 64, 64, mx=6)
+    with pytest.raises(tcm.TcmError):
+        tcm.plan(64, 64, 64, mx=1, out_dtype=tcm.F16)
     # empty problem plans nothing
     assert tcm.plan(0, 8, 8)["grid"] == 0
 
