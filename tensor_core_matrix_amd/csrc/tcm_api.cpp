@@ -389,7 +389,8 @@ tcm_status tcm_gemm_nvfp4(const void* A, const void* B, const void* scale_A, con
         return TCM_ERR_MISALIGNED;
     DeviceInfo dev;
     if ((s = device_info(&dev)) != TCM_OK) return s;
-    const bool wide = K % 256 == 0 && (!scale_A || aligned16(scale_A)) &&
+    // (the wide form walks a tile's slices in pairs: K > 0)
+    const bool wide = K > 0 && K % 256 == 0 && (!scale_A || aligned16(scale_A)) &&
                       (!scale_B || aligned16(scale_B));
     const int32_t v = nv4_variant(M, N, wide, dev.cus);
     tcm_plan plan;
@@ -611,8 +612,8 @@ tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dty
     }
     const int64_t b1 = batch < 1 ? 1 : batch, m1 = M < 1 ? 1 : M, n1 = N < 1 ? 1 : N;
     if (mx == 4)
-        plan_variant(nv4_variant(m1, n1, K % 256 == 0, num_cus), b1, m1, n1, K, num_cus, plan,
-                     nullptr);
+        plan_variant(nv4_variant(m1, n1, K > 0 && K % 256 == 0, num_cus), b1, m1, n1, K, num_cus,
+                     plan, nullptr);
     else if (mx == 5)
         plan_variant(mx_mn_variant(m1, n1, num_cus), b1, m1, n1, K, num_cus, plan, nullptr);
     else

@@ -197,3 +197,40 @@ def test_workload_mxfp8_8192_mn():
                                inp.raw(x["SB"]), w.M, w.N, w.K, ii, jj)
     got = out.cpu()[torch.from_numpy(ii), torch.from_numpy(jj)]
     check(got, ref, s, "bf16", "mxfp8_8192_mn sampled")
+
+
+def test_k_zero_writes_zeros_every_block_scaled_entry():
+    """K = 0: every output is the empty sum, 0, for each block-scaled entry
+    (no operand or scale byte is read)."""
+    M, N = 300, 260
+    u8 = dict(dtype=torch.uint8, device=DEV)
+
+    def fresh(dt=torch.float32):
+        return torch.full((M, N), float("nan"), dtype=dt, device=DEV)
+
+    outs = []
+    o = fresh()
+    tcm.gemm_mx_fp8(torch.empty(M, 0, **u8), torch.empty(N, 0, **u8), torch.empty(M, 0, **u8),
+                    torch.empty(N, 0, **u8), o)
+    outs.append(("mx_fp8", o))
+    o = fresh()
+    tcm.gemm_mx_fp4(torch.empty(M, 0, **u8), torch.empty(N, 0, **u8), torch.empty(M, 0, **u8),
+                    torch.empty(N, 0, **u8), o)
+    outs.append(("mx_fp4", o))
+    o = fresh()
+    tcm.gemm_mx_fp6(torch.empty(M, 0, **u8), torch.empty(N, 0, **u8), torch.empty(M, 0, **u8),
+                    torch.empty(N, 0, **u8), o)
+    outs.append(("mx_fp6", o))
+    o = fresh(torch.float16)
+    tcm.gemm_nvfp4(torch.empty(M, 0, **u8), torch.empty(N, 0, **u8), torch.empty(M, 0, **u8),
+                   torch.empty(N, 0, **u8), 2.0, 3.0, o)
+    outs.append(("nvfp4", o))
+    o = fresh()
+    # general MX entry: A column-major, B row-major, leading dimensions 16
+    A = torch.empty(0, 16 * ((M + 15) // 16), **u8)[:, :M].t()
+    B = torch.empty(0, 16 * ((N + 15) // 16), **u8)[:, :N]
+    tcm.gemm_mx(A, B, torch.empty(M, 0, **u8), torch.empty(N, 0, **u8), o)
+    outs.append(("mx general", o))
+    torch.cuda.synchronize()
+    for name, o in outs:
+        assert bool((o == 0).all()), name
