@@ -205,3 +205,22 @@ def test_large_sampled(orders):
     ref, s = orc.entries_ld(orc.BF16, inp.raw(ast), ao, lda, inp.raw(bst), bo, ldb, M, N, K, ii, jj)
     got = out.cpu()[torch.from_numpy(ii), torch.from_numpy(jj)]
     check(got, orc.axpby(1.0, ref), 1.0, s, np.zeros_like(ref), "bf16", f"{IDS[orders]} 4096")
+
+
+@pytest.mark.parametrize("ao,bo", [(R, C), (C, R)])
+def test_k_zero_general_form_is_beta_c(ao, bo):
+    """K = 0: the product is the empty sum, so Out = op(beta * C) exactly
+    (power-of-two beta), for K-major and M/N-major operands alike."""
+    M, N = 300, 260
+    g = inp.generator(1400 + ao)
+    c = inp.normal((M, N), g, 1.0, torch.float32)
+    a_st = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV) if ao == C else \
+        torch.empty(M, 8, dtype=torch.bfloat16, device=DEV)
+    b_st = torch.empty(0, 264, dtype=torch.bfloat16, device=DEV) if bo == R else \
+        torch.empty(N, 8, dtype=torch.bfloat16, device=DEV)
+    a = a_st[:, :0] if ao == R else torch.empty(0, 304, dtype=torch.bfloat16, device=DEV)[:, :M].t()
+    b = b_st[:, :N] if bo == R else b_st[:, :0].t()
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    tcm.gemm(a, b, c.to(DEV), out, alpha=3.0, beta=-0.5, op="relu")
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), torch.relu(-0.5 * c))
