@@ -5,7 +5,7 @@
 // and/or N-major B staged k row by k row and read with ds_read_b64_tr_b8
 // (A_MN / B_MN in gemm_kernel.h).  One translation unit per arrangement.
 #pragma once
-#include "gemm_kernel.h"
+#include "gemm_pingpong.h"
 
 namespace tcm {
 
@@ -28,12 +28,40 @@ static hipError_t by_scale_mode(int32_t scale_mode, const GemmArgs& a, int grid,
                            : launch_mx_mn_one<TOut, BM, BN, A_MN, B_MN, false>(a, grid, st);
 }
 
+// The ping-pong kernel (eight waves, ring of four 64-deep units) with an
+// M/N-major operand; scale_mode as for the TN MX kernels (0 bytes, 1 words,
+// 2 16-byte chunks).
+template <typename TOut, bool A_MN, bool B_MN>
+static hipError_t launch_mx_pp_mn(int32_t scale_mode, const GemmArgs& a, int grid, hipStream_t st) {
+    if constexpr (A_MN || B_MN) {
+        switch (scale_mode) {
+        case 2:
+            hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, 64, 4, 2, false, A_MN, B_MN>),
+                               dim3(grid), dim3(kPPThreads), 0, st, a);
+            break;
+        case 1:
+            hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, 64, 4, 1, false, A_MN, B_MN>),
+                               dim3(grid), dim3(kPPThreads), 0, st, a);
+            break;
+        default:
+            hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, 64, 4, 0, false, A_MN, B_MN>),
+                               dim3(grid), dim3(kPPThreads), 0, st, a);
+        }
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;  // both operands K-major: the 4-wave kernels
+    }
+}
+
 // scale_mode >= 1: each fragment row's scales of a slice read as one word
 template <bool A_MN, bool B_MN>
 hipError_t launch_gemm_mx_mn(int32_t variant, int32_t out_dtype, int32_t scale_mode,
                              const GemmArgs& a, int grid, hipStream_t st) {
     const bool bf = out_dtype == 1;
     switch (variant) {
+    case V_MXPP256_K64S4:
+        return bf ? launch_mx_pp_mn<__bf16, A_MN, B_MN>(scale_mode, a, grid, st)
+                  : launch_mx_pp_mn<float, A_MN, B_MN>(scale_mode, a, grid, st);
     case V_MX256x128:
         return bf ? by_scale_mode<__bf16, 256, 128, A_MN, B_MN>(scale_mode, a, grid, st)
                   : by_scale_mode<float, 256, 128, A_MN, B_MN>(scale_mode, a, grid, st);

@@ -46,7 +46,13 @@ constexpr int kPPThreads = 512;  // eight waves
 // pieces (K a multiple of 512, 16-byte-aligned arrays).
 // COPY_IN_MFMA moves a wave's operand copies from its memory half into its
 // MFMA half, one after every second MFMA (S >= 3 only).
-template <class Op, typename TOut, int UNIT_K, int S, int SCALE_MODE = 0, bool COPY_IN_MFMA = false>
+// A_MN (B_MN): MXFP8 A stored M-major (B N-major), K rows of lda (ldb)
+// bytes; the stage then holds the unit's 64 k rows of the tile's 256 values,
+// read with ds_read_b64_tr_b8 as in the 4-wave kernel, and the K-major
+// operand's rows are lda (ldb) bytes apart.  Every DMA is then issued as
+// inline assembly (see copy16_to_lds_asm).
+template <class Op, typename TOut, int UNIT_K, int S, int SCALE_MODE = 0, bool COPY_IN_MFMA = false,
+          bool A_MN = false, bool B_MN = false>
 __global__ __launch_bounds__(kPPThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256;
@@ -114,6 +120,9 @@ void pingpong_gemm_kernel(GemmArgs p) {
     static_assert(!SC_CHUNK || UPC * KSTEPS == 8, "8 packed scale bytes per lane per chunk");
     static_assert(!SC_CHUNK || UPC >= 2, "a chunk lands two halves after its DMA");
     static_assert(FP6 || (32 >> SWZ) % CPR == 0, "swizzle depends on the row within 32 only");
+    constexpr bool ANY_MN = A_MN || B_MN;
+    static_assert(!ANY_MN || (EBITS == 8 && Op::kScaled && BK == 64 && S >= 3 && !COPY_IN_MFMA),
+                  "M/N-major operands: MXFP8, 64-deep units, copies shared by both groups");
 
     __shared__ __attribute__((aligned(1024))) char lds[RING + 8 * STG_BYTES];
 
@@ -130,6 +139,10 @@ void pingpong_gemm_kernel(GemmArgs p) {
     const int T = my_tiles * p.ksteps;  // K units of this workgroup
     const int K = p.K;
     const uint32_t ROWB = (uint32_t)K * EBITS / 8;  // bytes of a whole operand row
+    // row strides of the stored operands: whole rows (K-major, dense) or the
+    // leading dimensions (kernels with an M/N-major operand)
+    const uint32_t ROWB_A = ANY_MN ? (uint32_t)p.lda : ROWB;
+    const uint32_t ROWB_B = ANY_MN ? (uint32_t)p.ldb : ROWB;
 
     auto locate = [&](TileCursor& c) { tile_coords(p, c.tl * G + lid, c.batch, c.tm, c.tn); };
     auto advance = [&](TileCursor& c) {
@@ -160,6 +173,24 @@ void pingpong_gemm_kernel(GemmArgs p) {
         const int qq = q < A_COPIES ? q : q - A_COPIES;
         return (uint32_t)(qq * RPC) * ROWB;
     };
+    // M/N-major operand (256-byte k rows, 16 chunks): copy qq fills k rows
+    // 4 qq .. 4 qq + 3; lane l writes physical chunk l % 16 of k row
+    // 4 qq + l / 16, holding logical chunk (l % 16) ^ 2 (k % 8).  A wave's
+    // copies all have qq of its own parity, so k % 8 = 4 (cw % 2) + l / 16
+    // and one lane offset serves every copy.
+    const int mn_k = 4 * (cw & 1) + lane / 16;
+    const int mn_lc = (lane % 16) ^ (2 * (mn_k & 7));
+    auto mn_lane_off = [&](uint32_t ld) -> uint32_t {
+        return (uint32_t)(lane / 16) * ld + (uint32_t)mn_lc * 16;
+    };
+    auto mn_row_off = [&](int t, uint32_t ld) -> uint32_t {
+        const int q = cw + t * NCW;
+        const int qq = q < A_COPIES ? q : q - A_COPIES;
+        return (uint32_t)(4 * qq) * ld;
+    };
+    // K-major operand of a kernel with an M/N-major one: rows ld apart
+    const uint32_t kmaj_lane_off_a = (uint32_t)cp_row * ROWB_A + cp_chunk * 16;
+    const uint32_t kmaj_lane_off_b = (uint32_t)cp_row * ROWB_B + cp_chunk * 16;
     // FP6: copy t fills chunk Qo = 64 qq + lane of its operand region (qq the
     // copy's index within A or B): row 16 (Qo / 48) + Qo % 16, chunk
     // (Qo % 48) / 16.  The pattern has no uniform step, so each copy keeps
@@ -184,6 +215,28 @@ void pingpong_gemm_kernel(GemmArgs p) {
     auto feed_resources = [&]() {
         const int rows_a = min(BM, p.M - fc.tm * BM);
         const int rows_b = min(BN, p.N - fc.tn * BN);
+        if constexpr (ANY_MN) {
+            // M/N-major: base at the tile's first column, records up to the
+            // last k row's last 16-byte piece holding a valid column, so k
+            // rows past K read as zeros (ld is a multiple of 16); K-major:
+            // the tile's rows of ld bytes
+            const char* abase = (const char*)p.A + fc.batch * p.stride_a;
+            const char* bbase = (const char*)p.B + fc.batch * p.stride_b;
+            auto mn_records = [&](int rows, uint32_t ld) -> uint32_t {
+                return K > 0 ? (uint32_t)(K - 1) * ld + (uint32_t)((rows + 15) & ~15) : 0u;
+            };
+            ra = A_MN ? make_rsrc(abase + (int64_t)fc.tm * BM, mn_records(rows_a, ROWB_A))
+                      : make_rsrc(abase + (int64_t)fc.tm * BM * ROWB_A, (uint32_t)rows_a * ROWB_A);
+            rb = B_MN ? make_rsrc(bbase + (int64_t)fc.tn * BN, mn_records(rows_b, ROWB_B))
+                      : make_rsrc(bbase + (int64_t)fc.tn * BN * ROWB_B, (uint32_t)rows_b * ROWB_B);
+            if constexpr (SC_LDS) {
+                const uint8_t* sab = (const uint8_t*)p.SA + (int64_t)fc.tm * BM * kblocks;
+                const uint8_t* sbb = (const uint8_t*)p.SB + (int64_t)fc.tn * BN * kblocks;
+                rsa = make_rsrc(sab, (uint32_t)rows_a * (uint32_t)kblocks);
+                rsb = make_rsrc(sbb, (uint32_t)rows_b * (uint32_t)kblocks);
+            }
+            return;
+        }
         const char* abase = (const char*)p.A + fc.batch * p.stride_a + (int64_t)fc.tm * BM * ROWB;
         const char* bbase = (const char*)p.B + fc.batch * p.stride_b + (int64_t)fc.tn * BN * ROWB;
         ra = make_rsrc(abase, (uint32_t)rows_a * ROWB);
@@ -210,9 +263,11 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // wave w copies 16 blocks of A rows 64 w .. (w < 4) or of B rows 64 (w - 4) ..
     auto issue_chunk = [&]() {
         const uint32_t off = cu < T ? sc_lane_off + (uint32_t)(scc.kk * (BK / 32)) : kOutOfRange;
-        copy16_to_lds(wave < 4 ? rca : rcb, lds + S * STAGE + ((cu / UPC) & 1) * CHUNK_BYTES +
-                                                wave * 1024,
-                      off);
+        char* dst = lds + S * STAGE + ((cu / UPC) & 1) * CHUNK_BYTES + wave * 1024;
+        if constexpr (ANY_MN)
+            copy16_to_lds_asm(wave < 4 ? rca : rcb, dst, off);
+        else
+            copy16_to_lds(wave < 4 ? rca : rcb, dst, off);
         cu += UPC;
         scc.kk += UPC;
         if (scc.kk >= p.ksteps) {
@@ -238,9 +293,32 @@ void pingpong_gemm_kernel(GemmArgs p) {
         else
             return (fu < T && k0 + cp_k < K) ? cp_lane_off + (uint32_t)k0 * EBITS / 8 : kOutOfRange;
     };
+    // kernels with an M/N-major operand: the unit's offsets of A's and B's
+    // lane pieces (copy t adds its row offset)
+    auto copy_base_op = [&](bool mn, bool is_a) -> uint32_t {
+        const int k0 = fc.kk * BK;
+        const uint32_t ld = is_a ? ROWB_A : ROWB_B;
+        if (fu >= T) return kOutOfRange;
+        if (mn) return (uint32_t)k0 * ld + mn_lane_off(ld);
+        return k0 + cp_k < K ? (is_a ? kmaj_lane_off_a : kmaj_lane_off_b) + (uint32_t)k0
+                             : kOutOfRange;
+    };
     auto issue_one = [&](int t, uint32_t base) {
         const int q = cw + t * NCW;
         uint32_t off;
+        if constexpr (ANY_MN) {
+            // base unused: each operand's own base
+            const bool is_a = q < A_COPIES;
+            const bool mn = is_a ? A_MN : B_MN;
+            const uint32_t ld = is_a ? ROWB_A : ROWB_B;
+            const uint32_t b0 = copy_base_op(mn, is_a);
+            const uint32_t row = mn ? mn_row_off(t, ld)
+                                    : (uint32_t)((q < A_COPIES ? q : q - A_COPIES) * RPC) * ld;
+            off = b0 == kOutOfRange ? kOutOfRange : b0 + row;
+            copy16_to_lds_asm(is_a ? ra : rb, lds + (fu % S) * STAGE + q * 1024, off);
+            (void)base;
+            return;
+        }
         if constexpr (FP6)
             off = base != kOutOfRange && base + cb6[t] < ROWB ? base + off6[t] : kOutOfRange;
         else
@@ -254,7 +332,10 @@ void pingpong_gemm_kernel(GemmArgs p) {
             // 64 (w - 4) ..; rows past M or N read as zero
             const uint32_t word = (uint32_t)(fc.kk * (BK / 32)) & ~3u;
             const uint32_t off = fu < T ? sc_lane_off + word : kOutOfRange;
-            copy4_to_lds(wave < 4 ? rsa : rsb, st + DATA + wave * 256, off);
+            if constexpr (ANY_MN)
+                copy4_to_lds_asm(wave < 4 ? rsa : rsb, st + DATA + wave * 256, off);
+            else
+                copy4_to_lds(wave < 4 ? rsa : rsb, st + DATA + wave * 256, off);
         }
         if (++fc.kk == p.ksteps) {
             fc.kk = 0;
@@ -309,14 +390,37 @@ void pingpong_gemm_kernel(GemmArgs p) {
         }
         return f;
     };
+    // M/N-major regions (256-byte k rows): lane 16 g + t reads k row
+    // 16 (g / 2) + t / 2 (+ 0, 8, 32, 40), columns c + 16 (g % 2) + 8 (t % 2),
+    // the row's swizzle 2 (k % 8) = 2 (t / 2) folded in (see the 4-wave kernel)
+    const int g16 = lane >> 4, t16 = lane & 15;
+    auto mn_frag = [&](int col_byte) -> uint32_t {
+        return (uint32_t)((16 * (g16 >> 1) + (t16 >> 1)) * 256 + (col_byte ^ (16 * (t16 & 14))) +
+                          16 * (g16 & 1) + 8 * (t16 & 1));
+    };
+    auto read_frag_mn = [&](const char* at) -> frag_t {
+        if constexpr (ANY_MN) {
+            const i32x2_t q0 = lds_read_tr8(at), q1 = lds_read_tr8(at + 8 * 256);
+            const i32x2_t q2 = lds_read_tr8(at + 32 * 256), q3 = lds_read_tr8(at + 40 * 256);
+            const i32x4_t lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3);
+            const i32x4_t up = __builtin_shufflevector(q2, q3, 0, 1, 2, 3);
+            return __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            return frag_t{};
+        }
+    };
     auto read_unit = [&](int u) {
         const char* st = lds + (u % S) * STAGE;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) fa[s][i] = read_frag(st + a_frag + i * FRAG_STRIDE, s);
+            for (int i = 0; i < FM; ++i)
+                fa[s][i] = A_MN ? read_frag_mn(st + mn_frag(grp * WTM + 32 * i))
+                                : read_frag(st + a_frag + i * FRAG_STRIDE, s);
 #pragma unroll
-            for (int jj = 0; jj < FN; ++jj) fb[s][jj] = read_frag(st + b_frag + jj * FRAG_STRIDE, s);
+            for (int jj = 0; jj < FN; ++jj)
+                fb[s][jj] = B_MN ? read_frag_mn(st + A_BYTES + mn_frag(sub * WTN + 32 * jj))
+                                 : read_frag(st + b_frag + jj * FRAG_STRIDE, s);
         }
     };
 

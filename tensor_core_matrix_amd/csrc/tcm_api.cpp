@@ -247,14 +247,23 @@ int32_t nv4_variant(int64_t M, int64_t N, bool wide, int cus) {
     return v;
 }
 
-// MXFP8 in other arrangements: 256 x 128 tiles where they fill the CUs with
-// little padding, else 128 x 128.
-int32_t mx_mn_variant(int64_t M, int64_t N, int cus) {
-    const int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
-    const double fill = double(M) * N / (double(tiles) * 256 * 128);
-    int32_t v = tiles >= cus && fill >= 0.9 ? V_MX256x128 : V_MX128x128;
+// MXFP8 in other arrangements.  With an M/N-major operand, dense output
+// rows and every k row's offset within 32 bits (K * ld), the ping-pong
+// kernel's 256 x 256 tiles where they fill the CUs; otherwise the 4-wave
+// kernel's 256 x 128 tiles where they do, else 128 x 128.
+int32_t mx_mn_variant(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldo,
+                      bool any_mn, int cus) {
+    auto fills = [&](int64_t tm, int64_t tn) {
+        const int64_t tiles = cdiv(M, tm) * cdiv(N, tn);
+        return tiles >= cus && double(M) * N / (double(tiles) * tm * tn) >= 0.9;
+    };
+    const int64_t lim = (int64_t(1) << 31) - 256;
+    const bool pp = any_mn && ldo == N && K * lda < lim && K * ldb < lim;
+    int32_t v = pp && fills(256, 256) ? V_MXPP256_K64S4
+                : fills(256, 128)     ? V_MX256x128
+                                      : V_MX128x128;
     const int32_t f = forced_variant();
-    if (f == V_MX256x128 || f == V_MX128x128) v = f;
+    if (f == V_MX256x128 || f == V_MX128x128 || (pp && f == V_MXPP256_K64S4)) v = f;
     return v;
 }
 
@@ -443,7 +452,7 @@ tcm_status tcm_gemm_mx(const void* A, tcm_order a_order, int64_t lda, const void
         return run_mx(8, A, B, scale_A, scale_B, Out, M, N, K, out_dtype, stream);
     DeviceInfo dev;
     if ((s = device_info(&dev)) != TCM_OK) return s;
-    const int32_t v = mx_mn_variant(M, N, dev.cus);
+    const int32_t v = mx_mn_variant(M, N, K, lda, ldb, ldo, a_mn || b_mn, dev.cus);
     tcm_plan plan;
     GemmArgs a;
     plan_variant(v, 1, M, N, K, dev.cus, &plan, &a);
@@ -455,10 +464,13 @@ tcm_status tcm_gemm_mx(const void* A, tcm_order a_order, int64_t lda, const void
     a.lda = (int32_t)lda;
     a.ldb = (int32_t)ldb;
     a.ldc = (int32_t)ldo;
-    // each fragment row's four scale bytes of a 128-deep slice as one word
-    // when they are whole words
+    // scale rows read as 16-byte pieces (ping-pong kernel, K % 512 == 0,
+    // 16-byte aligned arrays) or as words (K % 128 == 0, word-aligned), else
+    // byte by byte; the 4-wave kernels read words in modes 1 and 2
     const uintptr_t sa = reinterpret_cast<uintptr_t>(scale_A), sb = reinterpret_cast<uintptr_t>(scale_B);
-    const int32_t scale_mode = K > 0 && K % 128 == 0 && ((sa | sb) & 3u) == 0 ? 1 : 0;
+    const int32_t scale_mode = K > 0 && K % 512 == 0 && ((sa | sb) & 15u) == 0 ? 2
+                               : K > 0 && K % 128 == 0 && ((sa | sb) & 3u) == 0 ? 1
+                                                                                : 0;
     const int32_t od = (int32_t)out_dtype;
     const hipStream_t st = (hipStream_t)stream;
     hipError_t e;
@@ -615,7 +627,10 @@ tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dty
         plan_variant(nv4_variant(m1, n1, K > 0 && K % 256 == 0, num_cus), b1, m1, n1, K, num_cus,
                      plan, nullptr);
     else if (mx == 5)
-        plan_variant(mx_mn_variant(m1, n1, num_cus), b1, m1, n1, K, num_cus, plan, nullptr);
+        // (dense storage: leading dimensions M and N rounded to 16, ldo = N)
+        plan_variant(mx_mn_variant(m1, n1, K, (m1 + 15) / 16 * 16, (n1 + 15) / 16 * 16, n1, true,
+                                   num_cus),
+                     b1, m1, n1, K, num_cus, plan, nullptr);
     else
         make_plan(b1, m1, n1, K, mx == 3 ? 6 : mx == 2 ? 4 : mx ? 8 : 16, num_cus, plan, nullptr);
     if (empty) {

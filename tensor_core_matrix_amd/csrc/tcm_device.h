@@ -69,6 +69,17 @@ __device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, TCM_LDS_PTR(lds_wave_base), 4, voffset, 0, 0, 0);
 }
 
+// The 4-byte copy as inline assembly, for the same kernels as
+// copy16_to_lds_asm.
+__device__ __forceinline__ void copy4_to_lds_asm(__amdgpu_buffer_rsrc_t r, void* lds_wave_base,
+                                                 uint32_t voffset) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_wave_base;
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(r), "{m0}"(m0)
+                 : "memory");
+}
+
 // Transposing 8-byte LDS read of 16-bit elements (ds_read_b64_tr_b16).  The
 // lanes act in groups of 16; within a group, lane t addresses 8 bytes (4
 // elements), the group's 16 addresses forming a 4 x 16 block whose row r is

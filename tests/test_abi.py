@@ -190,8 +190,12 @@ def test_plans_of_the_workloads():
     assert tcm.plan(1024, 1024, 1024, mx=4, out_dtype=tcm.F16)["kernel"] == 25
     # MXFP8 with an M- or N-major operand: 256 x 128 x 128 tiles (variant 26),
     # 128 x 128 for problems they would not fill
+    # MXFP8 with an M- or N-major operand: the ping-pong kernel's 256 x 256
+    # tiles (variant 14) where they fill the CUs, else the 4-wave kernel's
+    # 256 x 128 (variant 26) or 128 x 128 tiles
     p = tcm.plan(8192, 8192, 8192, mx=5)
-    assert (p["tile_m"], p["tile_n"], p["tile_k"], p["kernel"]) == (256, 128, 128, 26)
+    assert (p["tile_m"], p["tile_n"], p["tile_k"], p["kernel"]) == (256, 256, 64, 14)
+    assert tcm.plan(4096, 2048, 4096, mx=5)["kernel"] == 26
     assert tcm.plan(512, 512, 512, mx=5)["kernel"] == 11
     with pytest.raises(tcm.TcmError):
         tcm.plan(64, 64, 64, mx=6)

@@ -122,6 +122,20 @@ def test_mx_arrangement_leading_dimensions_and_persistent_grid(ao, bo, variant):
     check(got, ref, s, "f32", f"ld, A {'RC'[ao]} B {'RC'[bo]}, variant {variant}")
 
 
+# the ping-pong kernel (variant 14) with an M/N-major operand, forced: K =
+# 1024 (scales by 16-byte chunks), 640 (by words), 544 (byte by byte, and a
+# 32-deep tail in the last 64-deep unit), on a persistent grid
+@pytest.mark.parametrize("K", [1024, 640, 544])
+@pytest.mark.parametrize("ao,bo", [(C, R), (C, C), (R, R)])
+def test_mx_arrangement_pingpong(ao, bo, K):
+    M, N = 600, 520
+    a, bt, sa, sb = make(M, N, K, 1370 + K + 2 * ao + bo)
+    odt = "bf16" if K == 640 else "f32"
+    with env(TCM_MAX_GRID=3, TCM_FORCE_VARIANT=14):
+        got, ref, s = run(a, bt, sa, sb, ao, bo, odt)
+    check(got, ref, s, odt, f"ping-pong, A {'RC'[ao]} B {'RC'[bo]}, K {K}")
+
+
 def test_mx_arrangement_unaligned_scales():
     """Scale tensors at odd addresses: the byte-wise scale reads."""
     M, N, K = 256, 384, 512
