@@ -909,7 +909,15 @@ void tiled_gemm_kernel(GemmArgs p) {
                 constexpr int CHK = STG_ROWB / 16;          // 16-byte chunks per staged row
                 constexpr int RPI = kWaveSize * 16 / STG_ROWB;  // rows per store instruction
                 char* stg = lds + S * STAGE + wave * STG_BYTES;
-                const int row_l = l32;                       // staged row this lane writes
+                // The lane index is taken afresh here: the per-lane LDS and
+                // row offsets below would otherwise be computed once before
+                // the tile loop and kept in registers across the K loop,
+                // which has none to spare (they were spilled, and each
+                // reload's wait also waited for the stores before it).
+                const int lane = (int)__builtin_amdgcn_mbcnt_hi(
+                    ~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+                const int row_l = lane & 31;                 // staged row this lane writes
+                const int hi = lane >> 5;
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
 #pragma unroll
