@@ -224,3 +224,22 @@ def test_k_zero_general_form_is_beta_c(ao, bo):
     tcm.gemm(a, b, c.to(DEV), out, alpha=3.0, beta=-0.5, op="relu")
     torch.cuda.synchronize()
     assert torch.equal(out.cpu(), torch.relu(-0.5 * c))
+
+
+def test_workload_bf16_8192_nn():
+    """The measured workload with both operands row-major (8192^3, B stored
+    K x N) in the call the bench times, on sampled outputs, a full row and a
+    full column."""
+    w = inp.WORKLOADS["bf16_8192_nn"]
+    x = inp.make(w)
+    out = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=DEV)
+    tcm.gemm(x["A"].to(DEV), x["B"].to(DEV), out=out)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    a, b = inp.raw(x["A"]), inp.raw(x["B"])
+    rng = np.random.default_rng(w.seed)
+    ii = np.concatenate([rng.integers(0, w.M, 4096), np.full(w.N, w.M // 3), np.arange(w.M)])
+    jj = np.concatenate([rng.integers(0, w.N, 4096), np.arange(w.N), np.full(w.M, w.N - 5)])
+    ref, s = orc.entries_ld(orc.BF16, a, R, w.K, b, R, w.N, w.M, w.N, w.K, ii, jj)
+    check(got[torch.from_numpy(ii), torch.from_numpy(jj)], orc.axpby(1.0, ref), 1.0, s,
+          np.zeros_like(ref), "bf16", "bf16_8192_nn sampled, row and column")
