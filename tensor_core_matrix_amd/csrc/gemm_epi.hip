@@ -8,8 +8,10 @@ namespace tcm {
 template <class Op, typename TOut, int BM, int BN, int OCC, int NSPLIT>
 static hipError_t launch_ab(const GemmArgs& a, int grid, hipStream_t st) {
     // swizzle shift 1: 128-byte rows of 64-deep 16-bit slices
-    // separate leading dimensions for A and B
-    hipLaunchKernelGGL((tiled_gemm_kernel<Op, TOut, BM, BN, 64, 2, OCC, 1, false, NSPLIT, false,
+    // separate leading dimensions for A and B; a plain product with a 16-bit
+    // output stages its tile through LDS where one workgroup has the CU
+    constexpr bool epi = OCC == 1 && sizeof(TOut) == 2;
+    hipLaunchKernelGGL((tiled_gemm_kernel<Op, TOut, BM, BN, 64, 2, OCC, 1, false, NSPLIT, epi,
                                           false, true, false, false, false>),
                        dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();

@@ -851,8 +851,12 @@ void tiled_gemm_kernel(GemmArgs p) {
         const int n_base = c.tn * BN + wn * WTN + 4 * hi;
         const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (ldc & 3) == 0;
         if constexpr (AB && OPJ > 0) {
-            op_epilogue(c);
-            return;
+            // a plain product (alpha 1, no C, no operation) takes the 16-bit
+            // staged form below where the kernel has it
+            if (!(EPI_LDS && p.alpha == 1.0f && p.beta == 0.0f && p.op == 0)) {
+                op_epilogue(c);
+                return;
+            }
         } else if constexpr (AB) {
             // (tiles without room for the staged form: no operation)
             // Each lane reads the C values of exactly the outputs it writes,

@@ -10,7 +10,10 @@ namespace tcm {
 template <class Op, typename TOut, int BM, int BN, int OCC, int NSPLIT, bool A_MN, bool B_MN>
 static hipError_t launch_mn_one(const GemmArgs& a, int grid, hipStream_t st) {
     // swizzle shift 1: 128-byte rows of the K-major operand's 64-deep slices
-    hipLaunchKernelGGL((tiled_gemm_kernel<Op, TOut, BM, BN, 64, 2, OCC, 1, false, NSPLIT, false,
+    // a plain product with a 16-bit output stages its tile through LDS
+    // where one workgroup has the CU
+    constexpr bool epi = OCC == 1 && sizeof(TOut) == 2;
+    hipLaunchKernelGGL((tiled_gemm_kernel<Op, TOut, BM, BN, 64, 2, OCC, 1, false, NSPLIT, epi,
                                           false, true, A_MN, B_MN, false>),
                        dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
