@@ -851,9 +851,11 @@ void tiled_gemm_kernel(GemmArgs p) {
         const int n_base = c.tn * BN + wn * WTN + 4 * hi;
         const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N && (ldc & 3) == 0;
         if constexpr (AB && OPJ > 0) {
-            // a plain product (alpha 1, no C, no operation) takes the 16-bit
-            // staged form below where the kernel has it
-            if (!(EPI_LDS && p.alpha == 1.0f && p.beta == 0.0f && p.op == 0)) {
+            // an interior tile of a product without C or operation takes the
+            // 16-bit staged form below (alpha applied there) where the kernel
+            // has it; every other tile keeps the alpha/beta epilogue
+            if (!(EPI_LDS && p.beta == 0.0f && p.op == 0 && full &&
+                  (ldc * (int)sizeof(TOut)) % 16 == 0)) {
                 op_epilogue(c);
                 return;
             }
@@ -922,6 +924,8 @@ void tiled_gemm_kernel(GemmArgs p) {
                     ~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
                 const int row_l = lane & 31;                 // staged row this lane writes
                 const int hi = lane >> 5;
+                // alpha of the C-input kernels (1 elsewhere: the product alone)
+                const float al = AB ? p.alpha : 1.0f;
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -933,8 +937,8 @@ void tiled_gemm_kernel(GemmArgs p) {
                             const int byte = col * (int)sizeof(TOut);
                             const int chunk = (byte / 16) ^ (row_l & (CHK - 1));
                             char* dst = stg + row_l * STG_ROWB + chunk * 16 + byte % 16;
-                            store4<TOut>((TOut*)dst, a4[4 * q], a4[4 * q + 1], a4[4 * q + 2],
-                                         a4[4 * q + 3]);
+                            store4<TOut>((TOut*)dst, al * a4[4 * q], al * a4[4 * q + 1],
+                                         al * a4[4 * q + 2], al * a4[4 * q + 3]);
                         }
                     // same-wave LDS writes then reads: the wave's own order holds
                     wave_lds_exchange();

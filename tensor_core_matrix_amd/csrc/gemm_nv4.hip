@@ -8,8 +8,10 @@ namespace tcm {
 
 template <typename TOut, int BM, int BN, int OCC, int NSPLIT, bool WIDE>
 static hipError_t launch_nv4(const GemmArgs& a, int grid, hipStream_t st) {
-    // swizzle shift 1: 128-byte fp16 rows of 64-deep slices
-    hipLaunchKernelGGL((tiled_gemm_kernel<OpNVFP4<WIDE>, TOut, BM, BN, 64, 2, OCC, 1, false, NSPLIT, false,
+    // swizzle shift 1: 128-byte fp16 rows of 64-deep slices; a 16-bit output
+    // is staged through LDS where one workgroup has the CU
+    constexpr bool epi = OCC == 1 && sizeof(TOut) == 2;
+    hipLaunchKernelGGL((tiled_gemm_kernel<OpNVFP4<WIDE>, TOut, BM, BN, 64, 2, OCC, 1, false, NSPLIT, epi,
                                           true, true, false, false, false>),
                        dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
