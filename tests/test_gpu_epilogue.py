@@ -102,17 +102,35 @@ def test_exact_quarter_integers():
     assert np.array_equal(got, ex)
 
 
-def test_large_sampled():
+def test_large_full_output():
+    """4096^3 with a bf16 C, every output against the oracle."""
     M = N = K = 4096
     g = inp.generator(740)
     a = inp.normal((M, K), g, 0.1, torch.bfloat16)
     b = inp.normal((N, K), g, 0.1, torch.bfloat16)
     c = inp.normal((M, N), g, 1.0, torch.bfloat16)
     out = run(a, b, c, 1.5, 0.25, "bf16")
-    rng = np.random.default_rng(740)
-    ii, jj = rng.integers(0, M, 2048), rng.integers(0, N, 2048)
-    ref, s = orc.entries(orc.BF16, inp.raw(a), inp.raw(b), ii, jj)
-    cs = c[torch.from_numpy(ii), torch.from_numpy(jj)]
-    ex = orc.axpby(1.5, ref, 0.25, inp.raw(cs), orc.BF16)
-    check(out[torch.from_numpy(ii), torch.from_numpy(jj)], ex, 1.5, s, 0.25 * cs.double().numpy(),
-          "bf16", "4096 sampled")
+    ref, s = orc.gemm_tn(orc.BF16, inp.raw(a), inp.raw(b))
+    ex = orc.axpby(1.5, ref, 0.25, inp.raw(c), orc.BF16)
+    check(out, ex, 1.5, s, 0.25 * c.double().numpy(), "bf16", "4096 full")
+
+
+@pytest.mark.parametrize("variant", [19, 1])
+@pytest.mark.parametrize("odt", ["bf16", "f16"])
+@pytest.mark.parametrize("grid", [None, 3])
+def test_staged_alpha_epilogue(variant, odt, grid, monkeypatch):
+    """alpha != 1 without C on the tiles that stage a 16-bit output through
+    LDS (256 x 256 and 128 x 256): N a multiple of 8 makes every interior
+    tile take the staged form, alpha applied as it is staged, while the
+    ragged last tile row (M = 777) keeps the alpha/beta epilogue.  Every
+    output against the oracle."""
+    monkeypatch.setenv("TCM_FORCE_VARIANT", str(variant))
+    if grid:
+        monkeypatch.setenv("TCM_MAX_GRID", str(grid))
+    M, N, K = 777, 648, 520
+    g = inp.generator(760 + variant)
+    a = inp.normal((M, K), g, 0.5, torch.bfloat16)
+    b = inp.normal((N, K), g, 0.5, torch.bfloat16)
+    ex, s, bc = expect(a, b, None, -0.75, 0.0, "bf16")
+    check(run(a, b, None, -0.75, 0.0, odt), ex, -0.75, s, bc, odt,
+          f"variant {variant} {odt} grid {grid}")

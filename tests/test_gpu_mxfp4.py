@@ -95,19 +95,3 @@ def test_mxfp4_scale_reaches_only_its_block():
     ref, _ = orc.gemm_mx(inp.raw(a), inp.raw(b), inp.raw(sa2), inp.raw(sb), dtype=orc.E2M1)
     assert np.array_equal(got, ref)
     assert np.array_equal(np.delete(got, 5, 0), np.delete(base, 5, 0))
-
-
-def test_workload_mxfp4():
-    w = inp.WORKLOADS["mxfp4_8192"]
-    x = inp.make(w)
-    out = run_fp4(x["A"], x["B"], x["SA"], x["SB"], "bf16")
-    rng = np.random.default_rng(w.seed)
-    ii = np.concatenate([rng.integers(0, w.M, 4096), [0, w.M - 1, 0, w.M - 1]])
-    jj = np.concatenate([rng.integers(0, w.N, 4096), [0, 0, w.N - 1, w.N - 1]])
-    ref, s = orc.entries(orc.E2M1, inp.raw(x["A"]), inp.raw(x["B"]), ii, jj,
-                         sa=inp.raw(x["SA"]), sb=inp.raw(x["SB"]))
-    check(out[torch.from_numpy(ii), torch.from_numpy(jj)], ref, s, "bf16", "mxfp4 8192")
-    r = 5001
-    ref, s = orc.entries(orc.E2M1, inp.raw(x["A"]), inp.raw(x["B"]), np.full(w.N, r),
-                         np.arange(w.N), sa=inp.raw(x["SA"]), sb=inp.raw(x["SB"]))
-    check(out[r], ref, s, "bf16", "mxfp4 8192 row")

@@ -96,16 +96,3 @@ def test_mxfp6_scale_reaches_only_its_block():
     ref, _ = oracle(a, b, sa2, sb, "e2m3")
     assert np.array_equal(got, ref)
     assert np.array_equal(np.delete(got, 5, 0), np.delete(base, 5, 0))
-
-
-def test_workload_mxfp6():
-    w = inp.WORKLOADS["mxfp6_8192"]
-    x = inp.make(w)
-    out = run_fp6(x["A"], x["B"], x["SA"], x["SB"], "bf16", w.dtype)
-    rng = np.random.default_rng(w.seed)
-    ii = np.concatenate([rng.integers(0, w.M, 4096), [0, w.M - 1, 0, w.M - 1]])
-    jj = np.concatenate([rng.integers(0, w.N, 4096), [0, 0, w.N - 1, w.N - 1]])
-    dt = orc.DTYPE_NAMES[w.dtype]
-    ref, s = orc.entries(dt, inp.raw(x["A"]), inp.raw(x["B"]), ii, jj,
-                         sa=inp.raw(x["SA"]), sb=inp.raw(x["SB"]))
-    check(out[torch.from_numpy(ii), torch.from_numpy(jj)], ref, s, "bf16", "mxfp6 8192")

@@ -135,14 +135,21 @@ def test_nvfp4_block_scale_reaches_only_its_16():
     assert np.array_equal(np.delete(got, 5, 0), np.delete(base, 5, 0))
 
 
-def test_workload_nvfp4():
-    w = inp.WORKLOADS["nvfp4_8192"]
-    x = inp.make(w)
-    ga, gb = w.globals
-    out = run(x["A"], x["B"], x["SA"], x["SB"], ga, gb, "bf16")
-    rng = np.random.default_rng(w.seed)
-    ii = np.concatenate([rng.integers(0, w.M, 4096), [0, w.M - 1, 0, w.M - 1]])
-    jj = np.concatenate([rng.integers(0, w.N, 4096), [0, 0, w.N - 1, w.N - 1]])
-    ref, s = orc.entries_nvfp4(inp.raw(x["A"]), inp.raw(x["B"]), inp.raw(x["SA"]),
-                               inp.raw(x["SB"]), ga, gb, ii, jj)
-    check(out[torch.from_numpy(ii), torch.from_numpy(jj)], ref, s, "bf16", "nvfp4 8192")
+@pytest.mark.parametrize("variant", [22, 24])
+@pytest.mark.parametrize("odt", ["bf16", "f16"])
+def test_nvfp4_staged_epilogue(variant, odt):
+    """The 256 x 256 NVFP4 kernels with N a multiple of 8: interior tiles stage
+    their 16-bit output through LDS with alpha = gA gB applied as it is
+    staged; the ragged last tile row takes the alpha/beta epilogue.  Every
+    output against the oracle, with and without a persistent grid."""
+    M, N, K = 777, 648, 768
+    a, b, sa, sb = make(M, N, K, 1250 + variant)
+    ga, gb = (2.0, 0.75) if odt == "bf16" else (0.03, -0.17)
+    ref, s = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), ga, gb)
+    for grid in (None, 3):
+        kv = {"TCM_FORCE_VARIANT": variant}
+        if grid:
+            kv["TCM_MAX_GRID"] = grid
+        with env(**kv):
+            got = run(a, b, sa, sb, ga, gb, odt)
+        check(got, ref, s, odt, f"variant {variant} {odt} grid {grid}")
