@@ -58,6 +58,14 @@
 extern "C" {
 #endif
 
+/* Result of every call: TCM_OK or the reason the call was refused.  This is
+ * the error-or-value form of "API Card: Blackwell Pipeline (tcgen05)", Host
+ * side., whose pipeline builder returns either a usable pipeline or an error
+ * (one of them that a misaligned operand was given, the card's
+ * alignment_unfulfilled, here TCM_ERR_MISALIGNED); unlike the card's
+ * Descriptor. gates, a request the fast path cannot take is never served by
+ * another algorithm but refused with one of these codes.  Ownership: a plain
+ * value; nothing to free. */
 typedef enum tcm_status {
     TCM_OK = 0,
     TCM_ERR_NULL_POINTER = 1,      /* a required pointer is NULL */
@@ -292,7 +300,12 @@ typedef struct tcm_plan {
 tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,
                          tcm_dtype out_dtype, int mx, int num_cus, tcm_plan* plan);
 
-/* Static, human-readable name of a status code (never NULL). */
+/* Static, human-readable name of a status code, the counterpart of the error
+ * string lookup of "API Card: Blackwell Pipeline (tcgen05)", Host side.
+ * (which names the card's error values, alignment_unfulfilled among them).
+ * Codes outside the enumeration give "TCM_ERR_UNKNOWN: unknown status code".  The string is
+ * static and owned by the library (never NULL, never freed by the caller);
+ * the call touches no device and is thread-safe. */
 const char* tcm_status_string(tcm_status s);
 
 #ifdef __cplusplus

@@ -44,28 +44,35 @@ _PACK = {E2M1: (2, 1), E2M3: (4, 3), E3M2: (4, 3)}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+# ORACLE_LIBRARY names another build of oracle.c (the sanitizer build below)
+_USE = os.environ.get("ORACLE_LIBRARY")
 _lock = threading.Lock()
 _lib = None
 
 
-def build(force: bool = True) -> str:
+def build(force: bool = True, sanitize: bool = False) -> str:
     """Compile oracle.c into liboracle.so beside it (gcc, -O2, no fast-math so
-    the fp64 sums keep their sequential order)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+    the fp64 sums keep their sequential order).  sanitize: liboracle_san.so,
+    the same with AddressSanitizer and UndefinedBehaviorSanitizer, for CPU
+    runs of the oracle's tests (load it with ORACLE_LIBRARY and libasan
+    preloaded)."""
+    lib = _SAN_LIB if sanitize else _LIB
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC):
+        tmp = lib + ".tmp%d" % os.getpid()
+        san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g"] if sanitize else []
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra",
-             "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+             "-fno-fast-math", "-ffp-contract=off", *san, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build(force=False)
-            lib = ctypes.CDLL(_LIB)
+            lib = ctypes.CDLL(_USE) if _USE else ctypes.CDLL(build(force=False))
             i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
             lib.oracle_decode.argtypes = [ctypes.c_int, vp, i64, dp]
             lib.oracle_gemm_tn.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, i64, dp, dp,

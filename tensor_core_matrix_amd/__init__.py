@@ -33,7 +33,11 @@ __all__ = ["gemm", "gemm_tn", "gemm_tn_ex", "batched_gemm_tn", "gemm_mx_fp8", "g
            "LIB_PATH", "F16", "BF16", "F32", "E4M3", "E8M0", "E2M1", "E2M3", "E3M2", "ROW_MAJOR",
            "COL_MAJOR", "OPS"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtcm.so")
+# TCM_LIBRARY names another build of the same library (the host-sanitizer
+# build of `python -m tensor_core_matrix_amd.build --sanitize`); by default
+# the in-tree libtcm.so.
+LIB_PATH = os.environ.get("TCM_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libtcm.so")
 
 # tcm_dtype codes
 F16, BF16, F32, E4M3, E8M0, E2M1, E2M3, E3M2 = 0, 1, 2, 3, 4, 5, 6, 7

@@ -855,7 +855,7 @@ void tiled_gemm_kernel(GemmArgs p) {
             // 16-bit staged form below (alpha applied there) where the kernel
             // has it; every other tile keeps the alpha/beta epilogue
             if (!(EPI_LDS && p.beta == 0.0f && p.op == 0 && full &&
-                  (ldc * (int)sizeof(TOut)) % 16 == 0)) {
+                  ldc % (16 / (int)sizeof(TOut)) == 0)) {
                 op_epilogue(c);
                 return;
             }
@@ -911,7 +911,7 @@ void tiled_gemm_kernel(GemmArgs p) {
             // read back as 16-byte row pieces, and stored so that every store
             // instruction writes whole 256-byte row segments (4 rows for
             // bf16, 2 for fp32) instead of 16-byte pieces of 32 rows.
-            if (full && (ldc * (int)sizeof(TOut)) % 16 == 0) {
+            if (full && ldc % (16 / (int)sizeof(TOut)) == 0) {
                 constexpr int CHK = STG_ROWB / 16;          // 16-byte chunks per staged row
                 constexpr int RPI = kWaveSize * 16 / STG_ROWB;  // rows per store instruction
                 char* stg = lds + S * STAGE + wave * STG_BYTES;

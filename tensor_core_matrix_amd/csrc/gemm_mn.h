@@ -10,8 +10,11 @@ namespace tcm {
 template <class Op, typename TOut, int BM, int BN, int OCC, int NSPLIT, bool A_MN, bool B_MN>
 static hipError_t launch_mn_one(const GemmArgs& a, int grid, hipStream_t st) {
     // swizzle shift 1: 128-byte rows of the K-major operand's 64-deep slices
-    // a plain product with a 16-bit output stages its tile through LDS
-    // where one workgroup has the CU
+    // where one workgroup has the CU and the output is 16-bit, every
+    // interior tile without a C input (beta = 0) or an operation stages its
+    // output through LDS, alpha applied as the accumulators are staged;
+    // edge tiles and calls with a C input or an operation take the
+    // alpha/beta epilogue
     constexpr bool epi = OCC == 1 && sizeof(TOut) == 2;
     hipLaunchKernelGGL((tiled_gemm_kernel<Op, TOut, BM, BN, 64, 2, OCC, 1, false, NSPLIT, epi,
                                           false, true, A_MN, B_MN, false>),

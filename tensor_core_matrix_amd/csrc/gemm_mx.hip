@@ -8,18 +8,18 @@ namespace tcm {
 // together by 16 lanes hit 16 different 16-byte bank groups.
 constexpr int kSwizzle8 = 1;
 
-template <typename TOut, int BM, int BN, bool WORDS, int NSPLIT = 1>
+template <typename TOut, int BM, int BN, bool WORDS>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     constexpr bool epi = 2 * (BM + BN) * 128 + 4 * 32 * (BN / 2) * (int)sizeof(TOut) <= 160 * 1024;
     hipLaunchKernelGGL(
-        (tiled_gemm_kernel<OpMXFP8, TOut, BM, BN, 128, 2, 1, kSwizzle8, WORDS, NSPLIT, epi>),
+        (tiled_gemm_kernel<OpMXFP8, TOut, BM, BN, 128, 2, 1, kSwizzle8, WORDS, 1, epi>),
         dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
-template <typename TOut, int MODE, int UNIT_K, int S, bool CM = false, class Op = OpMXFP8>
+template <typename TOut, int MODE, int UNIT_K, int S, class Op = OpMXFP8>
 static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((pingpong_gemm_kernel<Op, TOut, UNIT_K, S, MODE, CM && MODE != 1>),
+    hipLaunchKernelGGL((pingpong_gemm_kernel<Op, TOut, UNIT_K, S, MODE>),
                        dim3(grid), dim3(kPPThreads), 0, st, a);
     return hipGetLastError();
 }
@@ -30,13 +30,9 @@ template <typename TOut, int MODE>
 static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t st) {
     constexpr bool WORDS = MODE >= 1;
     switch (v) {
-    case V_MX256x256: return launch_one<TOut, 256, 256, WORDS>(a, grid, st);
     case V_MX128x128: return launch_one<TOut, 128, 128, WORDS>(a, grid, st);
-    case V_MX256x256_SPLIT2: return launch_one<TOut, 256, 256, WORDS, 2>(a, grid, st);
-    case V_MXPP256: return launch_pp<TOut, MODE, 128, 2>(a, grid, st);
     case V_MXPP256_K64S4: return launch_pp<TOut, MODE, 64, 4>(a, grid, st);
-    case V_MXPP256_K64S4_CM: return launch_pp<TOut, MODE, 64, 4, true>(a, grid, st);
-    case V_MX4PP256: return launch_pp<TOut, MODE, 128, 4, false, OpMXFP4>(a, grid, st);
+    case V_MX4PP256: return launch_pp<TOut, MODE, 128, 4, OpMXFP4>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

@@ -6,7 +6,7 @@ namespace tcm {
 
 template <typename TOut, int MODE, int FMT, int UNIT_K, int S>
 static hipError_t launch6(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP6<FMT>, TOut, UNIT_K, S, MODE, false>),
+    hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP6<FMT>, TOut, UNIT_K, S, MODE>),
                        dim3(grid), dim3(kPPThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -36,15 +36,15 @@ static hipError_t launch_mx_pp_mn(int32_t scale_mode, const GemmArgs& a, int gri
     if constexpr (A_MN || B_MN) {
         switch (scale_mode) {
         case 2:
-            hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, 64, 4, 2, false, A_MN, B_MN>),
+            hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, 64, 4, 2, A_MN, B_MN>),
                                dim3(grid), dim3(kPPThreads), 0, st, a);
             break;
         case 1:
-            hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, 64, 4, 1, false, A_MN, B_MN>),
+            hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, 64, 4, 1, A_MN, B_MN>),
                                dim3(grid), dim3(kPPThreads), 0, st, a);
             break;
         default:
-            hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, 64, 4, 0, false, A_MN, B_MN>),
+            hipLaunchKernelGGL((pingpong_gemm_kernel<OpMXFP8, TOut, 64, 4, 0, A_MN, B_MN>),
                                dim3(grid), dim3(kPPThreads), 0, st, a);
         }
         return hipGetLastError();

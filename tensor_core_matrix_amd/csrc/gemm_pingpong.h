@@ -19,13 +19,15 @@
 //    nothing but MFMAs, so the stalls of reads and copies (LDS latency, full
 //    address FIFOs) fall on the other wave and the matrix core of each SIMD
 //    stays busy.
-//  * An S-stage LDS ring of units.  Unit v is read in halves 2v-1 and 2v, so
-//    its stage is free from half 2v+1 on; the copies of unit v+S into it are
-//    issued in the memory halves of unit v+1 (both groups sharing them when
-//    S >= 3, group 0 alone when S = 2) and waited for by their issuing waves
-//    just before the barrier that precedes the first read of unit v+S.  With
-//    S = 4 a copy has four half-periods to land and each memory half issues
-//    a quarter of what a two-stage ring would need in one.
+//  * An S-stage LDS ring of units (S >= 3).  Unit v is read in halves 2v-1
+//    and 2v, so its stage is free from half 2v+1 on; the copies of unit v+S
+//    into it are issued in the memory halves of unit v+1, shared by both
+//    groups, and waited for by their issuing waves just before the barrier
+//    that precedes the first read of unit v+S.  With S = 4 a copy has four
+//    half-periods to land and each memory half issues a quarter of what a
+//    two-stage ring would need in one.  (A two-stage ring, with group 0
+//    alone copying because group 1's share would have to land within the
+//    half it is issued in, measured far slower.)
 //  * The epilogue of a tile runs in each wave's memory half right after its
 //    last MFMA half -- while the other group computes -- staged through a
 //    wave-private LDS area so that every store writes whole row segments.
@@ -44,15 +46,13 @@ constexpr int kPPThreads = 512;  // eight waves
 // SCALE_MODE (MX only) says how the E8M0 rows may be read: 0 byte by byte,
 // 1 as 32-bit words (K a multiple of 128, word-aligned arrays), 2 as 16-byte
 // pieces (K a multiple of 512, 16-byte-aligned arrays).
-// COPY_IN_MFMA moves a wave's operand copies from its memory half into its
-// MFMA half, one after every second MFMA (S >= 3 only).
 // A_MN (B_MN): MXFP8 A stored M-major (B N-major), K rows of lda (ldb)
 // bytes; the stage then holds the unit's 64 k rows of the tile's 256 values,
 // read with ds_read_b64_tr_b8 as in the 4-wave kernel, and the K-major
 // operand's rows are lda (ldb) bytes apart.  Every DMA is then issued as
 // inline assembly (see copy16_to_lds_asm).
-template <class Op, typename TOut, int UNIT_K, int S, int SCALE_MODE = 0, bool COPY_IN_MFMA = false,
-          bool A_MN = false, bool B_MN = false>
+template <class Op, typename TOut, int UNIT_K, int S, int SCALE_MODE = 0, bool A_MN = false,
+          bool B_MN = false>
 __global__ __launch_bounds__(kPPThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int BM = 256, BN = 256;
@@ -79,8 +79,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // row, the 4 blocks that hold the unit's blocks.  A DMA lane touches one
     // row, so fewer, wider pieces keep the address unit free for operands.
     constexpr bool SCALE_WORDS = SCALE_MODE >= 1;
-    constexpr bool SC_CHUNK = Op::kScaled && SCALE_MODE == 2 && S >= 3;
-    constexpr bool SC_LDS = Op::kScaled && SCALE_MODE == 1 && S >= 3;
+    constexpr bool SC_CHUNK = Op::kScaled && SCALE_MODE == 2;
+    constexpr bool SC_LDS = Op::kScaled && SCALE_MODE == 1;
     constexpr int SC_BYTES = SC_LDS ? (BM + BN) * 4 : 0;
     constexpr int STAGE = DATA + SC_BYTES;
     constexpr int UPC = 16 / (BK / 32);                       // units per scale chunk
@@ -89,11 +89,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32;
     constexpr int KSTEPS = BK / Op::kK;
     constexpr int CPL = Op::kK * EBITS / 8 / 32;  // 16-byte chunks per lane per MFMA (>= 8 bits)
-    // copies: 1 KiB per wave instruction; shared by both groups when S >= 3
-    // With two stages group 1's share would have to land within the half it
-    // is issued in (measured: far slower), so group 0 copies alone.
-    constexpr int COPY_GROUPS = S >= 3 ? 2 : 1;
-    constexpr int NCW = 4 * COPY_GROUPS;               // copying waves
+    // copies: 1 KiB per wave instruction, shared by all eight waves
+    constexpr int NCW = 8;                             // copying waves
     constexpr int A_COPIES = A_BYTES / 1024;
     constexpr int PW = DATA / 1024 / NCW;              // operand copies per wave per unit
     constexpr int OPS = PW + (SC_LDS ? 1 : 0);         // DMA operations per wave per unit
@@ -113,16 +110,13 @@ void pingpong_gemm_kernel(GemmArgs p) {
     static_assert(STAGE % 1024 == 0, "stage alignment");
     static_assert(RING + 8 * STG_BYTES <= 160 * 1024, "LDS budget");
     static_assert(S * OPS < 64, "vmcnt range");
-    static_assert(!COPY_IN_MFMA || (S >= 3 && COPY_GROUPS == 2 && !SC_LDS),
-                  "copies in MFMA halves: shared copies, no per-stage scale words");
-    static_assert(!(SC_LDS || SC_CHUNK) || NCW == 8,
-                  "one scale DMA per wave: 4 x 64 A rows, 4 x 64 B rows");
+    static_assert(S >= 3, "ring of at least three units");
     static_assert(!SC_CHUNK || UPC * KSTEPS == 8, "8 packed scale bytes per lane per chunk");
     static_assert(!SC_CHUNK || UPC >= 2, "a chunk lands two halves after its DMA");
     static_assert(FP6 || (32 >> SWZ) % CPR == 0, "swizzle depends on the row within 32 only");
     constexpr bool ANY_MN = A_MN || B_MN;
-    static_assert(!ANY_MN || (EBITS == 8 && Op::kScaled && BK == 64 && S >= 3 && !COPY_IN_MFMA),
-                  "M/N-major operands: MXFP8, 64-deep units, copies shared by both groups");
+    static_assert(!ANY_MN || (EBITS == 8 && Op::kScaled && BK == 64),
+                  "M/N-major operands: MXFP8, 64-deep units");
 
     __shared__ __attribute__((aligned(1024))) char lds[RING + 8 * STG_BYTES];
 
@@ -160,7 +154,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // copies are NCW RPC apart and the swizzle repeats every CPR << SWZ rows,
     // so a lane's chunk is the same in all of them: one lane offset serves
     // every copy, and each copy adds the wave-uniform row offset RPC qq K.
-    const int cw = COPY_GROUPS == 2 ? wave : sub;
+    const int cw = wave;
     static_assert(FP6 || ((NCW * RPC) % (CPR << SWZ) == 0 && (A_COPIES * RPC) % (CPR << SWZ) == 0),
                   "chunk independent of the copy");
     const int cp_row = lane / CPR;
@@ -496,19 +490,13 @@ void pingpong_gemm_kernel(GemmArgs p) {
 
     // ---- MFMAs of one unit --------------------------------------------------------
     f32x16_t acc[FM][FN];
-    auto compute = [&](auto ZERO, auto COPY) {
+    auto compute = [&](auto ZERO) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
-                    if constexpr (decltype(COPY)::value) {
-                        constexpr int NM = KSTEPS * FM * FN;
-                        constexpr int CSTEP = NM >= 2 * PW ? 2 : 1;
-                        const int x = (s * FM + i) * FN + j;
-                        if (x % CSTEP == 0 && x / CSTEP < PW) issue_one(x / CSTEP, copy_base());
-                    }
                     f32x16_t c;
                     if constexpr (decltype(ZERO)::value) {
                         if (s == 0) c = (f32x16_t){};
@@ -527,7 +515,6 @@ void pingpong_gemm_kernel(GemmArgs p) {
                     } else {
                         acc[i][j] = Op::mma(fb[s][j], fa[s][i], c);
                     }
-                    if constexpr (decltype(COPY)::value) __builtin_amdgcn_sched_barrier(0);
                 }
     };
 
@@ -538,7 +525,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
         const int col0 = c.tn * BN + sub * WTN;
         const bool full = c.tm * BM + BM <= p.M && c.tn * BN + BN <= p.N;
         if constexpr (EPI_LDS) {
-            if (full && (p.N * (int)sizeof(TOut)) % 16 == 0) {
+            if (full && p.N % (16 / (int)sizeof(TOut)) == 0) {
                 // each block of STG_ROWS rows: MFMA layout -> staging ->
                 // whole row pieces (lane l holds row l % 32 of a 32-row block)
                 constexpr int CHK = STG_ROWB / 16;
@@ -612,12 +599,9 @@ void pingpong_gemm_kernel(GemmArgs p) {
         chunk_resources();
         issue_chunk();  // chunk 0; chunk c + 1 follows in the memory halves of unit UPC c
     }
-    const bool copier = COPY_GROUPS == 2 || grp == 0;
-    if (copier) {
 #pragma unroll
-        for (int u = 0; u < S - 1; ++u) issue();
-        wait_vmcnt<0>();
-    }
+    for (int u = 0; u < S - 1; ++u) issue();
+    wait_vmcnt<0>();
     barrier_lds();
 
     // ---- half-periods -------------------------------------------------------------
@@ -628,7 +612,6 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // u also issues this wave's copies of unit u + S - 1.
     auto run = [&](auto GROUP0) {
         constexpr bool G0 = decltype(GROUP0)::value;
-        constexpr bool COPIES = G0 || COPY_GROUPS == 2;
         TileCursor cc = {0, 0, 0, 0, 0};
         locate(cc);
         if constexpr (!G0) __builtin_amdgcn_s_barrier();  // half -1: group 0 reads unit 0
@@ -649,30 +632,26 @@ void pingpong_gemm_kernel(GemmArgs p) {
                 // groups finished reading in earlier halves
                 if (u == cu - UPC) issue_chunk();
             }
-            if constexpr (COPIES && !COPY_IN_MFMA) issue();
+            issue();
             // Waits before the barrier.  Scales loaded to registers precede
             // this half's copies, and loads return in order, so vmcnt(OPS)
             // covers them.  Group 1's copies of unit u + 1, which group 0 reads
             // in the next half, have (S - 2) * OPS operations issued after
-            // them ((S - 3) * OPS when copies go out in MFMA halves).
+            // them.
             constexpr bool REG_SCALES = Op::kScaled && !SC_LDS && !SC_CHUNK;
             if constexpr (G0) {
                 if constexpr (REG_SCALES) wait_vmcnt<OPS>();
-            } else if constexpr (S == 2) {
-                if constexpr (COPIES || REG_SCALES) wait_vmcnt<0>();
             } else if constexpr (REG_SCALES) {
                 wait_vmcnt<OPS>();
             } else {
-                wait_vmcnt<(S - (COPY_IN_MFMA ? 3 : 2)) * OPS>();
+                wait_vmcnt<(S - 2) * OPS>();
             }
             barrier_lds();
             // ---- MFMA half
-            constexpr auto CP = std::integral_constant<bool, COPIES && COPY_IN_MFMA>{};
             if (cc.kk == 0)
-                compute(std::true_type{}, CP);
+                compute(std::true_type{});
             else
-                compute(std::false_type{}, CP);
-            if constexpr (COPIES && COPY_IN_MFMA) issue_finish();
+                compute(std::false_type{});
             advance(cc);
             // group 0's share of unit u + 1 lands before its next memory half
             if constexpr (G0) wait_vmcnt<(S - 2) * OPS>();

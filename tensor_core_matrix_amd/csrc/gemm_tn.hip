@@ -1,5 +1,5 @@
 // Kernel instances and launcher for the float16 / bfloat16 TN product.
-#include "gemm_pingpong.h"
+#include "gemm_kernel.h"
 
 namespace tcm {
 
@@ -20,41 +20,22 @@ constexpr bool epilogue_fits() {
     return S * (BM + BN) * BK * 2 + 4 * 32 * (BN / 2) * (int)sizeof(TOut) <= 160 * 1024;
 }
 
-template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int NSPLIT = 1,
-          bool EPI = true, bool VG = false>
+template <class Op, typename TOut, int BM, int BN, int BK, int S, int OCC, int NSPLIT = 1>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
-    constexpr bool epi = EPI && OCC == 1 && epilogue_fits<TOut, BM, BN, BK, S>();
+    constexpr bool epi = OCC == 1 && epilogue_fits<TOut, BM, BN, BK, S>();
     hipLaunchKernelGGL(
-        (tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, swizzle_shift<BK>(), false, NSPLIT, epi,
-                           VG>),
+        (tiled_gemm_kernel<Op, TOut, BM, BN, BK, S, OCC, swizzle_shift<BK>(), false, NSPLIT, epi>),
         dim3(grid), dim3(kThreads), 0, st, a);
-    return hipGetLastError();
-}
-
-template <class Op, typename TOut, int UNIT_K, int S, bool CM = false>
-static hipError_t launch_pp(const GemmArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((pingpong_gemm_kernel<Op, TOut, UNIT_K, S, 0, CM>), dim3(grid),
-                       dim3(kPPThreads), 0, st, a);
     return hipGetLastError();
 }
 
 template <class Op, typename TOut>
 static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t st) {
     switch (v) {
-    case V_T256x256: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 1, false>(a, grid, st);
     case V_T128x256: return launch_one<Op, TOut, 128, 256, 64, 2, 1>(a, grid, st);
     case V_T128x128: return launch_one<Op, TOut, 128, 128, 64, 2, 2>(a, grid, st);
     case V_T128x64: return launch_one<Op, TOut, 128, 64, 64, 2, 3>(a, grid, st);
-    case V_T256x256_K32S4: return launch_one<Op, TOut, 256, 256, 32, 4, 1, 2>(a, grid, st);
-    case V_T256x256_K32S5: return launch_one<Op, TOut, 256, 256, 32, 5, 1, 2>(a, grid, st);
-    case V_T256x256_SPLIT2: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 2>(a, grid, st);
-    case V_T256x256_SPLIT4: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 4>(a, grid, st);
     case V_T256x256_SPLIT3: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 3>(a, grid, st);
-    case V_T256x256_VG2: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 2, true, true>(a, grid, st);
-    case V_T256x256_VG4: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 4, true, true>(a, grid, st);
-    case V_PP256: return launch_pp<Op, TOut, 64, 2>(a, grid, st);
-    case V_PP256_K32S4: return launch_pp<Op, TOut, 32, 4>(a, grid, st);
-    case V_PP256_K32S4_CM: return launch_pp<Op, TOut, 32, 4, true>(a, grid, st);
     }
     return hipErrorInvalidValue;
 }

@@ -17,26 +17,12 @@ namespace tcm {
 
 VariantInfo variant_info(int32_t v) {
     switch (v) {
-    case V_T256x256: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_T128x256: return {128, 256, 64, 2, 1, 16, kThreads};
     case V_T128x128: return {128, 128, 64, 2, 2, 16, kThreads};
     case V_T128x64: return {128, 64, 64, 2, 3, 16, kThreads};
-    case V_T256x256_K32S4: return {256, 256, 32, 4, 1, 16, kThreads};
-    case V_T256x256_K32S5: return {256, 256, 32, 5, 1, 16, kThreads};
-    case V_T256x256_SPLIT2: return {256, 256, 64, 2, 1, 16, kThreads};
-    case V_T256x256_SPLIT4: return {256, 256, 64, 2, 1, 16, kThreads};
-    case V_MX256x256: return {256, 256, 128, 2, 1, 8, kThreads};
     case V_MX128x128: return {128, 128, 128, 2, 1, 8, kThreads};
-    case V_MX256x256_SPLIT2: return {256, 256, 128, 2, 1, 8, kThreads};
-    case V_PP256: return {256, 256, 64, 2, 1, 16, 512};
-    case V_PP256_K32S4: return {256, 256, 32, 4, 1, 16, 512};
-    case V_PP256_K32S4_CM: return {256, 256, 32, 4, 1, 16, 512};
-    case V_T256x256_VG2: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_T256x256_SPLIT3: return {256, 256, 64, 2, 1, 16, kThreads};
-    case V_T256x256_VG4: return {256, 256, 64, 2, 1, 16, kThreads};
-    case V_MXPP256: return {256, 256, 128, 2, 1, 8, 512};
     case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 8, 512};
-    case V_MXPP256_K64S4_CM: return {256, 256, 64, 4, 1, 8, 512};
     case V_MX4PP256: return {256, 256, 128, 4, 1, 4, 512};
     case V_MX6PP256: return {256, 256, 64, 4, 1, 6, 512};
     // NVFP4: the LDS tiles hold fp16

@@ -43,21 +43,14 @@ struct GemmArgs {
     int32_t op;  // per-element epilogue operation (tcm_op code; C-input kernels only)
 };
 
-// Kernel variants.  The id is reported by tcm_plan_gemm.
+// Kernel variants.  The id is reported by tcm_plan_gemm.  (Ids of variants
+// that measured slower and were removed are not reused.)
 enum Variant : int32_t {
-    V_T256x256 = 0,   // 256x256x64, 2-stage ring, 1 workgroup per CU
     V_T128x256 = 1,   // 128x256x64, 2-stage ring
     V_T128x128 = 2,   // 128x128x64, 2-stage ring, 2 workgroups per CU
     V_T128x64 = 3,    // 128x64x64, 2-stage ring, 3 workgroups per CU
-    V_T256x256_K32S4 = 4,  // 256x256x32, 4-stage ring
-    V_T256x256_K32S5 = 5,  // 256x256x32, 5-stage ring (all 160 KiB of LDS)
-    V_T256x256_SPLIT2 = 6, // 256x256x64, 2-stage ring, copies split over 2 K steps
-    V_T256x256_SPLIT4 = 7, // 256x256x64, 2-stage ring, copies split over 4 K steps
-    V_PP256 = 8,           // 256x256x64, eight waves taking turns (ping-pong), 2-stage ring
-    V_PP256_K32S4 = 9,     // 256x256x32 ping-pong, 4-stage ring, copies shared by all waves
-    V_PP256_K32S4_CM = 16, // variant 9 with the copies issued between the MFMAs
-    V_T256x256_VG2 = 17,   // variant 6 with register-staged copies (loads + ds_write)
-    V_T256x256_VG4 = 18,   // variant 7 with register-staged copies
+    V_MX128x128 = 11,       // MXFP8 128x128x128, 2-stage ring
+    V_MXPP256_K64S4 = 14,   // MXFP8 256x256x64 ping-pong, 4-stage ring
     V_T256x256_SPLIT3 = 19, // 256x256x64, 2-stage ring, copies split over 3 K steps (6/5/5)
     V_MX4PP256 = 20,        // MXFP4 256x256x128 ping-pong, 4-stage ring
     V_MX6PP256 = 21,        // MXFP6 256x256x64 ping-pong, 4-stage ring, grouped row layout
@@ -66,12 +59,6 @@ enum Variant : int32_t {
     V_NV4W_256 = 24,        // V_NV4_256 with a row's scales of four slices in one load
     V_NV4W_128 = 25,        // V_NV4_128, the same
     V_MX256x128 = 26,       // MXFP8 256x128x128, 2-stage ring (arrangements and leading dimensions)
-    V_MX256x256 = 10, // MXFP8 256x256x128, 2-stage ring
-    V_MX128x128 = 11, // MXFP8 128x128x128, 2-stage ring
-    V_MX256x256_SPLIT2 = 12, // MXFP8 256x256x128, copies split over 2 K steps
-    V_MXPP256 = 13,          // MXFP8 256x256x128, eight waves taking turns (ping-pong)
-    V_MXPP256_K64S4 = 14,    // MXFP8 256x256x64 ping-pong, 4-stage ring
-    V_MXPP256_K64S4_CM = 15, // variant 14 with the copies issued between the MFMAs
 };
 
 struct VariantInfo {
