@@ -61,12 +61,15 @@ void pingpong_gemm_kernel(GemmArgs p) {
     constexpr int BK = UNIT_K;
     constexpr int RB = BK * EBITS / 8;  // bytes of one operand row's K unit
     constexpr int CPR = RB / 16;        // 16-byte chunks per row
-    // FP6 rows of a unit are 48 (64-deep) or 96 (128-deep) bytes, CPR = 3 or
-    // 6 chunks: the stage holds groups of 16 rows, chunk-major within a group
-    // (chunk k of row r at chunk index (r / 16) 16 CPR + 16 k + r % 16 of the
-    // operand region), so that 16 lanes reading one chunk of 16 consecutive
-    // rows touch 16 consecutive chunks: every bank once.
-    constexpr int GROUP = 16 * CPR;  // chunks of a 16-row group (FP6)
+    // FP6 rows of a 64-deep unit are 48 bytes (CPR = 3 chunks), stored row
+    // after row without a swizzle: chunk k of row r is chunk 3 r + k of the
+    // operand region.  16 lanes reading one chunk of 16 consecutive rows
+    // touch chunks 3 r + k, which fall on 16 different 16-byte bank groups
+    // (3 r mod 16 takes every value once over 16 rows).  A copy's
+    // consecutive lanes take consecutive chunks, so each row's 48 bytes are
+    // fetched by three neighbouring lanes from one contiguous stretch of
+    // memory (a lane per row, as in a chunk-major layout, made the vector L1
+    // look up a separate cache line for nearly every lane).
     // chunk ^= row bits chosen so that the 16 rows read together by 16 lanes
     // fall on 16 different 16-byte bank groups (64 banks of 4 bytes)
     constexpr int SWZ = CPR == 8 ? 1 : 2;
@@ -102,8 +105,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
     constexpr bool EPI_LDS = sizeof(TOut) == 2 && RING + 8 * 16 * STG_ROWB <= 160 * 1024;
     constexpr int STG_ROWS = RING + 8 * 32 * STG_ROWB <= 160 * 1024 ? 32 : 16;
     constexpr int STG_BYTES = EPI_LDS ? STG_ROWS * STG_ROWB : 0;
-    static_assert(CPR == 4 || CPR == 8 || (FP6 && (BK == 64 || BK == 128)),
-                  "64- or 128-byte rows, or FP6 units of 64 or 128");
+    static_assert(CPR == 4 || CPR == 8 || (FP6 && BK == 64),
+                  "64- or 128-byte rows, or 64-deep FP6 units (48-byte rows)");
     static_assert(KSTEPS >= 1 && KSTEPS <= 4, "K steps per unit");
     static_assert(!Op::kScaled || KSTEPS <= 2, "scale bytes per register");
     static_assert((DATA / 1024) % NCW == 0, "copy split");
@@ -186,9 +189,9 @@ void pingpong_gemm_kernel(GemmArgs p) {
     const uint32_t kmaj_lane_off_a = (uint32_t)cp_row * ROWB_A + cp_chunk * 16;
     const uint32_t kmaj_lane_off_b = (uint32_t)cp_row * ROWB_B + cp_chunk * 16;
     // FP6: copy t fills chunk Qo = 64 qq + lane of its operand region (qq the
-    // copy's index within A or B): row 16 (Qo / 48) + Qo % 16, chunk
-    // (Qo % 48) / 16.  The pattern has no uniform step, so each copy keeps
-    // its own lane offset and chunk byte (for the K tail).
+    // copy's index within A or B): row Qo / CPR, chunk Qo % CPR.  The
+    // pattern has no uniform step, so each copy keeps its own lane offset
+    // and chunk byte (for the K tail).
     uint32_t off6[FP6 ? PW : 1];
     int cb6[FP6 ? PW : 1];
     if constexpr (FP6) {
@@ -197,7 +200,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
             const int q = cw + t * NCW;
             const int qq = q < A_COPIES ? q : q - A_COPIES;
             const int Qo = 64 * qq + lane;
-            const int r = 16 * (Qo / GROUP) + Qo % 16, k = (Qo % GROUP) / 16;
+            const int r = Qo / CPR, k = Qo % CPR;
             off6[t] = (uint32_t)r * ROWB + 16 * k;
             cb6[t] = 16 * k;
         }
@@ -349,14 +352,14 @@ void pingpong_gemm_kernel(GemmArgs p) {
 
     // ---- fragments of one unit -------------------------------------------------
     const int xr = (l32 >> SWZ) & (CPR - 1);
-    // FP6: byte of chunk 0 of row R in the grouped layout; the block of
+    // FP6: byte of chunk 0 of row R in the row-major layout; the block of
     // half-wave hi is chunk 2 hi (16 bytes) and half hi of chunk 1 (8 bytes)
-    auto fp6_row = [&](int R) -> uint32_t { return (uint32_t)(((R / 16) * GROUP + R % 16) * 16); };
+    auto fp6_row = [&](int R) -> uint32_t { return (uint32_t)(R * RB); };
     const uint32_t a_frag = FP6 ? fp6_row(grp * WTM + l32) : (uint32_t)(grp * WTM + l32) * RB;
     const uint32_t b_frag = (uint32_t)A_BYTES +
                             (FP6 ? fp6_row(sub * WTN + l32) : (uint32_t)(sub * WTN + l32) * RB);
     // distance between fragment blocks of 32 rows
-    constexpr uint32_t FRAG_STRIDE = FP6 ? 2 * GROUP * 16 : 32 * RB;
+    constexpr uint32_t FRAG_STRIDE = 32 * RB;
     typedef typename Op::frag_t frag_t;
     frag_t fa[KSTEPS][FM], fb[KSTEPS][FN];
     auto read_frag = [&](const char* base, int s) -> frag_t {
@@ -364,11 +367,15 @@ void pingpong_gemm_kernel(GemmArgs p) {
         if constexpr (FP6) {
             // K step s holds blocks 2s and 2s + 1, chunks 3s .. 3s + 2: block
             // 2s is chunk 3s then the low half of chunk 3s + 1, block 2s + 1
-            // the high half of chunk 3s + 1 then chunk 3s + 2
-            const i32x4_t c16 = *(const i32x4_t*)(base + 256 * (3 * s + 2 * hi));
-            const i32x2_t c8 = *(const i32x2_t*)(base + 256 * (3 * s + 1) + 8 * hi);
-            f = hi ? (i32x8_t){c8[0], c8[1], c16[0], c16[1], c16[2], c16[3], 0, 0}
-                   : (i32x8_t){c16[0], c16[1], c16[2], c16[3], c8[0], c8[1], 0, 0};
+            // the high half of chunk 3s + 1 then chunk 3s + 2.  The middle
+            // chunk is read whole (16 bytes) and its half picked in
+            // registers: 8-byte reads are served 32 lanes at a time, and rows
+            // r and r + 16 of 48-byte rows share banks.
+            const i32x4_t c16 = *(const i32x4_t*)(base + 16 * (3 * s + 2 * hi));
+            const i32x4_t mid = *(const i32x4_t*)(base + 16 * (3 * s + 1));
+            const int m0 = hi ? mid[2] : mid[0], m1 = hi ? mid[3] : mid[1];
+            f = hi ? (i32x8_t){m0, m1, c16[0], c16[1], c16[2], c16[3], 0, 0}
+                   : (i32x8_t){c16[0], c16[1], c16[2], c16[3], m0, m1, 0, 0};
         } else if constexpr (EBITS == 4) {
             // MXFP4: half-wave hi holds block hi of the MFMA's 64 K values,
             // the 16-byte chunk 2s + hi of the row

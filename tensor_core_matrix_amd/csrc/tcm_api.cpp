@@ -138,6 +138,14 @@ int64_t max_grid() {
     return g > 0 ? (int64_t)g : INT64_MAX;
 }
 
+// TCM_GROUP_M=<n> (read at every call) sets the tile rows per group of the
+// grouped tile order (tuning sweeps); unset or not positive, 4.
+int32_t group_m() {
+    const char* e = getenv("TCM_GROUP_M");
+    const long g = e && *e ? atol(e) : 0;
+    return g > 0 && g <= 1024 ? (int32_t)g : 4;
+}
+
 // Tile choice: the largest tile whose tile count still gives every CU at
 // least one tile with little padding; small problems take the smallest tile.
 // Families by element bits: 16 (f16/bf16), 8 (MXFP8), 6 (MXFP6), 4 (MXFP4).
@@ -207,7 +215,7 @@ tcm_status plan_variant(int32_t v, int64_t batch, int64_t M, int64_t N, int64_t 
         args->tiles_per_batch = (int32_t)(tm * tn);
         args->total_tiles = (int32_t)tiles;
         args->ksteps = K > 0 ? (int32_t)cdiv(K, vi.tile_k) : 1;
-        args->group_m = 4;
+        args->group_m = group_m();
         // dense storage unless the caller says otherwise
         args->lda = args->ldb = (int32_t)K;
         args->ldc = args->ldcin = (int32_t)N;
