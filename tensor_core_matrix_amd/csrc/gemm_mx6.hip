@@ -24,6 +24,7 @@ template <typename TOut, int FMT>
 static hipError_t by_variant(int32_t v, int32_t mode, const GemmArgs& a, int grid, hipStream_t st) {
     switch (v) {
     case V_MX6PP256: return by_mode<TOut, FMT, 64, 4>(mode, a, grid, st);
+    case V_MX6PP256_K128: return by_mode<TOut, FMT, 128, 3>(mode, a, grid, st);
     }
     return hipErrorInvalidValue;
 }

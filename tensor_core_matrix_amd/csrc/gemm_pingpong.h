@@ -73,6 +73,17 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // chunk ^= row bits chosen so that the 16 rows read together by 16 lanes
     // fall on 16 different 16-byte bank groups (64 banks of 4 bytes)
     constexpr int SWZ = CPR == 8 ? 1 : 2;
+    // FP6 with 128-deep units (PAIR6): rows of 96 bytes (6 chunks), chunk k
+    // of row r at chunk 6 r + (k ^ ((r >> 3) & 1)).  Over 16 consecutive
+    // rows 6 r mod 16 takes each even value twice, for rows r and r + 8; the
+    // XOR moves rows 8-15 of every 16 to the odd bank groups, so 16 lanes
+    // reading chunk k of 16 consecutive rows meet no conflict.  The MFMA's
+    // two K blocks per lane half are blocks {0, 2} (first K step) and {1, 3}
+    // (second) of the unit's four: then both lane halves start their
+    // 24-byte operand at a chunk boundary (bytes 0 and 48, then 24 and 72),
+    // and three 16-byte reads give both K steps' operands with no byte read
+    // twice (see read_pair6).
+    constexpr bool PAIR6 = FP6 && BK == 128;
     constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB, DATA = A_BYTES + B_BYTES;
     // MX scales reach the MFMA waves through LDS, copied by the same DMA as
     // the operands, so that no wave waits on a global load.  With 16-byte
@@ -105,8 +116,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
     constexpr bool EPI_LDS = sizeof(TOut) == 2 && RING + 8 * 16 * STG_ROWB <= 160 * 1024;
     constexpr int STG_ROWS = RING + 8 * 32 * STG_ROWB <= 160 * 1024 ? 32 : 16;
     constexpr int STG_BYTES = EPI_LDS ? STG_ROWS * STG_ROWB : 0;
-    static_assert(CPR == 4 || CPR == 8 || (FP6 && BK == 64),
-                  "64- or 128-byte rows, or 64-deep FP6 units (48-byte rows)");
+    static_assert(CPR == 4 || CPR == 8 || (FP6 && (BK == 64 || BK == 128)),
+                  "64- or 128-byte rows, or FP6 units 64 or 128 deep (48- or 96-byte rows)");
     static_assert(KSTEPS >= 1 && KSTEPS <= 4, "K steps per unit");
     static_assert(!Op::kScaled || KSTEPS <= 2, "scale bytes per register");
     static_assert((DATA / 1024) % NCW == 0, "copy split");
@@ -192,15 +203,19 @@ void pingpong_gemm_kernel(GemmArgs p) {
     // copy's index within A or B): row Qo / CPR, chunk Qo % CPR.  The
     // pattern has no uniform step, so each copy keeps its own lane offset
     // and chunk byte (for the K tail).
-    uint32_t off6[FP6 ? PW : 1];
-    int cb6[FP6 ? PW : 1];
+    // Where A's copies split evenly over the copying waves, copy t of A and
+    // copy t + A_COPIES / NCW (of B) have the same index within their
+    // operand, so NOFF offsets serve all of them.
+    constexpr int NOFF = FP6 && A_COPIES % NCW == 0 ? A_COPIES / NCW : PW;
+    uint32_t off6[FP6 ? NOFF : 1];
+    int cb6[FP6 ? NOFF : 1];
     if constexpr (FP6) {
 #pragma unroll
-        for (int t = 0; t < PW; ++t) {
+        for (int t = 0; t < NOFF; ++t) {
             const int q = cw + t * NCW;
             const int qq = q < A_COPIES ? q : q - A_COPIES;
             const int Qo = 64 * qq + lane;
-            const int r = Qo / CPR, k = Qo % CPR;
+            const int r = Qo / CPR, k = (Qo % CPR) ^ (PAIR6 ? (r >> 3) & 1 : 0);
             off6[t] = (uint32_t)r * ROWB + 16 * k;
             cb6[t] = 16 * k;
         }
@@ -317,7 +332,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
             return;
         }
         if constexpr (FP6)
-            off = base != kOutOfRange && base + cb6[t] < ROWB ? base + off6[t] : kOutOfRange;
+            off = base != kOutOfRange && base + cb6[t % NOFF] < ROWB ? base + off6[t % NOFF]
+                                                                    : kOutOfRange;
         else
             off = base + copy_row_off(t);
         copy16_to_lds(q < A_COPIES ? ra : rb, lds + (fu % S) * STAGE + q * 1024, off);
@@ -410,8 +426,31 @@ void pingpong_gemm_kernel(GemmArgs p) {
             return frag_t{};
         }
     };
+    // PAIR6: the operands of both K steps of a 32-row block.  Lane half hi
+    // takes blocks 2 hi (step 0) and 2 hi + 1 (step 1): bytes 48 hi .. +23
+    // and 48 hi + 24 .. +23 of the row, i.e. chunk 3 hi, the middle chunk
+    // 3 hi + 1 (its low half ends step 0's operand, its high half starts
+    // step 1's) and chunk 3 hi + 2.
+    auto read_pair6 = [&](const char* base, frag_t& f0, frag_t& f1) {
+        if constexpr (PAIR6) {
+            const int sw = (l32 >> 3) & 1;  // the row's swizzle (blocks start at multiples of 32 rows)
+            const i32x4_t x = *(const i32x4_t*)(base + 16 * ((3 * hi) ^ sw));
+            const i32x4_t y = *(const i32x4_t*)(base + 16 * ((3 * hi + 1) ^ sw));
+            const i32x4_t z = *(const i32x4_t*)(base + 16 * ((3 * hi + 2) ^ sw));
+            f0 = (i32x8_t){x[0], x[1], x[2], x[3], y[0], y[1], 0, 0};
+            f1 = (i32x8_t){y[2], y[3], z[0], z[1], z[2], z[3], 0, 0};
+        }
+    };
     auto read_unit = [&](int u) {
         const char* st = lds + (u % S) * STAGE;
+        if constexpr (PAIR6) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) read_pair6(st + a_frag + i * FRAG_STRIDE, fa[0][i], fa[1][i]);
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj)
+                read_pair6(st + b_frag + jj * FRAG_STRIDE, fb[0][jj], fb[1][jj]);
+            return;
+        }
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
@@ -429,9 +468,24 @@ void pingpong_gemm_kernel(GemmArgs p) {
     int sc_a[Op::kScaled ? FM : 1], sc_b[Op::kScaled ? FN : 1];
     // chunk mode: the 8 scale bytes a lane needs from its row's 16 (blocks
     // 2 k + hi, k = unit within the chunk), byte k of a 64-bit value
-    uint64_t pk[SC_CHUNK ? FM + FN : 1];
+    uint64_t pk[SC_CHUNK && !PAIR6 ? FM + FN : 1];
     auto load_scales = [&](const TileCursor& c, int u) {
-        if constexpr (SC_CHUNK) {
+        if constexpr (SC_CHUNK && PAIR6) {
+            // word k (unit k of the chunk: blocks 4 k .. 4 k + 3) of each
+            // fragment row's 16 bytes, read afresh every unit (holding a
+            // chunk's bytes in registers would not fit beside the paired
+            // fragments): bytes 2 hi and 2 hi + 1 serve the two K steps
+            const int k = u % UPC;
+            const char* sc = lds + S * STAGE + ((u / UPC) & 1) * CHUNK_BYTES;
+#pragma unroll
+            for (int f = 0; f < FM + FN; ++f) {
+                const bool is_a = f < FM;
+                const int idx = is_a ? f : f - FM;
+                const int row = (is_a ? grp * WTM : BM + sub * WTN) + idx * 32 + l32;
+                const int v = (int)(*(const uint32_t*)(sc + row * 16 + 4 * k) >> (16 * hi));
+                if (is_a) sc_a[idx] = v; else sc_b[idx] = v;
+            }
+        } else if constexpr (SC_CHUNK) {
             const int k = u % UPC;  // unit within the chunk
             if (k == 0) {
                 // first unit of a chunk: one 16-byte read per fragment row
@@ -458,7 +512,7 @@ void pingpong_gemm_kernel(GemmArgs p) {
             }
         } else if constexpr (SC_LDS) {
             const char* sc = lds + (u % S) * STAGE + DATA;
-            const int sh = 8 * (((c.kk * (BK / 32)) & 3) + hi);
+            const int sh = 8 * (((c.kk * (BK / 32)) & 3) + (PAIR6 ? 2 * hi : hi));
 #pragma unroll
             for (int f = 0; f < FM + FN; ++f) {
                 const bool is_a = f < FM;
@@ -481,13 +535,13 @@ void pingpong_gemm_kernel(GemmArgs p) {
                 if constexpr (SCALE_WORDS) {
                     // rows of K/32 bytes are whole words: the unit's bytes sit in one word
                     uint32_t w = *(const uint32_t*)(src + (kb0 & ~3));
-                    v = (int)(w >> (8 * ((kb0 & 3) + hi)));
+                    v = (int)(w >> (8 * ((kb0 & 3) + (PAIR6 ? 2 * hi : hi))));
                 } else {
-                    int q0 = kb0 + hi;
+                    int q0 = kb0 + (PAIR6 ? 2 * hi : hi);
                     v = q0 < kblocks ? src[q0] : 127;
                     if constexpr (KSTEPS > 1) {
-                        int q2 = kb0 + 2 + hi;
-                        v |= (q2 < kblocks ? src[q2] : 127) << 16;
+                        int q2 = PAIR6 ? q0 + 1 : kb0 + 2 + hi;
+                        v |= (q2 < kblocks ? src[q2] : 127) << (PAIR6 ? 8 : 16);
                     }
                 }
                 if (is_a) sc_a[idx] = v; else sc_b[idx] = v;
@@ -513,8 +567,8 @@ void pingpong_gemm_kernel(GemmArgs p) {
                     }
                     if constexpr (Op::kScaled) {
                         // the second K step's scale: byte 1 of a packed chunk
-                        // value, byte 2 of the other forms
-                        constexpr int SEL1 = SC_CHUNK ? 1 : 2;
+                        // value or of any PAIR6 form, byte 2 of the others
+                        constexpr int SEL1 = (SC_CHUNK || PAIR6) ? 1 : 2;
                         if (s == 0)
                             acc[i][j] = Op::template mma<0>(fb[s][j], fa[s][i], c, sc_b[j], sc_a[i]);
                         else

@@ -25,6 +25,7 @@ VariantInfo variant_info(int32_t v) {
     case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 8, 512};
     case V_MX4PP256: return {256, 256, 128, 4, 1, 4, 512};
     case V_MX6PP256: return {256, 256, 64, 4, 1, 6, 512};
+    case V_MX6PP256_K128: return {256, 256, 128, 3, 1, 6, 512};
     // NVFP4: the LDS tiles hold fp16
     case V_NV4_256: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_NV4_128: return {128, 128, 64, 2, 2, 16, kThreads};
@@ -157,7 +158,7 @@ int32_t choose_variant(int64_t batch, int64_t M, int64_t N, int32_t bits, int cu
     static const int32_t plain[] = {V_T256x256_SPLIT3, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MXPP256_K64S4, V_MX128x128};
     static const int32_t mx4[] = {V_MX4PP256};
-    static const int32_t mx6[] = {V_MX6PP256};
+    static const int32_t mx6[] = {V_MX6PP256_K128};
     const int32_t* cand = bits == 8 ? mxv : bits == 4 ? mx4 : bits == 6 ? mx6 : plain;
     const int n = bits == 8 ? 2 : bits == 4 ? 1 : bits == 6 ? 1 : 4;
     for (int i = 0; i < n; ++i) {
@@ -231,6 +232,14 @@ tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t bit
 // NVFP4: the 256 x 256 tile where it fills the CUs with little padding; a
 // row's scales of four slices in one 16-byte load where K and the scale
 // tensors allow it (wide).
+// MXFP6: the 128-deep kernel reads its scales as 32-bit words or 16-byte
+// pieces (K a multiple of 128, word-aligned scale tensors); with scales read
+// byte by byte it would spill registers, so such calls take the 64-deep
+// kernel unless a variant is forced.
+int32_t mx6_variant(int32_t v, bool scale_words) {
+    return v == V_MX6PP256_K128 && !scale_words && forced_variant() < 0 ? V_MX6PP256 : v;
+}
+
 int32_t nv4_variant(int64_t M, int64_t N, bool wide, int cus) {
     const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
     const double fill = double(M) * N / (double(tiles) * 256 * 256);
@@ -331,17 +340,6 @@ tcm_status run_mx(int32_t bits, const void* A, const void* B, const void* scale_
         return TCM_ERR_MISALIGNED;
     DeviceInfo dev;
     if ((s = device_info(&dev)) != TCM_OK) return s;
-    tcm_plan plan;
-    GemmArgs a;
-    make_plan(1, M, N, K, bits, dev.cus, &plan, &a);
-    a.A = A;
-    a.B = B;
-    a.SA = scale_A;
-    a.SB = scale_B;
-    a.C = Out;
-    a.stride_a = M * K * bits / 8;
-    a.stride_b = N * K * bits / 8;
-    a.stride_c = M * N * elem_bytes(out_dtype);
     // Wide scale reads need every row's K/32 bytes to be whole words (16-byte
     // pieces) and the arrays aligned to match.
     const uintptr_t sa = reinterpret_cast<uintptr_t>(scale_A), sb = reinterpret_cast<uintptr_t>(scale_B);
@@ -350,6 +348,21 @@ tcm_status run_mx(int32_t bits, const void* A, const void* B, const void* scale_
         scale_mode = 2;
     else if (K > 0 && K % 128 == 0 && ((sa | sb) & 3u) == 0)
         scale_mode = 1;
+    tcm_plan plan;
+    GemmArgs a;
+    if (bits == 6)
+        plan_variant(mx6_variant(choose_variant(1, M, N, bits, dev.cus), scale_mode >= 1), 1, M,
+                     N, K, dev.cus, &plan, &a);
+    else
+        make_plan(1, M, N, K, bits, dev.cus, &plan, &a);
+    a.A = A;
+    a.B = B;
+    a.SA = scale_A;
+    a.SB = scale_B;
+    a.C = Out;
+    a.stride_a = M * K * bits / 8;
+    a.stride_b = N * K * bits / 8;
+    a.stride_c = M * N * elem_bytes(out_dtype);
     hipError_t e = bits == 6 ? launch_gemm_mx6(plan.kernel, (int32_t)out_dtype, scale_mode,
                                                (int32_t)elem_dtype, a, plan.grid,
                                                (hipStream_t)stream)
@@ -625,8 +638,12 @@ tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dty
         plan_variant(mx_mn_variant(m1, n1, K, (m1 + 15) / 16 * 16, (n1 + 15) / 16 * 16, n1, true,
                                    num_cus),
                      b1, m1, n1, K, num_cus, plan, nullptr);
+    else if (mx == 3)
+        // (word-aligned scale tensors)
+        plan_variant(mx6_variant(choose_variant(b1, m1, n1, 6, num_cus), K > 0 && K % 128 == 0),
+                     b1, m1, n1, K, num_cus, plan, nullptr);
     else
-        make_plan(b1, m1, n1, K, mx == 3 ? 6 : mx == 2 ? 4 : mx ? 8 : 16, num_cus, plan, nullptr);
+        make_plan(b1, m1, n1, K, mx == 2 ? 4 : mx ? 8 : 16, num_cus, plan, nullptr);
     if (empty) {
         plan->grid = 0;
         plan->tiles = 0;

@@ -53,12 +53,13 @@ enum Variant : int32_t {
     V_MXPP256_K64S4 = 14,   // MXFP8 256x256x64 ping-pong, 4-stage ring
     V_T256x256_SPLIT3 = 19, // 256x256x64, 2-stage ring, copies split over 3 K steps (6/5/5)
     V_MX4PP256 = 20,        // MXFP4 256x256x128 ping-pong, 4-stage ring
-    V_MX6PP256 = 21,        // MXFP6 256x256x64 ping-pong, 4-stage ring, grouped row layout
+    V_MX6PP256 = 21,        // MXFP6 256x256x64 ping-pong, 4-stage ring, rows stored row after row
     V_NV4_256 = 22,         // NVFP4 256x256x64, dequantizing register-staged copies, fp16 MFMA
     V_NV4_128 = 23,         // NVFP4 128x128x64, the same
     V_NV4W_256 = 24,        // V_NV4_256 with a row's scales of four slices in one load
     V_NV4W_128 = 25,        // V_NV4_128, the same
     V_MX256x128 = 26,       // MXFP8 256x128x128, 2-stage ring (arrangements and leading dimensions)
+    V_MX6PP256_K128 = 27,   // MXFP6 ping-pong, 128-deep units (96-byte rows), ring of 3
 };
 
 struct VariantInfo {

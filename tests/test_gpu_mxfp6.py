@@ -4,7 +4,9 @@ acceptance rule as the other products: |gpu - ref| <= 1e-4 * sum_k |a_ik b_jk|
 (+ one bf16 ulp for bf16 output).  With unit scales, E2M3 products and sums
 up to K = 1024 are exact in fp32, so those cases must match bit for bit.  The
 shapes reach all three ways of reading the scales (bytes: K = 576, 32-bit
-words: K = 640, 16-byte pieces: K = 1536)."""
+words: K = 640, 16-byte pieces: K = 1536), each on both kernels: 128-deep
+units (variant 27, the default where scales are read as words or pieces;
+K = 576 leaves its last unit half empty) and 64-deep units (variant 21)."""
 import numpy as np
 import pytest
 import torch
@@ -60,10 +62,16 @@ def grid_cap(monkeypatch):
     return _set
 
 
+@pytest.fixture(params=[27, 21])
+def variant(request, monkeypatch):
+    monkeypatch.setenv("TCM_FORCE_VARIANT", str(request.param))
+    return request.param
+
+
 @pytest.mark.parametrize("K", [576, 640, 1536])
 @pytest.mark.parametrize("odt", ["f32", "bf16"])
 @pytest.mark.parametrize("elem", ["e2m3", "e3m2"])
-def test_mxfp6_ragged(K, odt, elem, grid_cap):
+def test_mxfp6_ragged(K, odt, elem, grid_cap, variant):
     M, N = 700, 520
     a, b, sa, sb = make(M, N, K, 1000 + K)
     ref, s = oracle(a, b, sa, sb, elem)
@@ -74,7 +82,7 @@ def test_mxfp6_ragged(K, odt, elem, grid_cap):
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 64), (33, 17, 64), (256, 256, 128), (300, 260, 1024)])
-def test_mxfp6_unit_scales_exact(shape):
+def test_mxfp6_unit_scales_exact(shape, variant):
     M, N, K = shape
     a, b, _, _ = make(M, N, K, 1100 + K)
     sa = torch.full((M, K // 32), 127, dtype=torch.uint8)
