@@ -12,10 +12,12 @@ operands row-major and MXFP8 8192^3 with M/N-major operands) are timed after
 it and reported in the same line.
 
 Every workload's inputs are drawn and copied to the device before the first
-timed call, so no host work idles the GPU between workloads.  Each workload
-then runs W untimed calls and R repeats of exactly K timed calls (HIP events
-on the launch stream, synchronised on both sides); the reported time is the
-median repeat.  After its timed repeats (outside them), each workload runs
+timed call, so no host work idles the GPU between workloads.  The headline
+workload then runs W untimed calls and R repeats of exactly K timed calls
+(HIP events on the launch stream, synchronised on both sides); the reported
+time is the median repeat.  Each other workload runs max(W, 4K) untimed calls
+first (the count is in its entry), so that it is timed at its settled rate
+rather than in the transient after the previous workload's clock window.  After its timed repeats (outside them), each workload runs
 untimed for 1.5 s while the shader clock and socket power are sampled
 (amdsmi; the firmware's table refreshes about once a second): the sustained
 clock each number was taken at.  The batched workload (184.5 MB per call,
@@ -362,17 +364,18 @@ def main() -> int:
     for name in order:
         pr = prepared[name]
         w = pr.w
-        steps = args.steps if name == order[0] else max(5, args.steps // 2)
+        steps = args.steps
+        warm = args.warmup if name == ORDER[0] else max(args.warmup, 4 * args.steps)
         if name == "tile_f16":
             steps = max(steps, 200)
-        reps = timed(pr.fn, steps, args.warmup, args.repeats, torch)
+        reps = timed(pr.fn, steps, warm, args.repeats, torch)
         # clock and power under sustained calls, after (outside) the timed
         # repeats; the single tile is launch-bound and gets none
         clock = None if name == "tile_f16" or args.no_clock else sampler.window(pr.fn, torch)
         ms = statistics.median(reps)
         tflops = w.flops / (ms * 1e-3) / 1e12
         results[name] = {
-            "ms": ms, "tflops": tflops, "steps": steps, "repeats": len(reps),
+            "ms": ms, "tflops": tflops, "steps": steps, "warmup": warm, "repeats": len(reps),
             "repeats_ms": [round(r, 5) for r in reps],
             "frac_of_peak": tflops / PEAK_TFLOPS[w.dtype],
             "gbs": pr.nbytes / (ms * 1e-3) / 1e9, "bytes": pr.nbytes, "sets": pr.sets,
