@@ -1,4 +1,5 @@
 // Kernel instances and launcher for the float16 / bfloat16 TN product.
+#include "gemm16.h"
 #include "gemm_kernel.h"
 
 namespace tcm {
@@ -29,6 +30,11 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The 16 x 16 x 32 form of each operand type (gemm16.h).
+template <class Op> struct op16;
+template <> struct op16<OpBF16> { typedef Op16BF16 type; };
+template <> struct op16<OpF16> { typedef Op16F16 type; };
+
 template <class Op, typename TOut>
 static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t st) {
     switch (v) {
@@ -36,6 +42,10 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_T128x128: return launch_one<Op, TOut, 128, 128, 64, 2, 2>(a, grid, st);
     case V_T128x64: return launch_one<Op, TOut, 128, 64, 64, 2, 3>(a, grid, st);
     case V_T256x256_SPLIT3: return launch_one<Op, TOut, 256, 256, 64, 2, 1, 3>(a, grid, st);
+    case V_T256x256_M16:
+        hipLaunchKernelGGL((gemm16_kernel<typename op16<Op>::type, TOut>), dim3(grid), dim3(kThreads), 0,
+                           st, a);
+        return hipGetLastError();
     }
     return hipErrorInvalidValue;
 }

@@ -22,6 +22,7 @@ VariantInfo variant_info(int32_t v) {
     case V_T128x64: return {128, 64, 64, 2, 3, 16, kThreads};
     case V_MX128x128: return {128, 128, 128, 2, 1, 8, kThreads};
     case V_T256x256_SPLIT3: return {256, 256, 64, 2, 1, 16, kThreads};
+    case V_T256x256_M16: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 8, 512};
     case V_MX4PP256: return {256, 256, 128, 4, 1, 4, 512};
     case V_MX6PP256: return {256, 256, 64, 4, 1, 6, 512};
@@ -155,7 +156,7 @@ int32_t choose_variant(int64_t batch, int64_t M, int64_t N, int32_t bits, int cu
     if (f >= 0 && variant_info(f).tile_m > 0 && variant_info(f).elem_bits == bits &&
         !own_entry_variant(f))
         return f;
-    static const int32_t plain[] = {V_T256x256_SPLIT3, V_T128x256, V_T128x128, V_T128x64};
+    static const int32_t plain[] = {V_T256x256_M16, V_T128x256, V_T128x128, V_T128x64};
     static const int32_t mxv[] = {V_MXPP256_K64S4, V_MX128x128};
     static const int32_t mx4[] = {V_MX4PP256};
     static const int32_t mx6[] = {V_MX6PP256_K128};

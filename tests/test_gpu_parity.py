@@ -231,7 +231,7 @@ def test_repeat_runs_bitwise_identical():
 
 
 # ------------------------------------------------------ every kernel variant
-PLAIN_VARIANTS = [1, 2, 3, 19]
+PLAIN_VARIANTS = [1, 2, 3, 19, 28]
 MX_VARIANTS = [11, 14]
 
 
@@ -304,10 +304,11 @@ def test_each_mx_variant(v, force_variant):
         assert_parity(run_mx(a3, b3, sa3, sb3, odt), ref3, s3, odt, f"mx variant {v} {odt} K {K3}")
 
 
-def test_batched_workload_through_large_tiles(force_variant):
-    """The batched problems forced through the 256 x 256 persistent kernel
+@pytest.mark.parametrize("v", [19, 28])
+def test_batched_workload_through_large_tiles(v, force_variant):
+    """The batched problems forced through the 256 x 256 persistent kernels
     (half of every tile lies past M = 128)."""
-    force_variant(19)
+    force_variant(v)
     g = inp.generator(301)
     a = inp.uniform((64, 128, 64), g, torch.bfloat16)
     b = inp.uniform((64, 256, 64), g, torch.bfloat16)
