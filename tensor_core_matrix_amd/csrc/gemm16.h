@@ -22,11 +22,12 @@
 //    (about 460 cycles) before its first use.
 //  * Two ring stages of 64 KiB.  Stage g % 2 holds slice g; the hand-off of
 //    slice g (this wave's copies of slice g + 1 landed, then a workgroup
-//    barrier) sits after the 29th product of its second K step, just before
-//    the first read of slice g + 1.  The 16 copies per wave of slice g + 2 go
-//    out one after every fifth product from there on (7 in this K step, 9 in
-//    the first K step of slice g + 1), so the address unit sees a steady
-//    stream and the last copy has about 50 products to land.
+//    barrier) sits after the 9th product of its second K step, before the
+//    first read of slice g + 1 (after the 29th).  The 16 copies per wave of
+//    slice g + 2 go out one after every fifth product from there on (11 in
+//    this K step, 5 in the first K step of slice g + 1), so the address unit
+//    sees a steady stream and the last copy has about 50 products to land.
+//    (Hand-off after product 28, 20 or 12: 0.2-1 % slower.)
 //  * The epilogue stages 32 (fp32: 16) rows of a wave's output at a time
 //    through a wave-private LDS area and stores whole 256-byte row segments.
 #pragma once
@@ -52,10 +53,10 @@ struct Op16F16 {
 
 // Schedule of one K step (slot x = after the x-th product, 0 .. 63).
 namespace g16 {
-constexpr int kHandoff = 28;                    // second K step: hand-off after product 28
+constexpr int kHandoff = 8;                     // second K step: hand-off after product 8
 constexpr int kCopyStep = 5;                    // one copy after every fifth product
-constexpr int kCopyFirst1 = 30, kCopies1 = 7;  // second K step: copies 0..6 of slice g + 2
-constexpr int kCopyFirst0 = 1, kCopies0 = 9;   // first K step: copies 7..15 of slice g + 1
+constexpr int kCopyFirst1 = 10, kCopies1 = 11; // second K step: copies 0..10 of slice g + 2
+constexpr int kCopyFirst0 = 1, kCopies0 = 5;   // first K step: copies 11..15 of slice g + 1
 // product x: quadrant q = x / 16 (A half q / 2, B half q % 2), B block
 // (x % 16) / 4 within the half, A block x % 4 within the half
 __device__ constexpr int a_of(int x) { return 4 * ((x >> 4) >> 1) + (x & 3); }
@@ -244,7 +245,7 @@ void gemm16_kernel(GemmArgs p) {
     };
 
     // ---- the K steps ---------------------------------------------------------
-    // First K step of slice g: reads of K step 1 (stage g % 2), copies 7..15
+    // First K step of slice g: reads of K step 1 (stage g % 2), copies 11..15
     // of slice g + 1 (stage (g + 1) % 2), then the stream moves to slice g + 2.
     auto step0 = [&](int g, auto ZERO) {
         const int st = g & 1;
@@ -262,8 +263,8 @@ void gemm16_kernel(GemmArgs p) {
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    // Second K step of slice g: hand-off, then reads of slice g + 1's first
-    // K step (stage (g + 1) % 2) and copies 0..6 of slice g + 2 (stage g % 2).
+    // Second K step of slice g: hand-off, then copies 0..10 of slice g + 2
+    // (stage g % 2) and reads of slice g + 1's first K step (stage (g + 1) % 2).
     auto step1 = [&](int g) {
         const int st = g & 1;
         static_for<64>([&](auto X) {
@@ -281,7 +282,7 @@ void gemm16_kernel(GemmArgs p) {
         });
     };
 
-    // ---- prologue: slice 0 whole, copies 0..6 of slice 1 ---------------------
+    // ---- prologue: slice 0 whole, copies 0..10 of slice 1 --------------------
     locate(fc);
     feed_resources();
     feed_offsets(true);
