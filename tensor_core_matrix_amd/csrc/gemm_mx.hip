@@ -1,4 +1,5 @@
 // Kernel instances and launcher for the MXFP8 (E4M3 + E8M0 per 32) product.
+#include "gemm16_mx.h"
 #include "gemm_pingpong.h"
 
 namespace tcm {
@@ -33,6 +34,12 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_MX128x128: return launch_one<TOut, 128, 128, WORDS>(a, grid, st);
     case V_MXPP256_K64S4: return launch_pp<TOut, MODE, 64, 4>(a, grid, st);
     case V_MX4PP256: return launch_pp<TOut, MODE, 128, 4, OpMXFP4>(a, grid, st);
+    case V_MX16_256:
+        if constexpr (MODE == 2) {
+            hipLaunchKernelGGL((gemm16_mx_kernel<TOut>), dim3(grid), dim3(kThreads), 0, st, a);
+            return hipGetLastError();
+        }
+        break;
     }
     return hipErrorInvalidValue;
 }

@@ -61,6 +61,7 @@ enum Variant : int32_t {
     V_MX256x128 = 26,       // MXFP8 256x128x128, 2-stage ring (arrangements and leading dimensions)
     V_MX6PP256_K128 = 27,   // MXFP6 ping-pong, 128-deep units (96-byte rows), ring of 3
     V_T256x256_M16 = 28,    // 256x256x64 on the 16x16x32 MFMA, 2-stage ring (gemm16.h)
+    V_MX16_256 = 31,        // MXFP8 256x256x128 on the 16x16x128 scaled MFMA, scale chunks by DMA (gemm16_mx.h)
 };
 
 struct VariantInfo {

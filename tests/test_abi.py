@@ -181,11 +181,16 @@ def test_plans_of_the_workloads():
     p = tcm.plan(8192, 8192, 8192)
     assert (p["tile_m"], p["tile_n"], p["grid"], p["tiles"]) == (256, 256, 256, 1024)
     assert p["lds_bytes"] <= 160 * 1024
-    # MXFP8 8192^3: 256 x 256 tiles, eight waves taking turns, a ring of four
-    # 64-deep units (32 KiB each)
+    # MXFP8 8192^3: 256 x 256 tiles on the 16 x 16 x 128 product, two
+    # 128-deep stages (64 KiB each), four waves (variant 31); K not a multiple
+    # of 512 (scales not read as 16-byte pieces): eight waves taking turns, a
+    # ring of four 64-deep units (32 KiB each; variant 14)
     p = tcm.plan(8192, 8192, 8192, mx=True)
-    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"]) == \
-        (256, 64, 32 * 1024, 4, 512)
+    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"], p["kernel"]) == \
+        (256, 128, 64 * 1024, 2, 256, 31)
+    p = tcm.plan(8192, 8192, 8064, mx=True)
+    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"], p["kernel"]) == \
+        (256, 64, 32 * 1024, 4, 512, 14)
     # MXFP4 8192^3: the same ring of four 32 KiB units, 128 E2M1 deep
     p = tcm.plan(8192, 8192, 8192, mx=2)
     assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"]) == \

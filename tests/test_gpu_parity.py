@@ -232,7 +232,7 @@ def test_repeat_runs_bitwise_identical():
 
 # ------------------------------------------------------ every kernel variant
 PLAIN_VARIANTS = [1, 2, 3, 19, 28]
-MX_VARIANTS = [11, 14]
+MX_VARIANTS = [11, 14, 31]
 
 
 @pytest.fixture
