@@ -215,7 +215,8 @@ void gemm16_kernel(GemmArgs p) {
                     const i32x4_t d = *(const i32x4_t*)(stg + r * STG_ROWB + ((ck ^ (r & 15)) * 16));
                     char* gp = Cb + ((int64_t)(m0 + STG_ROWS * ps + r) * ldc + n0) * (int64_t)sizeof(TOut) +
                                ck * 16;
-                    *(i32x4_t*)gp = d;
+                    // non-temporal: the output does not displace operand rows in L2
+                    __builtin_nontemporal_store(d, (i32x4_t*)gp);
                 }
                 wave_lds_exchange();
             }

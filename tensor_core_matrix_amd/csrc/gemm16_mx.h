@@ -200,7 +200,8 @@ void gemm16_mx_kernel(GemmArgs p) {
                         const int ck = ln % CHK;
                         const i32x4_t d = *(const i32x4_t*)(stg + r * STG_ROWB + ((ck ^ r) * 16));
                         char* gp = Cb + ((int64_t)(m0 + 16 * i + r) * ldc + n0) * (int64_t)sizeof(TOut) + ck * 16;
-                        *(i32x4_t*)gp = d;
+                        // non-temporal: the output does not displace operand rows in L2
+                        __builtin_nontemporal_store(d, (i32x4_t*)gp);
                     }
                     wave_lds_exchange();
                 }
