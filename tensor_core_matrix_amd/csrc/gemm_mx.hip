@@ -40,6 +40,12 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
             return hipGetLastError();
         }
         break;
+    case V_MX4_16_256:
+        if constexpr (MODE == 2) {
+            hipLaunchKernelGGL((gemm16_kernel<Op16MXFP4, TOut>), dim3(grid), dim3(kThreads), 0, st, a);
+            return hipGetLastError();
+        }
+        break;
     }
     return hipErrorInvalidValue;
 }

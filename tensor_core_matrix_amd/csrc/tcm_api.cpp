@@ -24,6 +24,7 @@ VariantInfo variant_info(int32_t v) {
     case V_T256x256_SPLIT3: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_T256x256_M16: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_MX16_256: return {256, 256, 128, 2, 1, 8, kThreads};
+    case V_MX4_16_256: return {256, 256, 256, 2, 1, 4, kThreads};
     case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 8, 512};
     case V_MX4PP256: return {256, 256, 128, 4, 1, 4, 512};
     case V_MX6PP256: return {256, 256, 64, 4, 1, 6, 512};
@@ -251,6 +252,15 @@ int32_t mx8_variant(int32_t v, bool scale_chunks) {
     return v;
 }
 
+// MXFP4 256 x 256 tiles, the same way: the 16 x 16 x 128 kernel (variant 32)
+// with 16-byte scale pieces, the ping-pong kernel (variant 20) elsewhere or
+// when forced.
+int32_t mx4_variant(int32_t v, bool scale_chunks) {
+    if (v == V_MX4_16_256 && !scale_chunks) return V_MX4PP256;
+    if (v == V_MX4PP256 && scale_chunks && forced_variant() != V_MX4PP256) return V_MX4_16_256;
+    return v;
+}
+
 int32_t nv4_variant(int64_t M, int64_t N, bool wide, int cus) {
     const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
     const double fill = double(M) * N / (double(tiles) * 256 * 256);
@@ -366,6 +376,9 @@ tcm_status run_mx(int32_t bits, const void* A, const void* B, const void* scale_
                      N, K, dev.cus, &plan, &a);
     else if (bits == 8)
         plan_variant(mx8_variant(choose_variant(1, M, N, bits, dev.cus), scale_mode == 2), 1, M, N,
+                     K, dev.cus, &plan, &a);
+    else if (bits == 4)
+        plan_variant(mx4_variant(choose_variant(1, M, N, bits, dev.cus), scale_mode == 2), 1, M, N,
                      K, dev.cus, &plan, &a);
     else
         make_plan(1, M, N, K, bits, dev.cus, &plan, &a);
@@ -659,6 +672,10 @@ tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dty
     else if (mx == 1)
         // (16-byte aligned scale tensors)
         plan_variant(mx8_variant(choose_variant(b1, m1, n1, 8, num_cus), K > 0 && K % 512 == 0),
+                     b1, m1, n1, K, num_cus, plan, nullptr);
+    else if (mx == 2)
+        // (16-byte aligned scale tensors)
+        plan_variant(mx4_variant(choose_variant(b1, m1, n1, 4, num_cus), K > 0 && K % 512 == 0),
                      b1, m1, n1, K, num_cus, plan, nullptr);
     else
         make_plan(b1, m1, n1, K, mx == 2 ? 4 : mx ? 8 : 16, num_cus, plan, nullptr);

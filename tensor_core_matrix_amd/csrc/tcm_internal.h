@@ -62,6 +62,7 @@ enum Variant : int32_t {
     V_MX6PP256_K128 = 27,   // MXFP6 ping-pong, 128-deep units (96-byte rows), ring of 3
     V_T256x256_M16 = 28,    // 256x256x64 on the 16x16x32 MFMA, 2-stage ring (gemm16.h)
     V_MX16_256 = 31,        // MXFP8 256x256x128 on the 16x16x128 scaled MFMA, scale chunks by DMA (gemm16_mx.h)
+    V_MX4_16_256 = 32,      // MXFP4 256x256x256 on the 16x16x128 scaled MFMA, scale chunks by DMA (gemm16.h)
 };
 
 struct VariantInfo {

@@ -191,10 +191,15 @@ def test_plans_of_the_workloads():
     p = tcm.plan(8192, 8192, 8064, mx=True)
     assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"], p["kernel"]) == \
         (256, 64, 32 * 1024, 4, 512, 14)
-    # MXFP4 8192^3: the same ring of four 32 KiB units, 128 E2M1 deep
+    # MXFP4 8192^3: the 16 x 16 x 128 product, two 256-deep stages of 128-byte
+    # rows (64 KiB each), four waves (variant 32); K not a multiple of 512: the
+    # ping-pong kernel's ring of four 128-deep 32 KiB units (variant 20)
     p = tcm.plan(8192, 8192, 8192, mx=2)
-    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"]) == \
-        (256, 128, 32 * 1024, 4, 512)
+    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"], p["kernel"]) == \
+        (256, 256, 64 * 1024, 2, 256, 32)
+    p = tcm.plan(8192, 8192, 8064, mx=2)
+    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"], p["kernel"]) == \
+        (256, 128, 32 * 1024, 4, 512, 20)
     # MXFP6 8192^3: 128-deep units of 96-byte rows (48 KiB) in a ring of
     # three (variant 27); K not a multiple of 128 (scales read byte by byte):
     # the 64-deep kernel's ring of four 24 KiB units (variant 21)
