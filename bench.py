@@ -57,17 +57,14 @@ ORDER = ["bf16_8192", "mxfp8_8192", "mxfp6_8192", "mxfp4_8192", "nvfp4_8192", "b
 # input/output sets a workload rotates over (more than the 256 MB last-level
 # cache holds, so each call streams from HBM)
 SETS = {"batched": 3}
-KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pingpong.h", "tcm_device.h", "tcm_internal.h", "gemm_tn.hip",
-                  "gemm_mx.hip", "gemm_mx6.hip", "gemm_nv4.hip", "gemm_epi.hip", "gemm_mn.h", "gemm_mn_a.hip", "gemm_mn_b.hip",
-                  "gemm_mn_ab.hip", "gemm_mx_mn.h", "gemm_mx_ld.hip", "gemm_mx_mn_a.hip", "gemm_mx_mn_b.hip",
-                  "gemm_mx_mn_ab.hip", "tcm_api.cpp"]
-
-
 def kernel_hash() -> str:
+    """Hash of every kernel and host source file of the library (csrc/)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "tensor_core_matrix_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "tensor_core_matrix_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
