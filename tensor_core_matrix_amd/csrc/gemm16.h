@@ -15,19 +15,21 @@
 //    16 x 16 (256 registers).  A 64-deep slice is two K steps of 32; a K step
 //    is 64 products, walked in four quadrants -- (A rows 0-3, B rows 0-3),
 //    (A 0-3, B 4-7), (A 4-7, B 0-3), (A 4-7, B 4-7) in 16-row blocks -- each
-//    B block by B block.
+//    A block by A block, so that consecutive products share the
+//    instruction's second operand.
 //  * One register set of 8 A and 8 B fragments (64 registers): each fragment
 //    is read again for the next K step right after its last product of this
-//    one.  In the quadrant order every such read has at least 29 products
-//    (about 460 cycles) before its first use.
+//    one.  In the quadrant order every such read has at least 20 products
+//    (about 320 cycles) before its first use.
 //  * Two ring stages of 64 KiB.  Stage g % 2 holds slice g; the hand-off of
 //    slice g (this wave's copies of slice g + 1 landed, then a workgroup
 //    barrier) sits after the 9th product of its second K step, before the
-//    first read of slice g + 1 (after the 29th).  The 16 copies per wave of
+//    first read of slice g + 1 (after the 20th).  The 16 copies per wave of
 //    slice g + 2 go out one after every fifth product from there on (11 in
 //    this K step, 5 in the first K step of slice g + 1), so the address unit
 //    sees a steady stream and the last copy has about 50 products to land.
-//    (Hand-off after product 28, 20 or 12: 0.2-1 % slower.)
+//    (With the products B block by B block, a hand-off after product 28, 20
+//    or 12 ran 0.2-1 % slower than after product 8.)
 //  * The epilogue stages 32 (fp32: 16) rows of a wave's output at a time
 //    through a wave-private LDS area and stores whole 256-byte row segments.
 #pragma once
@@ -76,17 +78,25 @@ constexpr int kHandoff = 8;                     // second K step: hand-off after
 constexpr int kCopyStep = 5;                    // one copy after every fifth product
 constexpr int kCopyFirst1 = 10, kCopies1 = 11; // second K step: copies 0..10 of slice g + 2
 constexpr int kCopyFirst0 = 1, kCopies0 = 5;   // first K step: copies 11..15 of slice g + 1
-// product x: quadrant q = x / 16 (A half q / 2, B half q % 2), B block
-// (x % 16) / 4 within the half, A block x % 4 within the half
-__device__ constexpr int a_of(int x) { return 4 * ((x >> 4) >> 1) + (x & 3); }
-__device__ constexpr int b_of(int x) { return 4 * ((x >> 4) & 1) + ((x & 15) >> 2); }
-// fragment read for the next K step after product x (-1: none): A block i
-// after its last product (28 + i for i < 4, 56 + i for i >= 4); B block j
-// after 35 + 4 j
+// product x: quadrant q = x / 16 (A half q / 2, B half q % 2), A block
+// (x % 16) / 4 within the half, B block x % 4 within the half: four
+// consecutive products share their A fragment, the instruction's second
+// operand.  (With register operands only, products that keep the second
+// operand for eight in a row sustain 2120 TFLOP/s, those that keep the first
+// 1935: the matrix core's power, and so the clock, depends on which operand
+// changes.)
+__device__ constexpr int a_of(int x) { return 4 * ((x >> 4) >> 1) + ((x & 15) >> 2); }
+__device__ constexpr int b_of(int x) { return 4 * ((x >> 4) & 1) + (x & 3); }
+// fragment read for the next K step after product x (-1: none), right after
+// the fragment's last product: A block i after product 19 + 4 i (i < 4) or
+// 35 + 4 i; B block j after product 44 + j (j < 4) or 56 + j.  Each read has
+// at least 20 products before its first use.
 __device__ constexpr int a_read(int x) {
-    return (x >= 28 && x < 32) ? x - 28 : (x >= 60 ? x - 56 : -1);
+    return (x >= 19 && x <= 31 && (x - 19) % 4 == 0) ? (x - 19) / 4
+           : (x >= 51 && (x - 51) % 4 == 0)          ? (x - 35) / 4
+                                                     : -1;
 }
-__device__ constexpr int b_read(int x) { return (x >= 35 && (x - 35) % 4 == 0) ? (x - 35) / 4 : -1; }
+__device__ constexpr int b_read(int x) { return (x >= 44 && x < 48) ? x - 44 : (x >= 60 ? x - 56 : -1); }
 __device__ constexpr int copy1(int x) {
     return (x >= kCopyFirst1 && (x - kCopyFirst1) % kCopyStep == 0 &&
             (x - kCopyFirst1) / kCopyStep < kCopies1)
