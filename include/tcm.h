@@ -273,7 +273,10 @@ tcm_status tcm_gemm_mx(const void* A, tcm_order a_order, int64_t lda, const void
  * its block scale is exact in fp16; the products are summed in fp32 and
  * multiplied by the fp32 product gA gB before the one rounding to out_dtype.
  * With K a multiple of 256 and both scale tensors 16-byte aligned, a faster
- * form reads each row's scales of 256 K values at once (same results).
+ * form reads each row's scales of 256 K values at once; where such a product
+ * also has enough 256 x 256 tiles to fill the device, a kernel that keeps the
+ * elements 4-bit in LDS and converts them per fragment runs instead (its
+ * fp32 sums run in another order, within the same bound).
  */
 tcm_status tcm_gemm_nvfp4(const void* A, const void* B, const void* scale_A, const void* scale_B,
                           float global_scale_A, float global_scale_B, void* Out, int64_t M,

@@ -2,7 +2,7 @@
 // fp32 per tensor): register-staged copies that dequantize into fp16 LDS
 // tiles, the fp16 MFMA, and the C-input epilogue (alpha = the two tensor
 // scales' product).
-#include "gemm_kernel.h"
+#include "gemm16_nv4.h"
 
 namespace tcm {
 
@@ -24,6 +24,9 @@ static hipError_t by_variant(int32_t v, const GemmArgs& a, int grid, hipStream_t
     case V_NV4_128: return launch_nv4<TOut, 128, 128, 2, 1, false>(a, grid, st);
     case V_NV4W_256: return launch_nv4<TOut, 256, 256, 1, 2, true>(a, grid, st);
     case V_NV4W_128: return launch_nv4<TOut, 128, 128, 2, 1, true>(a, grid, st);
+    case V_NV4_16_256:
+        hipLaunchKernelGGL((gemm16_nv4_kernel<TOut>), dim3(grid), dim3(kThreads), 0, st, a);
+        return hipGetLastError();
     }
     return hipErrorInvalidValue;
 }

@@ -34,6 +34,8 @@ VariantInfo variant_info(int32_t v) {
     case V_NV4_128: return {128, 128, 64, 2, 2, 16, kThreads};
     case V_NV4W_256: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_NV4W_128: return {128, 128, 64, 2, 2, 16, kThreads};
+    // NVFP4 on the 16x16 kernel: E2M1 rows in LDS
+    case V_NV4_16_256: return {256, 256, 256, 2, 1, 4, kThreads};
     case V_MX256x128: return {256, 128, 128, 2, 1, 8, kThreads};
     }
     return {0, 0, 0, 0, 0, 0, kThreads};
@@ -118,7 +120,8 @@ tcm_status check_range(int64_t batch, int64_t M, int64_t N, int64_t K) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool is_nv4_variant(int32_t v) {
-    return v == V_NV4_256 || v == V_NV4_128 || v == V_NV4W_256 || v == V_NV4W_128;
+    return v == V_NV4_256 || v == V_NV4_128 || v == V_NV4W_256 || v == V_NV4W_128 ||
+           v == V_NV4_16_256;
 }
 
 // variants launched only by their own entry point (not forceable elsewhere)
@@ -265,9 +268,11 @@ int32_t nv4_variant(int64_t M, int64_t N, bool wide, int cus) {
     const int64_t tiles = cdiv(M, 256) * cdiv(N, 256);
     const double fill = double(M) * N / (double(tiles) * 256 * 256);
     const bool big = tiles >= cus && fill >= 0.9;
-    int32_t v = wide ? (big ? V_NV4W_256 : V_NV4W_128) : (big ? V_NV4_256 : V_NV4_128);
+    int32_t v = wide ? (big ? V_NV4_16_256 : V_NV4W_128) : (big ? V_NV4_256 : V_NV4_128);
     const int32_t f = forced_variant();
-    if (f == V_NV4_256 || f == V_NV4_128 || (wide && (f == V_NV4W_256 || f == V_NV4W_128))) v = f;
+    if (f == V_NV4_256 || f == V_NV4_128 ||
+        (wide && (f == V_NV4W_256 || f == V_NV4W_128 || f == V_NV4_16_256)))
+        v = f;
     return v;
 }
 

@@ -63,6 +63,7 @@ enum Variant : int32_t {
     V_T256x256_M16 = 28,    // 256x256x64 on the 16x16x32 MFMA, 2-stage ring (gemm16.h)
     V_MX16_256 = 31,        // MXFP8 256x256x128 on the 16x16x128 scaled MFMA, scale chunks by DMA (gemm16_mx.h)
     V_MX4_16_256 = 32,      // MXFP4 256x256x256 on the 16x16x128 scaled MFMA, scale chunks by DMA (gemm16.h)
+    V_NV4_16_256 = 34,      // NVFP4 256x256x256, E2M1 rows by DMA, converted per fragment for the 16x16x32 fp16 MFMA (gemm16_nv4.h)
 };
 
 struct VariantInfo {

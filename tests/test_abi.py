@@ -208,10 +208,12 @@ def test_plans_of_the_workloads():
         (256, 128, 48 * 1024, 3, 27)
     p = tcm.plan(8192, 8192, 8128, mx=3)
     assert (p["tile_k"], p["stage_bytes"], p["stages"], p["kernel"]) == (64, 24 * 1024, 4, 21)
-    # NVFP4 8192^3: the 256 x 256 fp16 tile, a row's scales of four slices per
-    # load (variant 24); K not a multiple of 256: variant 22; small: 128 x 128
+    # NVFP4 8192^3: the 16 x 16 kernel on 256-deep E2M1 slices, 64 KiB stages
+    # (variant 34); K not a multiple of 256: the dequantizing 256 x 256 fp16
+    # tile (variant 22); small: 128 x 128
     p = tcm.plan(8192, 8192, 8192, mx=4)
-    assert (p["tile_m"], p["tile_n"], p["tile_k"], p["kernel"]) == (256, 256, 64, 24)
+    assert (p["tile_m"], p["tile_n"], p["tile_k"], p["stage_bytes"], p["kernel"]) == \
+        (256, 256, 256, 64 * 1024, 34)
     assert tcm.plan(8192, 8192, 8160, mx=4)["kernel"] == 22
     assert tcm.plan(1024, 1024, 1024, mx=4, out_dtype=tcm.F16)["kernel"] == 25
     # MXFP8 with an M- or N-major operand: 256 x 128 x 128 tiles (variant 26),

@@ -73,9 +73,10 @@ def test_nvfp4_ragged(K, odt):
 
 # 22 / 23: 256 and 128 tiles with two scale bytes per half row and slice;
 # 24 / 25: the same tiles with a row's scales of four slices in one load
-# (K a multiple of 256: here three such groups per tile)
+# (K a multiple of 256: here three such groups per tile); 34: the 16 x 16
+# kernel on 256-deep E2M1 slices (three slices per tile)
 @pytest.mark.parametrize("variant,K", [(22, 352), (23, 352), (22, 768), (23, 768), (24, 768),
-                                       (25, 768)])
+                                       (25, 768), (34, 768)])
 def test_nvfp4_each_tile_with_persistent_grid(variant, K):
     M, N = 777, 645
     a, b, sa, sb = make(M, N, K, 1210 + variant)
@@ -85,7 +86,7 @@ def test_nvfp4_each_tile_with_persistent_grid(variant, K):
     check(got, ref, s, "bf16", f"variant {variant} K {K}")
 
 
-@pytest.mark.parametrize("variant", [24, 25])
+@pytest.mark.parametrize("variant", [24, 25, 34])
 def test_nvfp4_wide_form_declined(variant):
     """A wide variant asked for where K is not a multiple of 256, or where a
     scale tensor is only 2-byte aligned, runs the two-bytes-per-half form."""
@@ -107,35 +108,45 @@ def test_nvfp4_wide_form_declined(variant):
         check(out.cpu(), ref, s, "f32", f"variant {variant} K {K} scale offset {shift}")
 
 
-@pytest.mark.parametrize("shape", [(1, 1, 32), (33, 17, 64), (256, 256, 128), (300, 260, 1024)])
-def test_nvfp4_unit_scales_exact(shape):
+@pytest.mark.parametrize("shape,variant", [((1, 1, 32), None), ((33, 17, 64), None),
+                                           ((256, 256, 128), None), ((300, 260, 1024), None),
+                                           ((300, 260, 1024), 34), ((256, 256, 256), 34)])
+def test_nvfp4_unit_scales_exact(shape, variant):
     M, N, K = shape
     a, b, _, _ = make(M, N, K, 1220 + K)
     one = 0x38  # E4M3 1.0
     sa = torch.full((M, K // 16), one, dtype=torch.uint8)
     sb = torch.full((N, K // 16), one, dtype=torch.uint8)
     ref, _ = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), 1.0, 1.0)
-    got = run(a, b, sa, sb, 1.0, 1.0, "f32").double().numpy()
+    with env(**({"TCM_FORCE_VARIANT": variant} if variant else {})):
+        got = run(a, b, sa, sb, 1.0, 1.0, "f32").double().numpy()
     assert np.array_equal(got, ref)
 
 
-def test_nvfp4_block_scale_reaches_only_its_16():
+@pytest.mark.parametrize("variant", [None, 34])
+def test_nvfp4_block_scale_reaches_only_its_16(variant):
     """Changing one 16-element scale of A changes exactly row 5's outputs, and
-    those as the oracle says (positions in K pinned by the oracle)."""
-    M, N, K = 64, 48, 256
+    those as the oracle says (positions in K pinned by the oracle).  Variant
+    34 spreads a lane's 32 K values over four K steps: every block of 16 of
+    a 512-deep row is changed in turn there."""
+    M, N, K = 64, 48, 256 if variant is None else 512
     a, b, _, _ = make(M, N, K, 1230)
     sa = torch.full((M, K // 16), 0x38, dtype=torch.uint8)
     sb = torch.full((N, K // 16), 0x38, dtype=torch.uint8)
-    base = run(a, b, sa, sb, 1.0, 1.0, "f32").double().numpy()
-    sa2 = sa.clone()
-    sa2[5, 7] = 0x4C  # E4M3 3.5
-    got = run(a, b, sa2, sb, 1.0, 1.0, "f32").double().numpy()
-    ref, _ = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa2), inp.raw(sb), 1.0, 1.0)
-    assert np.array_equal(got, ref)
-    assert np.array_equal(np.delete(got, 5, 0), np.delete(base, 5, 0))
+    kv = {"TCM_FORCE_VARIANT": variant} if variant else {}
+    with env(**kv):
+        base = run(a, b, sa, sb, 1.0, 1.0, "f32").double().numpy()
+    for q in ([7] if variant is None else range(K // 16)):
+        sa2 = sa.clone()
+        sa2[5, q] = 0x4C  # E4M3 3.5
+        with env(**kv):
+            got = run(a, b, sa2, sb, 1.0, 1.0, "f32").double().numpy()
+        ref, _ = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa2), inp.raw(sb), 1.0, 1.0)
+        assert np.array_equal(got, ref), f"block {q}"
+        assert np.array_equal(np.delete(got, 5, 0), np.delete(base, 5, 0)), f"block {q}"
 
 
-@pytest.mark.parametrize("variant", [22, 24])
+@pytest.mark.parametrize("variant", [22, 24, 34])
 @pytest.mark.parametrize("odt", ["bf16", "f16"])
 def test_nvfp4_staged_epilogue(variant, odt):
     """The 256 x 256 NVFP4 kernels with N a multiple of 8: interior tiles stage
@@ -153,3 +164,17 @@ def test_nvfp4_staged_epilogue(variant, odt):
         with env(**kv):
             got = run(a, b, sa, sb, ga, gb, odt)
         check(got, ref, s, odt, f"variant {variant} {odt} grid {grid}")
+
+
+@pytest.mark.parametrize("K", [256, 1024])
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+def test_nvfp4_16x16_tile_sequences(K, odt):
+    """Variant 34 with one slice per tile (K 256) and with four, several tiles
+    per workgroup (a grid of 5 for 12 tiles), every output against the
+    oracle, and block-scale pieces of B row r offset from A's."""
+    M, N = 768, 1024
+    a, b, sa, sb = make(M, N, K, 1260 + K)
+    ref, s = orc.gemm_nvfp4(inp.raw(a), inp.raw(b), inp.raw(sa), inp.raw(sb), -0.5, 1.25)
+    with env(TCM_FORCE_VARIANT=34, TCM_MAX_GRID=5):
+        got = run(a, b, sa, sb, -0.5, 1.25, odt)
+    check(got, ref, s, odt, f"variant 34 K {K} {odt}")
