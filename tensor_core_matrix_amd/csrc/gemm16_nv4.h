@@ -16,9 +16,11 @@
 //    body is a pair of K steps (a body of four pairs, 512 products, defeats
 //    the register allocator: it moves accumulators at every back edge).
 //  * Lane l + 16 g of a fragment takes, for K steps 2 n and 2 n + 1 of a
-//    slice, 8 bytes of row l: half n % 2 of 16-byte chunk 4 (n / 2) + g, i.e.
-//    the 16 E2M1 values of block 8 (n / 2) + 2 g + n % 2, values 0-7 for the
-//    first K step and 8-15 for the second, and that block's scale byte.  The
+//    slice, 8 bytes of row l: half h = (n + g) % 2 of 16-byte chunk
+//    4 (n / 2) + g, i.e. the 16 E2M1 values of block 8 (n / 2) + 2 g + h,
+//    values 0-7 for the first K step and 8-15 for the second, and that
+//    block's scale byte.  (With h = n % 2 for every lane, the 32 lanes that
+//    an 8-byte LDS read serves at once would meet each bank twice.)  The
 //    matrix core sums a K step over its 32 positions whatever K values they
 //    hold, so a K step sums its own 32 K values of the slice and the eight K
 //    steps all 256: the same sum in another order.
@@ -224,8 +226,8 @@ void gemm16_nv4_kernel(GemmArgs p) {
     // stored at chunk ^ ((row / 2) % 8), i.e. the 16 E2M1 values of block
     // 8 q + 2 (l / 16) + h of the slice; sc[f]: that block's E4M3 scale,
     // made fp16 at the half's first conversion; cv[f]: the fp16 fragment of
-    // the current K step.  K step t of a slice takes half (t / 2) % 2 of quad
-    // t / 4, dword t % 2.
+    // the current K step.  K step t of a slice takes half (t / 2 + l / 16) % 2
+    // of quad t / 4, dword t % 2.
     const int r16 = lane & 15, g4 = lane >> 4;
     const int xr = r16 >> 1;
     const uint32_t a_row = (uint32_t)(wm * 128 + r16) * RB;
@@ -248,9 +250,10 @@ void gemm16_nv4_kernel(GemmArgs p) {
     };
     // the half that K steps 2 n and 2 n + 1 of slice h take (n = 0 .. 3)
     auto aim_reads = [&](int h, int n) __attribute__((always_inline)) {
-        const int st = h & 1, q = n >> 1, hf = n & 1;
-        nro = (uint32_t)(st * STAGE) + (q ? chq1 : chq0) + 8u * (uint32_t)hf;
-        nso = (uint32_t)(st * CHUNK + 8 * q + hf);
+        const int st = h & 1, q = n >> 1;
+        const uint32_t hf = (uint32_t)((n ^ g4) & 1);
+        nro = (uint32_t)(st * STAGE) + (q ? chq1 : chq0) + 8u * hf;
+        nso = (uint32_t)(st * CHUNK + 8 * q) + hf;
     };
     // Part PP of fragment F for a K step of parity T (values 2 PP, 2 PP + 1 of
     // the lane's 8: byte PP of dword T of the half), in two stages one
