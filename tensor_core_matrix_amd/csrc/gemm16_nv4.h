@@ -41,6 +41,8 @@
 //    8 KiB piece buffer per stage); the epilogue multiplies by the product of
 //    the tensor scales and stages 16 rows of 16-bit output per wave through
 //    LDS (fp32 output is stored directly).
+// One problem per launch (the NVFP4 entry point takes no batch); K a multiple
+// of 256 and both scale tensors 16-byte aligned, as the host checks.
 #pragma once
 
 #include "gemm16.h"
