@@ -82,6 +82,26 @@ __device__ constexpr int first_use(int f) {
 __device__ constexpr int conv_nops(int f, int p) {
     return first_use(f) - conv_slot(f, p) == 2 ? 1 : -1;
 }
+// the last product using fragment f in the K step its slots count from
+__device__ constexpr int last_use(int f) {
+    return f < 4 ? 19 + 4 * f : f < 8 ? 35 + 4 * f : f < 12 ? 44 + (f - 8) : 56 + (f - 8);
+}
+// Every part after the fragment's last product and two before its first, the
+// parts of a fragment in order, at most two conversions after one product.
+__device__ constexpr bool slots_valid() {
+    int per_slot[128] = {};
+    for (int f = 0; f < 16; ++f)
+        for (int p = 0; p < 4; ++p) {
+            const int s = conv_slot(f, p);
+            if (s <= last_use(f) || s + 2 > first_use(f) || s >= 128) return false;
+            if (p > 0 && s < conv_slot(f, p - 1)) return false;
+            if (++per_slot[s] > 2) return false;
+        }
+    for (int x = 0; x < 64; ++x)
+        if (per_slot[x] + per_slot[x + 64] > 2) return false;
+    return true;
+}
+static_assert(slots_valid(), "conversion slots");
 static_assert(conv_slot(6, 3) + 2 == first_use(6) && conv_slot(7, 3) + 2 == first_use(7), "A6, A7 windows");
 // the k-th conversion (4 f + p) at slot s, k = 0, 1 (at most two share a slot), or -1
 __device__ constexpr int task_at(int s, int k) {
