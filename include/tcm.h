@@ -298,7 +298,8 @@ typedef struct tcm_plan {
 } tcm_plan;
 
 /* mx == 1 plans tcm_gemm_mx_fp8 and mx == 2 tcm_gemm_mx_fp4 (with 16-byte aligned
- * scale tensors), mx == 3 tcm_gemm_mx_fp6 (with 4-byte aligned scale tensors), mx == 4 tcm_gemm_nvfp4 (with 16-byte aligned scale
+ * scale tensors), mx == 3 tcm_gemm_mx_fp6 (with 16-byte aligned scale tensors where
+ * K % 512 == 0, else 4-byte aligned), mx == 4 tcm_gemm_nvfp4 (with 16-byte aligned scale
  * tensors), mx == 5 tcm_gemm_mx with an M- or N-major operand (dtype is then ignored);
  * other mx values are TCM_ERR_INVALID_ARGUMENT. */
 tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dtype dtype,

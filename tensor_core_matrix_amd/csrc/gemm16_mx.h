@@ -24,6 +24,21 @@
 //
 // Requires K % 512 == 0 and 16-byte aligned scale arrays (whole 16-byte
 // pieces per row); dense storage (rows K apart, Out rows N apart).
+//
+// MXFP6 (FMT 2: E2M3, 3: E3M2) runs the same kernel.  Lane l + 16 b of a
+// 16 x 16 x 128 product holds the whole block b of its row: 32 six-bit codes
+// as the block's 24 stored bytes in the operand's first six registers (as in
+// the 32 x 32 x 64 form, one lane group per block).  A 128-deep slice is 96
+// bytes of a stored row.  Its LDS row keeps the 128 bytes and 8 chunks of the
+// fp8 layout: chunk b < 4 holds bytes 0-15 of block b, chunk 4 + b the 16
+// stored bytes from byte 8 of block b (b = 0, 3: the block's last 8 bytes in
+// the chunk's upper half) or from byte 16 (b = 1, 2: in its lower half,
+// followed by the next block's first 8).  A fragment is a 16-byte read of
+// chunk b and an 8-byte read of the block's last 8 bytes from chunk 4 + b;
+// the 32 lanes served together by an 8-byte read (blocks 0 and 1, or 2 and
+// 3) use opposite halves of their chunks and so meet no bank twice.  Every
+// copy stays inside its row's slice.  A product takes half the cycles of an
+// fp8 one, so the same copy stream serves twice the products per cycle.
 #pragma once
 
 #include "gemm16.h"
@@ -41,13 +56,22 @@ __device__ constexpr int copy_at(int x) {
                : -1;
 }
 static_assert(kLastCopy < 64 && kScaleSlot1 < 64, "slots");
+// MXFP6: the stored byte of a slice row that LDS chunk c (0..7) starts at
+__device__ constexpr int f6_chunk(int c) {
+    return c < 4 ? 24 * c : 24 * (c - 4) + ((c == 4 || c == 7) ? 8 : 16);
+}
+static_assert(f6_chunk(7) + 16 == 96 && f6_chunk(6) + 16 <= 96, "MXFP6 chunks stay inside the slice");
 }  // namespace g16mx
 
-template <typename TOut>
+// FMT: the operands' format code of the scaled product, 0 E4M3, 2 E2M3, 3 E3M2
+template <typename TOut, int FMT = 0>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm16_mx_kernel(GemmArgs p) {
+    static_assert(FMT == 0 || FMT == 2 || FMT == 3, "E4M3, E2M3 or E3M2");
+    constexpr bool F6 = FMT != 0;
     constexpr int BM = 256, BN = 256, BK = 128, S = 2;
-    constexpr int RB = BK;                 // bytes of one row's slice
+    constexpr int RB = BK;                 // LDS bytes of one row's slice
+    constexpr int RBG = F6 ? 96 : 128;     // stored bytes of one row's slice
     constexpr int A_BYTES = BM * RB;       // 32 KiB
     constexpr int STAGE = A_BYTES + BN * RB;
     constexpr int CHUNK = (BM + BN) * 16;  // scale bytes of four slices, 8 KiB
@@ -70,24 +94,26 @@ void gemm16_mx_kernel(GemmArgs p) {
     const int total = my_tiles * p.ksteps;
     const int K = p.K;
     const int KS = K / 32;  // scale bytes per row
+    const int RS = F6 ? K / 4 * 3 : K;  // stored bytes per row
 
-    // ---- operand copies (as gemm16.h, 128 fp8 values per row and slice) ----
+    // ---- operand copies (as gemm16.h, 128 values per row and slice) --------
     const int cp_row = wave * 8 + lane / 8;
     const int cp_chunk = (lane & 7) ^ ((cp_row >> 1) & 7);
-    const uint32_t cp_off = (uint32_t)cp_row * (uint32_t)K + (uint32_t)cp_chunk * 16u;
-    const uint32_t cp_step = 32u * (uint32_t)K;
+    const uint32_t cp_byte = F6 ? (uint32_t)g16mx::f6_chunk(cp_chunk) : (uint32_t)cp_chunk * 16u;
+    const uint32_t cp_off = (uint32_t)cp_row * (uint32_t)RS + cp_byte;
+    const uint32_t cp_step = 32u * (uint32_t)RS;
 
     auto locate = [&](TileCursor& c) { tile_coords(p, c.tl * G + lid, c.batch, c.tm, c.tn); };
     TileCursor fc = {0, 0, 0, 0, 0};
     __amdgpu_buffer_rsrc_t ra, rb;
     auto feed_resources = [&]() {
         const int rows_a = min(BM, p.M - fc.tm * BM), rows_b = min(BN, p.N - fc.tn * BN);
-        ra = make_rsrc((const char*)p.A + (int64_t)fc.tm * BM * K, (uint32_t)rows_a * (uint32_t)K);
-        rb = make_rsrc((const char*)p.B + (int64_t)fc.tn * BN * K, (uint32_t)rows_b * (uint32_t)K);
+        ra = make_rsrc((const char*)p.A + (int64_t)fc.tm * BM * RS, (uint32_t)rows_a * (uint32_t)RS);
+        rb = make_rsrc((const char*)p.B + (int64_t)fc.tn * BN * RS, (uint32_t)rows_b * (uint32_t)RS);
     };
     uint32_t foff0 = 0;
     int fg = 0;
-    auto feed_offsets = [&]() { foff0 = fg < total ? cp_off + (uint32_t)(fc.kk * RB) : kOutOfRange; };
+    auto feed_offsets = [&]() { foff0 = fg < total ? cp_off + (uint32_t)(fc.kk * RBG) : kOutOfRange; };
     auto feed_next = [&]() {
         if (++fc.kk == p.ksteps) {
             fc.kk = 0;
@@ -145,25 +171,29 @@ void gemm16_mx_kernel(GemmArgs p) {
     const int xr = r16 >> 1;
     const uint32_t a_row = (uint32_t)(wm * 128 + r16) * RB;
     const uint32_t b_row = (uint32_t)A_BYTES + (uint32_t)(wn * 128 + r16) * RB;
-    const uint32_t ch0 = (uint32_t)(g4 ^ xr) * 16u, ch1 = (uint32_t)((4 + g4) ^ xr) * 16u;
+    const uint32_t ch0 = (uint32_t)(g4 ^ xr) * 16u;
+    // MXFP6: the block's last 8 bytes sit at byte 8 of chunk 4 + b for b = 0, 3
+    const uint32_t ch1 = (uint32_t)((4 + g4) ^ xr) * 16u + (F6 && (g4 == 0 || g4 == 3) ? 8u : 0u);
     const uint32_t sa_row = (uint32_t)(wm * 128 + r16) * 16u + (uint32_t)g4;
     const uint32_t sb_row = 4096u + (uint32_t)(wn * 128 + r16) * 16u + (uint32_t)g4;
     // the two 16-byte halves of each fragment are kept apart and joined at
     // the product (an 8-register value refilled in the loop made the compiler
     // move every fragment register at the loop's back edge)
-    i32x4_t fa0[8], fa1[8], fb0[8], fb1[8];
+    typedef typename std::conditional<F6, i32x2_t, i32x4_t>::type half_t;
+    i32x4_t fa0[8], fb0[8];
+    half_t fa1[8], fb1[8];
     int sa[8], sb[8];
     // fragments of slice h: stage h % 2; scales: chunk buffer (h / 4) % 2, byte 4 (h % 4) + l / 16
     auto read_a = [&](int h, int i) {
         const char* p0 = lds + (h & 1) * STAGE + a_row + i * 16 * RB;
         fa0[i] = *(const i32x4_t*)(p0 + ch0);
-        fa1[i] = *(const i32x4_t*)(p0 + ch1);
+        fa1[i] = *(const half_t*)(p0 + ch1);
         sa[i] = *(const unsigned char*)(scb + ((h >> 2) & 1) * CHUNK + sa_row + i * 256 + 4 * (h & 3));
     };
     auto read_b = [&](int h, int j) {
         const char* p0 = lds + (h & 1) * STAGE + b_row + j * 16 * RB;
         fb0[j] = *(const i32x4_t*)(p0 + ch0);
-        fb1[j] = *(const i32x4_t*)(p0 + ch1);
+        fb1[j] = *(const half_t*)(p0 + ch1);
         sb[j] = *(const unsigned char*)(scb + ((h >> 2) & 1) * CHUNK + sb_row + j * 256 + 4 * (h & 3));
     };
 
@@ -237,9 +267,18 @@ void gemm16_mx_kernel(GemmArgs p) {
             constexpr int x = decltype(X)::value;
             constexpr int i = g16::a_of(x), j = g16::b_of(x);
             const f32x4_t c = decltype(ZERO)::value ? (f32x4_t){} : acc[i][j];
-            const i32x8_t a8 = __builtin_shufflevector(fa0[i], fa1[i], 0, 1, 2, 3, 4, 5, 6, 7);
-            const i32x8_t b8 = __builtin_shufflevector(fb0[j], fb1[j], 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, c, 0, 0, 0, sb[j], 0, sa[i]);
+            i32x8_t a8, b8;
+            if constexpr (F6) {
+                // registers 0-5: the block's 24 bytes; 6, 7 unused
+                a8 = __builtin_shufflevector(fa0[i], __builtin_shufflevector(fa1[i], fa1[i], 0, 1, -1, -1), 0, 1,
+                                             2, 3, 4, 5, -1, -1);
+                b8 = __builtin_shufflevector(fb0[j], __builtin_shufflevector(fb1[j], fb1[j], 0, 1, -1, -1), 0, 1,
+                                             2, 3, 4, 5, -1, -1);
+            } else {
+                a8 = __builtin_shufflevector(fa0[i], fa1[i], 0, 1, 2, 3, 4, 5, 6, 7);
+                b8 = __builtin_shufflevector(fb0[j], fb1[j], 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, c, FMT, FMT, 0, sb[j], 0, sa[i]);
             if constexpr (x == g16mx::kHandoff) {
                 wait_vmcnt<0>();
                 barrier_lds();

@@ -1,5 +1,7 @@
 // Kernel instances and launcher for the MXFP6 (E2M3 or E3M2 + E8M0 per 32)
-// product: the ping-pong kernel with 64-deep units in a ring of four.
+// product: the ping-pong kernel with 64- or 128-deep units, and the 16 x 16
+// x 128 kernel of gemm16_mx.h where scales come as 16-byte pieces.
+#include "gemm16_mx.h"
 #include "gemm_pingpong.h"
 
 namespace tcm {
@@ -25,6 +27,12 @@ static hipError_t by_variant(int32_t v, int32_t mode, const GemmArgs& a, int gri
     switch (v) {
     case V_MX6PP256: return by_mode<TOut, FMT, 64, 4>(mode, a, grid, st);
     case V_MX6PP256_K128: return by_mode<TOut, FMT, 128, 3>(mode, a, grid, st);
+    case V_MX6_16_256:
+        if (mode == 2) {
+            hipLaunchKernelGGL((gemm16_mx_kernel<TOut, FMT>), dim3(grid), dim3(kThreads), 0, st, a);
+            return hipGetLastError();
+        }
+        break;
     }
     return hipErrorInvalidValue;
 }

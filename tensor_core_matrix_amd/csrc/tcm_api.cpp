@@ -25,6 +25,8 @@ VariantInfo variant_info(int32_t v) {
     case V_T256x256_M16: return {256, 256, 64, 2, 1, 16, kThreads};
     case V_MX16_256: return {256, 256, 128, 2, 1, 8, kThreads};
     case V_MX4_16_256: return {256, 256, 256, 2, 1, 4, kThreads};
+    // MXFP6 on the 16x16 kernel: 96-byte rows in 128-byte LDS rows
+    case V_MX6_16_256: return {256, 256, 128, 2, 1, 6, kThreads};
     case V_MXPP256_K64S4: return {256, 256, 64, 4, 1, 8, 512};
     case V_MX4PP256: return {256, 256, 128, 4, 1, 4, 512};
     case V_MX6PP256: return {256, 256, 64, 4, 1, 6, 512};
@@ -198,7 +200,9 @@ tcm_status plan_variant(int32_t v, int64_t batch, int64_t M, int64_t N, int64_t 
     int64_t grid = tiles < slots ? tiles : slots;
     const int64_t cap = max_grid();
     if (grid > cap) grid = cap;
-    int32_t stage = (vi.tile_m + vi.tile_n) * vi.tile_k * vi.elem_bits / 8;
+    // (the 16x16 MXFP6 kernel keeps each 96-byte row slice in 128 LDS bytes)
+    const int32_t lds_bits = v == V_MX6_16_256 ? 8 : vi.elem_bits;
+    int32_t stage = (vi.tile_m + vi.tile_n) * vi.tile_k * lds_bits / 8;
     if (plan) {
         plan->tile_m = vi.tile_m;
         plan->tile_n = vi.tile_n;
@@ -241,9 +245,13 @@ tcm_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, int32_t bit
 // MXFP6: the 128-deep kernel reads its scales as 32-bit words or 16-byte
 // pieces (K a multiple of 128, word-aligned scale tensors); with scales read
 // byte by byte it would spill registers, so such calls take the 64-deep
-// kernel unless a variant is forced.
-int32_t mx6_variant(int32_t v, bool scale_words) {
-    return v == V_MX6PP256_K128 && !scale_words && forced_variant() < 0 ? V_MX6PP256 : v;
+// kernel unless a variant is forced.  Where scales come as 16-byte pieces
+// (K % 512 == 0, 16-byte aligned scale tensors) the 16 x 16 x 128 kernel
+// (variant 36) takes the 128-deep kernel's place unless that one is forced.
+int32_t mx6_variant(int32_t v, bool scale_words, bool scale_chunks) {
+    if (v == V_MX6_16_256 && !scale_chunks) v = V_MX6PP256_K128;
+    if (v == V_MX6PP256_K128 && scale_chunks && forced_variant() != V_MX6PP256_K128) return V_MX6_16_256;
+    return v == V_MX6PP256_K128 && !scale_words && forced_variant() != V_MX6PP256_K128 ? V_MX6PP256 : v;
 }
 
 // MXFP8 256 x 256 tiles: the 16 x 16 x 128 kernel (variant 31) where scales
@@ -377,8 +385,8 @@ tcm_status run_mx(int32_t bits, const void* A, const void* B, const void* scale_
     tcm_plan plan;
     GemmArgs a;
     if (bits == 6)
-        plan_variant(mx6_variant(choose_variant(1, M, N, bits, dev.cus), scale_mode >= 1), 1, M,
-                     N, K, dev.cus, &plan, &a);
+        plan_variant(mx6_variant(choose_variant(1, M, N, bits, dev.cus), scale_mode >= 1, scale_mode == 2),
+                     1, M, N, K, dev.cus, &plan, &a);
     else if (bits == 8)
         plan_variant(mx8_variant(choose_variant(1, M, N, bits, dev.cus), scale_mode == 2), 1, M, N,
                      K, dev.cus, &plan, &a);
@@ -672,7 +680,8 @@ tcm_status tcm_plan_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, tcm_dty
                      b1, m1, n1, K, num_cus, plan, nullptr);
     else if (mx == 3)
         // (word-aligned scale tensors)
-        plan_variant(mx6_variant(choose_variant(b1, m1, n1, 6, num_cus), K > 0 && K % 128 == 0),
+        plan_variant(mx6_variant(choose_variant(b1, m1, n1, 6, num_cus), K > 0 && K % 128 == 0,
+                                 K > 0 && K % 512 == 0),
                      b1, m1, n1, K, num_cus, plan, nullptr);
     else if (mx == 1)
         // (16-byte aligned scale tensors)

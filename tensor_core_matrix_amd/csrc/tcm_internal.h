@@ -64,6 +64,7 @@ enum Variant : int32_t {
     V_MX16_256 = 31,        // MXFP8 256x256x128 on the 16x16x128 scaled MFMA, scale chunks by DMA (gemm16_mx.h)
     V_MX4_16_256 = 32,      // MXFP4 256x256x256 on the 16x16x128 scaled MFMA, scale chunks by DMA (gemm16.h)
     V_NV4_16_256 = 34,      // NVFP4 256x256x256, E2M1 rows by DMA, converted per fragment for the 16x16x32 fp16 MFMA (gemm16_nv4.h)
+    V_MX6_16_256 = 36,      // MXFP6 256x256x128 on the 16x16x128 scaled MFMA, 96-byte rows in 128-byte LDS rows (gemm16_mx.h)
 };
 
 struct VariantInfo {

@@ -120,7 +120,7 @@ def test_mxfp6_entry_validation():
     assert f6(a=None) == NULLP
     p = tcm.plan(8192, 8192, 8192, mx=3)
     assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"]) == \
-        (256, 128, 48 * 1024, 3, 512)
+        (256, 128, 64 * 1024, 2, 256)
 
 
 def test_nvfp4_entry_validation():
@@ -200,10 +200,15 @@ def test_plans_of_the_workloads():
     p = tcm.plan(8192, 8192, 8064, mx=2)
     assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["threads"], p["kernel"]) == \
         (256, 128, 32 * 1024, 4, 512, 20)
-    # MXFP6 8192^3: 128-deep units of 96-byte rows (48 KiB) in a ring of
-    # three (variant 27); K not a multiple of 128 (scales read byte by byte):
-    # the 64-deep kernel's ring of four 24 KiB units (variant 21)
+    # MXFP6 8192^3: the 16 x 16 kernel, 128-deep slices of 96-byte rows kept
+    # in 128-byte LDS rows (64 KiB stages, variant 36); K a multiple of 128
+    # only (scales read as words): 128-deep units of 96-byte rows (48 KiB) in
+    # a ring of three (variant 27); K not a multiple of 128 (scales read byte
+    # by byte): the 64-deep kernel's ring of four 24 KiB units (variant 21)
     p = tcm.plan(8192, 8192, 8192, mx=3)
+    assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["kernel"]) == \
+        (256, 128, 64 * 1024, 2, 36)
+    p = tcm.plan(8192, 8192, 8064, mx=3)
     assert (p["tile_m"], p["tile_k"], p["stage_bytes"], p["stages"], p["kernel"]) == \
         (256, 128, 48 * 1024, 3, 27)
     p = tcm.plan(8192, 8192, 8128, mx=3)

@@ -6,7 +6,10 @@ up to K = 1024 are exact in fp32, so those cases must match bit for bit.  The
 shapes reach all three ways of reading the scales (bytes: K = 576, 32-bit
 words: K = 640, 16-byte pieces: K = 1536), each on both kernels: 128-deep
 units (variant 27, the default where scales are read as words or pieces;
-K = 576 leaves its last unit half empty) and 64-deep units (variant 21)."""
+K = 576 leaves its last unit half empty) and 64-deep units (variant 21),
+and, where scales come as 16-byte pieces (K = 1536, 1024), the 16 x 16 x 128
+kernel (variant 36; forced on other shapes it gives way to variant 27 or
+21)."""
 import numpy as np
 import pytest
 import torch
@@ -62,7 +65,7 @@ def grid_cap(monkeypatch):
     return _set
 
 
-@pytest.fixture(params=[27, 21])
+@pytest.fixture(params=[27, 21, 36])
 def variant(request, monkeypatch):
     monkeypatch.setenv("TCM_FORCE_VARIANT", str(request.param))
     return request.param
@@ -104,3 +107,32 @@ def test_mxfp6_scale_reaches_only_its_block():
     ref, _ = oracle(a, b, sa2, sb, "e2m3")
     assert np.array_equal(got, ref)
     assert np.array_equal(np.delete(got, 5, 0), np.delete(base, 5, 0))
+
+
+@pytest.mark.parametrize("K", [512, 1024, 2560])
+@pytest.mark.parametrize("elem", ["e2m3", "e3m2"])
+def test_mxfp6_16x16_tile_sequences(K, elem, grid_cap, monkeypatch):
+    """The 16 x 16 x 128 kernel forced on a ragged multi-tile shape: one, two
+    and five scale chunks of 512 K per tile, every workgroup of a grid of 5
+    walking several tiles (the last ragged in M and N), both outputs."""
+    monkeypatch.setenv("TCM_FORCE_VARIANT", "36")
+    M, N = 600, 1100
+    a, b, sa, sb = make(M, N, K, 1200 + K)
+    ref, s = oracle(a, b, sa, sb, elem)
+    for cap in (None, 5):
+        grid_cap(cap)
+        for odt in ("f32", "bf16"):
+            check(run_fp6(a, b, sa, sb, odt, elem), ref, s, odt, f"variant 36 {elem} K {K} {odt} grid {cap}")
+
+
+def test_mxfp6_16x16_wide_block_scales(monkeypatch):
+    """Variant 36 with every (row, block) scale of A and B drawn from
+    2^-8 .. 2^8: a block whose scale reached another block's values, or
+    values read from the wrong bytes of a 96-byte row slice, moves outputs
+    by factors far outside the bound."""
+    monkeypatch.setenv("TCM_FORCE_VARIANT", "36")
+    M, N, K = 256, 256, 512
+    a, b, sa, sb = make(M, N, K, 1300, -8, 8)
+    for elem in ("e2m3", "e3m2"):
+        ref, s = oracle(a, b, sa, sb, elem)
+        check(run_fp6(a, b, sa, sb, "f32", elem), ref, s, "f32", f"variant 36 wide scales {elem}")
