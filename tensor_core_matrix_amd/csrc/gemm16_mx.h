@@ -324,7 +324,22 @@ void gemm16_mx_kernel(GemmArgs p) {
     for (int tl = 0; tl < my_tiles; ++tl) {
         slice(g, std::true_type{});
         ++g;
-        for (int kk = 1; kk < p.ksteps; ++kk, ++g) slice(g, std::false_type{});
+        if constexpr (F6) {
+            // two slices per iteration: with one, the compiler moved ten
+            // fragments' registers at every back edge (MXFP8's 8-register
+            // fragments do not fit two slices' worth and spill)
+            int kk = 1;
+            for (; kk + 1 < p.ksteps; kk += 2, g += 2) {
+                slice(g, std::false_type{});
+                slice(g + 1, std::false_type{});
+            }
+            if (kk < p.ksteps) {
+                slice(g, std::false_type{});
+                ++g;
+            }
+        } else {
+            for (int kk = 1; kk < p.ksteps; ++kk, ++g) slice(g, std::false_type{});
+        }
         TileCursor ec = {tl, 0, 0, 0, 0};
         locate(ec);
         __builtin_amdgcn_sched_barrier(0);
