@@ -4,12 +4,12 @@ acceptance rule as the other products: |gpu - ref| <= 1e-4 * sum_k |a_ik b_jk|
 (+ one bf16 ulp for bf16 output).  With unit scales, E2M3 products and sums
 up to K = 1024 are exact in fp32, so those cases must match bit for bit.  The
 shapes reach all three ways of reading the scales (bytes: K = 576, 32-bit
-words: K = 640, 16-byte pieces: K = 1536), each on both kernels: 128-deep
-units (variant 27, the default where scales are read as words or pieces;
-K = 576 leaves its last unit half empty) and 64-deep units (variant 21),
-and, where scales come as 16-byte pieces (K = 1536, 1024), the 16 x 16 x 128
-kernel (variant 36; forced on other shapes it gives way to variant 27 or
-21)."""
+words: K = 640, 16-byte pieces: K = 1536), each on the ping-pong kernels:
+128-deep units (variant 27, the default where scales are read as words;
+K = 576 leaves its last unit half empty) and 64-deep units (variant 21);
+and, where scales come as 16-byte pieces (K = 1536, 1024), on the default
+there, the 16 x 16 x 128 kernel (variant 36; forced on other shapes it gives
+way to variant 27 or 21)."""
 import numpy as np
 import pytest
 import torch
